@@ -1,0 +1,517 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU oracle for the forward pass
+ * of one routed mixture-of-experts layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * includes, links or calls anything in this directory, and this file includes
+ * nothing from the GPU library.
+ *
+ * Arithmetic: every sum and product is done in IEEE double, in the order the
+ * loops below state (no blocking, no reordering, no fused multiply-add: build
+ * with -ffp-contract=off).  Storage roundings to bfloat16 / float32 are applied
+ * exactly where the layer stores a tensor in that precision, using the
+ * round-to-nearest-even rule implemented below from its definition.
+ *
+ * What the layer computes (sources):
+ *   - Marin 535B-A23B: the half of a training run nobody usually shows you,
+ *     section "What is actually being trained": a 6,144-wide token is projected
+ *     to a 3,072-wide latent, normalised, sent to 8 of 384 routed experts,
+ *     weighted-combined, projected back up; two shared experts see every token.
+ *   - Marin Begins Open Training of a 535B-Parameter MoE Model, section 2
+ *     "How the Sparse Model Is Organized": the up-projected routed output is
+ *     added to the shared-expert path; capacity overflow is dropped and counted.
+ *   - same page, section 4: a dropped assignment skips only that expert; the
+ *     shared experts still process the token.
+ *   - Marin 535B-A23B article, section "The one knob nobody pinned": the router
+ *     has a weight and a bias (both free parameters).
+ *   - Marin: Week of July 6th summary, JaxPP paragraph: the expert MLP is gated
+ *     (SwiGLU) and an approximate activation broke parity, so the activation here
+ *     is the exact silu(v) = v / (1 + exp(-v)).
+ *   - Marin weekly summary of September 14 (post-training section): the combine
+ *     is an ordered gather, summed in a fixed order, not an atomic scatter-add.
+ *   - same summary (hero-run engineering): capacity is an integer computation
+ *     so that it can never exceed the buffer by a row.
+ * Readings where the pages are silent (router input, tie rule, capacity rounding,
+ * gate/up halves, eps) are stated next to the function that takes them.
+ *
+ * Parity status: every exported function is pinned by CPU tests against
+ * closed forms, brute force and library routines (see tests/test_oracle_*.py).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define DT_F32 0
+#define DT_BF16 1
+
+/* ---------------------------------------------------------------- storage --- */
+
+/* bfloat16 bits -> exact value.  A bfloat16 is the upper half of a float32. */
+static double bf16_val(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Round a double to the nearest bfloat16, ties to even, straight from the
+ * double (no intermediate float).  bfloat16 has an 8-bit significand and the
+ * float32 exponent range; below 2^-126 the quantum is fixed at 2^-133. */
+uint16_t moe_ref_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7FC0;
+    int neg = signbit(x) ? 1 : 0;
+    double a = fabs(x);
+    if (isinf(a) || a == 0.0) {
+        uint16_t mag = isinf(a) ? 0x7F80 : 0x0000;
+        return (uint16_t)(mag | (neg << 15));
+    }
+    int e;
+    (void)frexp(a, &e);               /* a = m * 2^e, m in [0.5, 1) */
+    int qe = e - 8;                   /* quantum exponent of an 8-bit significand */
+    if (qe < -133)
+        qe = -133;                    /* subnormal range */
+    double q = ldexp(a, -qe);         /* exact: a power-of-two scaling */
+    double r = nearbyint(q);          /* current rounding mode = to nearest, ties even */
+    double v = ldexp(r, qe);
+    uint16_t out;
+    if (v >= 0x1p128) {
+        out = 0x7F80;                 /* overflow to infinity */
+    } else {
+        float f = (float)v;           /* exact: v has at most 8 significant bits */
+        uint32_t u;
+        memcpy(&u, &f, sizeof u);
+        out = (uint16_t)(u >> 16);
+    }
+    return (uint16_t)(out | (neg << 15));
+}
+
+/* Value of a double after storage in the given precision. */
+static double store_as(double v, int dt)
+{
+    if (dt == DT_BF16)
+        return bf16_val(moe_ref_to_bf16(v));
+    return (double)(float)v;          /* float32: C's conversion rounds to nearest even */
+}
+
+/* Element i of a float32 or bfloat16 array, as an exact double. */
+static double ld(const void *p, int dt, int64_t i)
+{
+    if (dt == DT_BF16)
+        return bf16_val(((const uint16_t *)p)[i]);
+    return (double)((const float *)p)[i];
+}
+
+/* ------------------------------------------------------------------ norm --- */
+
+/* RMSNorm of one row: z = v / sqrt(mean(v^2) + eps) * g.  g may be NULL (= 1).
+ * Reading: eps = 1e-5 unless the caller passes another; the pages only say the
+ * latent is "normalised" and that norm gains are free parameters. */
+void moe_ref_rmsnorm_row(const double *v, int64_t n, const float *g, double eps, double *z)
+{
+    double ss = 0.0;
+    for (int64_t i = 0; i < n; i++)
+        ss += v[i] * v[i];
+    double inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (int64_t i = 0; i < n; i++)
+        z[i] = v[i] * inv * (g ? (double)g[i] : 1.0);
+}
+
+/* ------------------------------------------------------------------ top-k --- */
+
+/* Does (va, ia) rank above (vb, ib)?  Larger value first; equal values (and
+ * +0 == -0, which C's == already treats as equal) go to the lower expert id;
+ * a NaN ranks below every number, NaNs among themselves by id. */
+static int ranks_above(float va, int ia, float vb, int ib)
+{
+    int na = isnan(va), nb = isnan(vb);
+    if (na || nb) {
+        if (na && nb)
+            return ia < ib;
+        return nb;                    /* the non-NaN one is above */
+    }
+    if (va > vb)
+        return 1;
+    if (va < vb)
+        return 0;
+    return ia < ib;
+}
+
+/* Top-k selection and routing weights for T tokens.
+ *   logits [T, E] float32 -> ids [T, k] int32, w [T, k] float32.
+ * The spec's order: softmax over all E in double, select k experts, renormalise
+ * the selected probabilities to sum to one.  Selection is taken on the float32
+ * logits themselves (softmax is strictly increasing, so this is the same set in
+ * exact arithmetic, and it avoids ties that rounded probabilities would create).
+ * ids[t, j] is the j-th best expert.  Selection is k passes, each taking the
+ * best expert not yet taken. */
+void moe_ref_topk(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *ids, float *w)
+{
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    char *taken = (char *)malloc((size_t)E);
+    for (int64_t t = 0; t < T; t++) {
+        const float *l = logits + t * E;
+        /* softmax over all experts, double precision */
+        double m = -INFINITY;
+        for (int32_t e = 0; e < E; e++)
+            if ((double)l[e] > m)
+                m = (double)l[e];
+        double s = 0.0;
+        for (int32_t e = 0; e < E; e++) {
+            p[e] = exp((double)l[e] - m);
+            s += p[e];
+        }
+        for (int32_t e = 0; e < E; e++)
+            p[e] /= s;
+        /* selection */
+        memset(taken, 0, (size_t)E);
+        double ps = 0.0;
+        for (int32_t j = 0; j < k; j++) {
+            int best = -1;
+            for (int32_t e = 0; e < E; e++) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || ranks_above(l[e], e, l[best], best))
+                    best = e;
+            }
+            taken[best] = 1;
+            ids[t * k + j] = best;
+            ps += p[best];
+        }
+        /* renormalise over the selected set */
+        for (int32_t j = 0; j < k; j++)
+            w[t * k + j] = (float)(p[ids[t * k + j]] / ps);
+    }
+    free(p);
+    free(taken);
+}
+
+/* -------------------------------------------------------------- capacity --- */
+
+/* Per-expert capacity C = ceil(cf * n_assign / E) with cf = num/den, computed
+ * in integers so that no rounding can add a row (the pages report a float
+ * capacity rounding that could exceed the buffer by one row). */
+int64_t moe_ref_capacity(int64_t cf_num, int64_t cf_den, int64_t n_assign, int64_t E)
+{
+    return (cf_num * n_assign + cf_den * E - 1) / (cf_den * E);
+}
+
+/* ---------------------------------------------------------------- permute --- */
+
+/* Group assignments by expert.
+ *   ids [n] int32: expert of assignment a (a = t*k + j for routed tokens, or a
+ *       pool row); a negative id is padding and takes part in nothing.
+ *   capacity: rows kept per expert, or < 0 for no limit.
+ * Outputs:
+ *   counts [E]     assignments per expert (before the capacity cut)
+ *   offsets [E+1]  exclusive prefix sum of kept rows: expert e owns rows
+ *                  [offsets[e], offsets[e+1])
+ *   slot_row [n]   row of assignment a, or -1 if a is padding or dropped
+ *   row_src [R_phys] assignment that fills each row, -1 beyond offsets[E]
+ *   n_dropped      assignments cut by the capacity
+ * The kept assignments of an expert are its first `capacity` ones in ascending
+ * a (arrival order), and they fill its rows in that order.
+ * Returns 0, or -1 on an id >= E or too few physical rows. */
+int moe_ref_permute(const int32_t *ids, int64_t n, int32_t E, int64_t capacity,
+                    int32_t *counts, int32_t *offsets, int32_t *slot_row,
+                    int32_t *row_src, int64_t R_phys, int64_t *n_dropped)
+{
+    for (int32_t e = 0; e < E; e++)
+        counts[e] = 0;
+    for (int64_t a = 0; a < n; a++) {
+        if (ids[a] >= E)
+            return -1;
+        if (ids[a] >= 0)
+            counts[ids[a]]++;
+    }
+    offsets[0] = 0;
+    int64_t dropped = 0;
+    for (int32_t e = 0; e < E; e++) {
+        int64_t kept = counts[e];
+        if (capacity >= 0 && kept > capacity)
+            kept = capacity;
+        dropped += counts[e] - kept;
+        offsets[e + 1] = (int32_t)(offsets[e] + kept);
+    }
+    if (offsets[E] > R_phys)
+        return -1;
+    for (int64_t r = 0; r < R_phys; r++)
+        row_src[r] = -1;
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    for (int64_t a = 0; a < n; a++) {
+        int32_t e = ids[a];
+        if (e < 0) {
+            slot_row[a] = -1;
+            continue;
+        }
+        int32_t rank = seen[e]++;
+        if (rank < offsets[e + 1] - offsets[e]) {
+            int32_t row = offsets[e] + rank;
+            slot_row[a] = row;
+            row_src[row] = (int32_t)a;
+        } else {
+            slot_row[a] = -1;
+        }
+    }
+    free(seen);
+    *n_dropped = dropped;
+    return 0;
+}
+
+/* ------------------------------------------------------------- expert FFN --- */
+
+/* One expert applied to one row: the gated (SwiGLU) MLP.
+ *   x [d] exact values, W_gu [2H, d] (rows [0, H) are the gate projection,
+ *   rows [H, 2H) the up projection -- a reading: the pages name a w13 layout
+ *   without fixing the order), W_d [d, H].
+ *   u = W_gu x;  h_i = silu(u_i) * u_{H+i} stored in dt;  y = W_d h.
+ * y is returned unrounded (the caller stores it). */
+static void expert_row(const double *x, int64_t d, int64_t H, const void *W_gu,
+                       const void *W_d, int dt, double *h, double *y)
+{
+    for (int64_t i = 0; i < H; i++) {
+        double g = 0.0, u = 0.0;
+        for (int64_t c = 0; c < d; c++) {
+            g += ld(W_gu, dt, i * d + c) * x[c];
+            u += ld(W_gu, dt, (H + i) * d + c) * x[c];
+        }
+        double silu = g / (1.0 + exp(-g));
+        h[i] = store_as(silu * u, dt);
+    }
+    for (int64_t o = 0; o < d; o++) {
+        double s = 0.0;
+        for (int64_t i = 0; i < H; i++)
+            s += ld(W_d, dt, o * H + i) * h[i];
+        y[o] = s;
+    }
+}
+
+/* Expert FFN over rows, each with its own expert:
+ *   X [n, d] (dt), expert [n] (row r uses expert expert[r]; < 0 = skip),
+ *   W_gu_e[e] -> [2H, d], W_d_e[e] -> [d, H]  (per-expert pointers, so callers
+ *   can pass only the experts they use).
+ *   Y [n, d] double, unrounded; h_out [n, H] double (stored values), nullable. */
+void moe_ref_expert_rows(const void *X, int dt, int64_t n, int64_t d, int64_t H,
+                         const int32_t *expert, const void *const *W_gu_e,
+                         const void *const *W_d_e, double *Y, double *h_out)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < n; r++) {
+        double *x = (double *)malloc(sizeof(double) * (size_t)d);
+        double *h = (double *)malloc(sizeof(double) * (size_t)H);
+        if (expert[r] >= 0) {
+            for (int64_t c = 0; c < d; c++)
+                x[c] = ld(X, dt, r * d + c);
+            expert_row(x, d, H, W_gu_e[expert[r]], W_d_e[expert[r]], dt, h, Y + r * d);
+            if (h_out)
+                memcpy(h_out + r * H, h, sizeof(double) * (size_t)H);
+        } else {
+            for (int64_t c = 0; c < d; c++)
+                Y[r * d + c] = 0.0;
+        }
+        free(x);
+        free(h);
+    }
+}
+
+/* Weighted combine, ordered gather: c_t = sum over j = 0..k-1 (ascending) of
+ * w[t,j] * Y[slot_row[t*k+j]], skipping slots < 0 (dropped: contributes zero,
+ * the survivors are not renormalised).  w may be NULL (weight 1).  Y [*, d] in
+ * dt; c [T, d] double, unrounded. */
+void moe_ref_combine(const void *Y, int dt, const int32_t *slot_row, const float *w,
+                     int64_t T, int32_t k, int64_t d, double *c)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; t++) {
+        for (int64_t o = 0; o < d; o++)
+            c[t * d + o] = 0.0;
+        for (int32_t j = 0; j < k; j++) {
+            int32_t row = slot_row[t * k + j];
+            if (row < 0)
+                continue;
+            double wj = w ? (double)w[t * k + j] : 1.0;
+            for (int64_t o = 0; o < d; o++)
+                c[t * d + o] += wj * ld(Y, dt, (int64_t)row * d + o);
+        }
+    }
+}
+
+/* ------------------------------------------------------------- full layer --- */
+
+typedef struct {
+    int64_t T, D, L;      /* L = 0: no latent; routing and experts act on x */
+    int32_t E, k;
+    int64_t H;            /* routed expert hidden width */
+    int32_t n_shared;
+    int64_t Hs;           /* shared expert hidden width */
+    int32_t dtype;        /* DT_F32 or DT_BF16: storage of activations and weights */
+    double eps;
+} moe_ref_dims;
+
+typedef struct {
+    const void *W_dn;             /* [L, D] */
+    const float *norm_g;          /* [L], NULL = ones */
+    const float *W_r;             /* [E, d_r] float32 (d_r = L, or D without latent) */
+    const float *b_r;             /* [E], NULL = zeros */
+    const void *const *W_gu_e;    /* E pointers to [2H, d_e] */
+    const void *const *W_d_e;     /* E pointers to [d_e, H] */
+    const void *W_up;             /* [D, L] */
+    const void *W_gu_s;           /* [n_shared, 2Hs, D] */
+    const void *W_d_s;            /* [n_shared, D, Hs] */
+} moe_ref_weights;
+
+/* Router/expert input of token t as exact doubles (length d_r = L, or D
+ * without latent):
+ *   without latent: x_t;
+ *   with latent:    z = RMSNorm(W_dn x_t) * g, computed in double. */
+static void token_input(const moe_ref_dims *dm, const moe_ref_weights *W, const void *x,
+                        int64_t t, double *r)
+{
+    const int dt = dm->dtype;
+    if (dm->L > 0) {
+        double *zp = (double *)malloc(sizeof(double) * (size_t)dm->L);
+        for (int64_t o = 0; o < dm->L; o++) {
+            double s = 0.0;
+            for (int64_t c = 0; c < dm->D; c++)
+                s += ld(W->W_dn, dt, o * dm->D + c) * ld(x, dt, t * dm->D + c);
+            zp[o] = s;
+        }
+        moe_ref_rmsnorm_row(zp, dm->L, W->norm_g, dm->eps, r);
+        free(zp);
+    } else {
+        for (int64_t c = 0; c < dm->D; c++)
+            r[c] = ld(x, dt, t * dm->D + c);
+    }
+}
+
+/* Router part of the layer for a list of tokens.
+ *   x [T, D] (dt); tok [n] token indices.
+ * Per token t (outputs indexed by position i in tok):
+ *   without latent: r = x_t;
+ *   with latent:    z_pre = W_dn x_t;  z = RMSNorm(z_pre) * g  (double);
+ *   router input    h32 = float32(r or z);  expert input h_e = dt(r or z).
+ *   logits = W_r h32 + b_r, summed in double from float32 operands and stored
+ *   as float32 (logits64 keeps the double sum).
+ *   ids/w from moe_ref_topk on the float32 logits.
+ * Reading: the router reads the normalised latent (project, normalise, route),
+ * in float32, as the spec fixes the router's precision.
+ * Any output pointer may be NULL except ids and w. */
+void moe_ref_route_tokens(const moe_ref_dims *dm, const moe_ref_weights *W, const void *x,
+                          const int32_t *tok, int64_t n, double *z_out, float *logits32,
+                          double *logits64, int32_t *ids, float *w)
+{
+    const int64_t d_r = dm->L > 0 ? dm->L : dm->D;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; i++) {
+        const int64_t t = tok[i];
+        double *r = (double *)malloc(sizeof(double) * (size_t)d_r);
+        float *l32 = (float *)malloc(sizeof(float) * (size_t)dm->E);
+        token_input(dm, W, x, t, r);
+        if (z_out)
+            memcpy(z_out + i * d_r, r, sizeof(double) * (size_t)d_r);
+        for (int32_t e = 0; e < dm->E; e++) {
+            double s = 0.0;
+            for (int64_t c = 0; c < d_r; c++)
+                s += (double)W->W_r[(int64_t)e * d_r + c] * (double)(float)r[c];
+            if (W->b_r)
+                s += (double)W->b_r[e];
+            l32[e] = (float)s;
+            if (logits32)
+                logits32[i * dm->E + e] = (float)s;
+            if (logits64)
+                logits64[i * dm->E + e] = s;
+        }
+        moe_ref_topk(l32, 1, dm->E, dm->k, ids + i * dm->k, w + i * dm->k);
+        free(r);
+        free(l32);
+    }
+}
+
+/* Output part of the layer for a list of tokens, given each token's routing.
+ *   ids/w [n, k] for the tokens in tok (position i), keep [n, k] (1 kept,
+ *   0 dropped by capacity; NULL = all kept).
+ * Per token:
+ *   h_e = dt(r or z)  (r = x_t without latent; z from moe_ref_route_tokens' rule)
+ *   Y_j = dt(FFN_{ids_j}(h_e)) for kept j
+ *   c   = dt(sum_j w_j Y_j)    (ordered, ascending j)
+ *   routed = W_up c  (latent)  or  c  (no latent)
+ *   shared = sum_i W_d_s[i] * dt(silu(W1_i x) * (W3_i x)),  W_gu_s[i] = [W1_i; W3_i]
+ *   y = routed + shared, unrounded double.
+ * c_out [n, d_e] (the stored c) may be NULL. */
+void moe_ref_output_tokens(const moe_ref_dims *dm, const moe_ref_weights *W, const void *x,
+                           const int32_t *tok, int64_t n, const int32_t *ids, const float *w,
+                           const int32_t *keep, double *y, double *c_out)
+{
+    const int64_t d_e = dm->L > 0 ? dm->L : dm->D;
+    const int dt = dm->dtype;
+    const int32_t k = dm->k;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t i = 0; i < n; i++) {
+        const int64_t t = tok[i];
+        double *he = (double *)malloc(sizeof(double) * (size_t)d_e);
+        double *xv = (double *)malloc(sizeof(double) * (size_t)dm->D);
+        double *Yj = (double *)malloc(sizeof(double) * (size_t)d_e);
+        double *hbuf = (double *)malloc(sizeof(double) * (size_t)(dm->H > dm->Hs ? dm->H : dm->Hs));
+        double *c = (double *)calloc((size_t)d_e, sizeof(double));
+        for (int64_t cc = 0; cc < dm->D; cc++)
+            xv[cc] = ld(x, dt, t * dm->D + cc);
+        token_input(dm, W, x, t, he);
+        for (int64_t o = 0; o < d_e; o++)
+            he[o] = store_as(he[o], dt);   /* expert input is stored in dt */
+        /* routed experts and the ordered weighted combine */
+        for (int32_t j = 0; j < k; j++) {
+            if (keep && !keep[i * k + j])
+                continue;
+            int32_t e = ids[i * k + j];
+            expert_row(he, d_e, dm->H, W->W_gu_e[e], W->W_d_e[e], dt, hbuf, Yj);
+            double wj = (double)w[i * k + j];
+            for (int64_t o = 0; o < d_e; o++)
+                c[o] += wj * store_as(Yj[o], dt);
+        }
+        for (int64_t o = 0; o < d_e; o++)
+            c[o] = store_as(c[o], dt);
+        if (c_out)
+            memcpy(c_out + i * d_e, c, sizeof(double) * (size_t)d_e);
+        double *yo = y + i * dm->D;
+        /* up-projection */
+        for (int64_t o = 0; o < dm->D; o++) {
+            if (dm->L > 0) {
+                double s = 0.0;
+                for (int64_t cc = 0; cc < dm->L; cc++)
+                    s += ld(W->W_up, dt, o * dm->L + cc) * c[cc];
+                yo[o] = s;
+            } else {
+                yo[o] = c[o];
+            }
+        }
+        /* shared experts: unweighted, every token */
+        for (int32_t si = 0; si < dm->n_shared; si++) {
+            const int64_t Hs = dm->Hs, D = dm->D;
+            const int64_t gu_off = (int64_t)si * 2 * Hs * D;
+            const int64_t d_off = (int64_t)si * D * Hs;
+            for (int64_t q = 0; q < Hs; q++) {
+                double g = 0.0, u = 0.0;
+                for (int64_t cc = 0; cc < D; cc++) {
+                    g += ld(W->W_gu_s, dt, gu_off + q * D + cc) * xv[cc];
+                    u += ld(W->W_gu_s, dt, gu_off + (Hs + q) * D + cc) * xv[cc];
+                }
+                hbuf[q] = store_as(g / (1.0 + exp(-g)) * u, dt);
+            }
+            for (int64_t o = 0; o < D; o++) {
+                double s = 0.0;
+                for (int64_t q = 0; q < Hs; q++)
+                    s += ld(W->W_d_s, dt, d_off + o * Hs + q) * hbuf[q];
+                yo[o] += s;
+            }
+        }
+        free(he);
+        free(xv);
+        free(Yj);
+        free(hbuf);
+        free(c);
+    }
+}
