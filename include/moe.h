@@ -1,0 +1,219 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts layer forward.
+ *
+ * The layer (Marin 535B-A23B: the half of a training run nobody usually shows
+ * you, section "What is actually being trained"; Marin Begins Open Training of a
+ * 535B-Parameter MoE Model, section 2 "How the Sparse Model Is Organized"):
+ *   z   = RMSNorm(x W_dn^T) * g                 latent (optional)
+ *   l   = z W_r^T + b_r                          router logits, float32
+ *   ids = top-k of l; w = softmax(l) over all experts, renormalised over the k
+ *   Y_a = W_d[e] (silu(W_g[e] z) * (W_u[e] z))   per kept assignment a = (t, j)
+ *   c_t = sum_j w_tj Y_(t,j)                      ordered, dropped j contribute 0
+ *   y   = c W_up^T + sum_i SwiGLU_i(x)            shared experts see every token
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are device memory on the current HIP device; the
+ *     caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; all work is enqueued on `stream` (a hipStream_t, NULL = the
+ *     null stream) in call order, and device-written outputs are valid once that
+ *     stream has been synchronised.
+ *   - Matrices are row-major and contiguous.  Projections use the [out, in]
+ *     layout, so both operands of every product are contiguous along the
+ *     reduction.  Pointers must be 16-byte aligned.
+ *   - Every shape, dtype, alignment and workspace check runs on the host before
+ *     anything is enqueued; a failed check returns an error code, enqueues
+ *     nothing and writes nothing.  MOE_ELAUNCH reports a launch failure seen by
+ *     hipGetLastError; faults inside a kernel surface at the caller's next sync.
+ *   - The library keeps no mutable global state: calls on different streams or
+ *     devices may run concurrently (a shared handle that hung under concurrent
+ *     calls is reported in Marin: Week of July 6th summary, JaxPP paragraph).
+ *   - Workspaces are scratch owned by the caller; their contents on entry do not
+ *     matter and on return are unspecified.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_EINVAL = 1,     /* null pointer where one is required, bad flag */
+    MOE_ESHAPE = 2,     /* a size out of range or not a supported multiple */
+    MOE_EDTYPE = 3,     /* unsupported dtype combination */
+    MOE_EALIGN = 4,     /* pointer not 16-byte aligned */
+    MOE_EWORKSPACE = 5, /* workspace missing or smaller than required */
+    MOE_ELAUNCH = 6     /* a kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* A hipStream_t, passed as an opaque pointer so that this header needs no HIP
+ * headers.  NULL is the null stream. */
+typedef void *moe_stream;
+
+/* Version of this ABI (changes when a signature or struct changes). */
+int moe_abi_version(void);
+
+/* Name of a status code (static string). */
+const char *moe_status_str(moe_status s);
+
+/* ------------------------------------------------------------------ route -- */
+/* Router: optional RMSNorm, float32 logits, top-k, routing weights.
+ * Follows the spec's order: softmax over all E experts, keep the k largest,
+ * renormalise them to sum to one.  The largest logits are the largest
+ * probabilities, so selection is taken on the float32 logits: larger first,
+ * equal values (+0 and -0 are equal) to the lower expert id, NaN below all.
+ * Router weight and bias are free parameters (Marin 535B-A23B article, section
+ * "The one knob nobody pinned"); a more accurate router changed top-8 for ~9%
+ * of tokens there (section "What I'd take from it"), which is why the router is
+ * float32 throughout.
+ *   h          (device) [T, d_r] in h_dt (MOE_F32 or MOE_BF16)
+ *   norm_g     (device) [d_r] float32 gain, NULL = ones; used if apply_norm
+ *   apply_norm nonzero: r = h / sqrt(mean(h^2) + eps) * g, else r = h
+ *   W_r        (device) [E, d_r] float32;  b_r (device) [E] float32 or NULL
+ *   r_out      (device) [T, d_r] in r_dt, or NULL: the router input r, stored
+ *   logits_out (device) [T, E] float32, or NULL
+ *   topk_ids   (device) [T, k] int32: j-th best expert of token t
+ *   topk_w     (device) [T, k] float32 routing weights
+ * Limits: 1 <= E <= 512, 1 <= k <= min(E, 16), d_r a multiple of 16, T >= 0. */
+moe_status moe_route(const void *h, moe_dtype h_dt, int64_t T, int64_t d_r,
+                     const float *norm_g, float eps, int32_t apply_norm,
+                     const float *W_r, const float *b_r, int32_t E, int32_t k,
+                     void *r_out, moe_dtype r_dt, float *logits_out,
+                     int32_t *topk_ids, float *topk_w, moe_stream stream);
+
+/* ---------------------------------------------------------------- permute -- */
+/* Group assignments by expert (the rows each expert's GEMM reads).
+ * Source: expert group boundaries passed to the grouped GEMM as cu_seqlens
+ * (Marin 535B-A23B article, section "21% to 27% MFU without stopping the run");
+ * fixed capacity with overflow dropped and reported separately (launch blog,
+ * section 2); integer capacity so no buffer overflows by a row (Marin weekly
+ * summary of September 14, hero-run engineering).
+ *   ids       (device) [n_assign] int32 expert of assignment a (a = t*k + j, or a
+ *             pool row); a negative id is padding and takes part in nothing.
+ *   capacity  rows kept per expert, < 0 = unlimited.  The kept assignments of an
+ *             expert are its first `capacity` in ascending a.
+ *   src, dst  (device) optional row copy: dst[row(a)] = src[a / src_div], rows of
+ *             `width` elements of dt.  Both NULL = no copy.
+ *   R_phys    rows of dst / row_src; must be >= the kept rows (n_assign suffices)
+ * Outputs (device): slot_row [n_assign] (row of a, -1 if padding or dropped),
+ *   row_src [R_phys] (assignment in each row, -1 past the last kept row),
+ *   counts [E] (before the capacity cut), offsets [E+1] (exclusive prefix sum of
+ *   kept rows), n_dropped [1] int64.  Integer outputs are deterministic.
+ *   ws        (device) workspace of moe_permute_workspace_size(n_assign, E) bytes.
+ * Limits: 1 <= E <= 1024, 0 <= n_assign < 2^31. */
+moe_status moe_permute(const int32_t *ids, int64_t n_assign, int32_t E, int64_t capacity,
+                       const void *src, moe_dtype dt, int64_t width, int32_t src_div,
+                       void *dst, int64_t R_phys, int32_t *slot_row, int32_t *row_src,
+                       int32_t *counts, int32_t *offsets, int64_t *n_dropped,
+                       void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_permute_workspace_size(int64_t n_assign, int32_t E);
+
+/* ------------------------------------------------------------ grouped FFN -- */
+/* Per-expert gated MLP over contiguous row groups (the pages' ragged_dot with
+ * group sizes: Marin: Week of April 26th summary; the gated expert MLP: Marin:
+ * Week of July 6th summary, JaxPP paragraph).  Rows [offsets[e], offsets[e+1])
+ * of X go through expert e:
+ *   Y[r] = W_d[e] (silu(G) * U),  [G | U] = W_gu[e] X[r]
+ * with G the first H rows of W_gu[e] and U the last H.  silu is computed with
+ * an accurate exp and division (an approximate activation broke parity on the
+ * pages).  Only active rows are computed; rows >= offsets[E] are not touched.
+ *   X      (device) [R_phys, d] in dt;  offsets (device) [E+1] int32, ascending,
+ *          offsets[0] = 0, offsets[E] <= R_phys
+ *   W_gu   (device) [E, 2H, d];  W_d (device) [E, d, H]  (dt)
+ *   Y      (device) [R_phys, d] in dt
+ *   ws     (device) moe_grouped_ffn_workspace_size(E, R_phys, H, dt) bytes
+ * Accumulation is float32; the hidden h is stored in dt.
+ * Limits: d and H multiples of 32, E <= 1024. */
+moe_status moe_grouped_ffn(const void *X, const int32_t *offsets, int32_t E, int64_t R_phys,
+                           const void *W_gu, const void *W_d, int64_t d, int64_t H,
+                           moe_dtype dt, void *Y, void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt);
+
+/* ---------------------------------------------------------------- combine -- */
+/* Ordered weighted gather (Marin weekly summary of September 14: an ordered
+ * gather replaced an atomic scatter-add so repeated scoring is bitwise exact):
+ *   out[t] = sum over j = 0..k-1 in order of w[t*k+j] * Y[slot_row[t*k+j]],
+ * skipping slots < 0 (a dropped assignment contributes zero; the others are not
+ * renormalised -- launch blog, section 4).  float32 accumulation.
+ *   Y (device) [*, width] dt;  slot_row (device) [T*k];  w (device) [T*k] float32
+ *   or NULL (weights 1);  out (device) [T, width] dt.
+ *   flags: MOE_COMBINE_KEEP_UNROUTED leaves out[t] untouched when every slot of t
+ *   is < 0 (unpermute of a receiver pool whose padding rows must survive);
+ *   otherwise such a row is written as zeros. */
+#define MOE_COMBINE_KEEP_UNROUTED 1
+moe_status moe_combine(const void *Y, moe_dtype dt, const int32_t *slot_row, const float *w,
+                       int64_t T, int32_t k, int64_t width, void *out, int32_t flags,
+                       moe_stream stream);
+
+/* ------------------------------------------------------------ full layer -- */
+typedef struct {
+    int64_t T;          /* tokens */
+    int64_t D;          /* model width */
+    int64_t L;          /* latent width; 0 = no latent (routing and experts act on x) */
+    int32_t E;          /* routed experts */
+    int32_t k;          /* experts per token */
+    int64_t H;          /* routed expert hidden width */
+    int32_t n_shared;   /* shared experts (0..3) */
+    int64_t Hs;         /* shared expert hidden width */
+    moe_dtype dtype;    /* storage of x, weights, intermediates and y */
+    float eps;          /* RMSNorm epsilon */
+    int64_t capacity;   /* rows kept per expert, < 0 = unlimited (dropless) */
+} moe_layer_desc;
+
+typedef struct {
+    const void *W_dn;    /* [L, D] dtype (latent only) */
+    const float *norm_g; /* [L] float32 or NULL = ones (latent only) */
+    const float *W_r;    /* [E, d_r] float32, d_r = L or D */
+    const float *b_r;    /* [E] float32 or NULL */
+    const void *W_gu;    /* [E, 2H, d_e] dtype, d_e = L or D; gate rows then up rows */
+    const void *W_d;     /* [E, d_e, H] dtype */
+    const void *W_up;    /* [D, L] dtype (latent only) */
+    const void *W_gu_s;  /* [n_shared, 2Hs, D] dtype */
+    const void *W_d_s;   /* [n_shared, D, Hs] dtype */
+} moe_layer_weights;
+
+/* Stage boundaries at which moe_layer_fwd records caller-supplied events. */
+enum {
+    MOE_EV_START = 0,      /* before the first kernel */
+    MOE_EV_DOWNPROJ = 1,   /* after x W_dn^T */
+    MOE_EV_ROUTE = 2,      /* after RMSNorm + router + top-k */
+    MOE_EV_PERMUTE = 3,    /* after grouping */
+    MOE_EV_GEMM1 = 4,      /* after gate/up + SwiGLU */
+    MOE_EV_GEMM2 = 5,      /* after the down projection of the experts */
+    MOE_EV_COMBINE = 6,    /* after the weighted combine */
+    MOE_EV_SHARED = 7,     /* after the shared experts' gate/up + SwiGLU */
+    MOE_EV_OUTPUT = 8,     /* after up-projection + shared down (the output) */
+    MOE_EV_COUNT = 9
+};
+
+typedef struct {
+    float *logits;        /* [T, E] or NULL */
+    int32_t *ids;         /* [T, k] or NULL */
+    float *w;             /* [T, k] or NULL */
+    int32_t *counts;      /* [E] or NULL */
+    int32_t *offsets;     /* [E+1] or NULL */
+    int64_t *n_dropped;   /* [1] or NULL */
+    int32_t *slot_row;    /* [T*k] or NULL */
+    void **events;        /* MOE_EV_COUNT hipEvent_t handles, or NULL: each is
+                             recorded on `stream` at its stage boundary (timing) */
+} moe_layer_aux;
+
+/* The whole layer forward.  x (device) [T, D] dtype -> y (device) [T, D] dtype.
+ * aux may be NULL; each of its pointers may be NULL.  ws: device workspace of
+ * moe_layer_workspace_size(d) bytes.  Limits: those of the parts, plus D, L, H,
+ * Hs multiples of 32 and n_shared <= 3. */
+moe_status moe_layer_fwd(const moe_layer_desc *d, const moe_layer_weights *W, const void *x,
+                         void *y, const moe_layer_aux *aux, void *ws, size_t ws_bytes,
+                         moe_stream stream);
+size_t moe_layer_workspace_size(const moe_layer_desc *d);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

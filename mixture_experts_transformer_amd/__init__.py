@@ -1,0 +1,11 @@
+"""MI355X-native forward pass of one routed mixture-of-experts layer.
+
+The compute lives in libmoe.so (hand-written gfx950 HIP kernels behind the C ABI
+of include/moe.h); this package is its thin Python binding.  Importing it fails
+loudly if the library has not been built.
+"""
+from .moe import (  # noqa: F401
+    LayerDesc, MoeError, abi_version, layer_desc, moe_combine, moe_grouped_ffn,
+    moe_grouped_ffn_workspace_size, moe_layer_fwd, moe_layer_workspace_size, moe_permute,
+    moe_permute_workspace_size, moe_route, status_str, MOE_COMBINE_KEEP_UNROUTED, EV_NAMES,
+    MOE_EV_COUNT)

@@ -1,0 +1,406 @@
+// C ABI of libmoe: host-side validation, workspace carving and the order in
+// which the layer's kernels are enqueued.  Every check runs before anything
+// is enqueued; nothing here allocates, frees or synchronises device memory,
+// and no mutable global state is kept.
+#include <string.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline int esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+inline bool dt_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+inline hipStream_t hs(moe_stream s) { return (hipStream_t)s; }
+
+#define MOE_TRY(expr)                              \
+    do {                                           \
+        if ((expr) != hipSuccess) return MOE_ELAUNCH; \
+    } while (0)
+
+// Carves consecutive 256-byte-aligned regions out of a workspace (or, with a
+// null base, only measures them).
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base((char*)b) {}
+    template <typename P>
+    P* take(size_t bytes) {
+        P* p = base ? (P*)(base + off) : nullptr;
+        off += a256(bytes > 0 ? bytes : 1);
+        return p;
+    }
+};
+
+int64_t grouped_tile_bound(int64_t rows, int G, int64_t N, int epi) {
+    const int64_t BM = gemm_block_m();
+    const int64_t cols = gemm_cols_per_tile(epi);
+    return ((rows + BM - 1) / BM + G) * ((N + cols - 1) / cols);
+}
+int64_t dense_tiles(int64_t rows, int64_t N, int epi) {
+    const int64_t BM = gemm_block_m();
+    const int64_t cols = gemm_cols_per_tile(epi);
+    return ((rows + BM - 1) / BM) * ((N + cols - 1) / cols);
+}
+
+GemmParams gemm_base() {
+    GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.a_div = 1;
+    p.group_m = 1;
+    return p;
+}
+
+// Grouped gated MLP over row groups: h = SwiGLU(X W_gu[g]^T), Y = h W_d[g]^T.
+// X rows optionally gathered (a_rows / a_div).
+moe_status grouped_ffn_impl(const void* X, int64_t ldx, const int32_t* a_rows, int a_div,
+                            const int32_t* offsets, const int32_t* tile_prefix, int E,
+                            int64_t R_rows, const void* W_gu, const void* W_d, int64_t d,
+                            int64_t H, moe_dtype dt, void* h, void* Y, hipStream_t s) {
+    GemmParams p = gemm_base();
+    p.offsets = offsets;
+    p.tile_prefix = tile_prefix;
+    p.G = E;
+    p.a_rows = a_rows;
+    p.a_div = a_div;
+    p.b_group_rows = 2 * H;
+    p.N = H;
+    p.n_per = H;
+    p.seg[0] = GemmSeg{X, ldx, W_gu, d, (int32_t)d};
+    p.nseg = 1;
+    p.C = h;
+    p.ldc = H;
+    MOE_TRY(launch_gemm(p, dt, false, EPI_SWIGLU, grouped_tile_bound(R_rows, E, H, EPI_SWIGLU), s));
+    return MOE_OK;
+}
+
+moe_status grouped_down_impl(const void* h, const int32_t* offsets, const int32_t* tile_prefix,
+                             int E, int64_t R_rows, const void* W_d, int64_t d, int64_t H,
+                             moe_dtype dt, void* Y, hipStream_t s) {
+    GemmParams p = gemm_base();
+    p.offsets = offsets;
+    p.tile_prefix = tile_prefix;
+    p.G = E;
+    p.b_group_rows = d;
+    p.N = d;
+    p.seg[0] = GemmSeg{h, H, W_d, H, (int32_t)H};
+    p.nseg = 1;
+    p.C = Y;
+    p.ldc = d;
+    MOE_TRY(launch_gemm(p, dt, dt == MOE_F32, EPI_STORE,
+                        grouped_tile_bound(R_rows, E, d, EPI_STORE), s));
+    return MOE_OK;
+}
+
+struct LayerBufs {
+    float* z_pre;
+    void* z_e;
+    float* logits;
+    int32_t* ids;
+    float* w;
+    void* perm_ws;
+    int32_t* counts;
+    int32_t* offsets;
+    int64_t* n_dropped;
+    int32_t* slot_row;
+    int32_t* row_src;
+    int32_t* tile_prefix;
+    void* h;
+    void* Y;
+    void* c;
+    void* h_s;
+};
+
+LayerBufs carve_layer(const moe_layer_desc* d, void* ws, size_t* total) {
+    Carver cv(ws);
+    LayerBufs b;
+    const int64_t T = d->T, R = d->T * d->k;
+    const int64_t de = d->L > 0 ? d->L : d->D;
+    const int es = esize(d->dtype);
+    b.z_pre = d->L > 0 ? cv.take<float>((size_t)T * d->L * 4) : nullptr;
+    b.z_e = d->L > 0 ? cv.take<char>((size_t)T * d->L * es) : nullptr;
+    b.logits = cv.take<float>((size_t)T * d->E * 4);
+    b.ids = cv.take<int32_t>((size_t)R * 4);
+    b.w = cv.take<float>((size_t)R * 4);
+    b.perm_ws = cv.take<char>(permute_ws_bytes(R, d->E));
+    b.counts = cv.take<int32_t>((size_t)d->E * 4);
+    b.offsets = cv.take<int32_t>((size_t)(d->E + 1) * 4);
+    b.n_dropped = cv.take<int64_t>(8);
+    b.slot_row = cv.take<int32_t>((size_t)R * 4);
+    b.row_src = cv.take<int32_t>((size_t)R * 4);
+    b.tile_prefix = cv.take<int32_t>((size_t)(d->E + 1) * 4);
+    b.h = cv.take<char>((size_t)R * d->H * es);
+    b.Y = cv.take<char>((size_t)R * de * es);
+    b.c = cv.take<char>((size_t)T * de * es);
+    b.h_s = d->n_shared > 0 ? cv.take<char>((size_t)T * d->n_shared * d->Hs * es) : nullptr;
+    *total = cv.off;
+    return b;
+}
+
+moe_status check_layer(const moe_layer_desc* d, const moe_layer_weights* W, const void* x,
+                       const void* y) {
+    if (!d || !W || !x || !y) return MOE_EINVAL;
+    if (!dt_ok(d->dtype)) return MOE_EDTYPE;
+    if (d->T < 0 || d->D <= 0 || d->L < 0 || d->H <= 0) return MOE_ESHAPE;
+    if (d->E < 1 || d->E > 512 || d->k < 1 || d->k > 16 || d->k > d->E) return MOE_ESHAPE;
+    if (d->n_shared < 0 || d->n_shared > 3 || (d->n_shared > 0 && d->Hs <= 0)) return MOE_ESHAPE;
+    if (d->D % 32 || d->L % 32 || d->H % 32 || (d->n_shared > 0 && d->Hs % 32)) return MOE_ESHAPE;
+    if (d->T * d->k >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!(d->eps >= 0.0f)) return MOE_EINVAL;
+    if (!W->W_r || !W->W_gu || !W->W_d) return MOE_EINVAL;
+    if (d->L > 0 && (!W->W_dn || !W->W_up)) return MOE_EINVAL;
+    if (d->n_shared > 0 && (!W->W_gu_s || !W->W_d_s)) return MOE_EINVAL;
+    const void* ptrs[] = {x, y, W->W_dn, W->norm_g, W->W_r, W->b_r, W->W_gu, W->W_d, W->W_up,
+                          W->W_gu_s, W->W_d_s};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return kAbiVersion; }
+
+const char* moe_status_str(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_EINVAL: return "invalid argument";
+        case MOE_ESHAPE: return "unsupported shape";
+        case MOE_EDTYPE: return "unsupported dtype";
+        case MOE_EALIGN: return "pointer not 16-byte aligned";
+        case MOE_EWORKSPACE: return "workspace too small";
+        case MOE_ELAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+// ---------------------------------------------------------------- route ----
+moe_status moe_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d_r, const float* norm_g,
+                     float eps, int32_t apply_norm, const float* W_r, const float* b_r, int32_t E,
+                     int32_t k, void* r_out, moe_dtype r_dt, float* logits_out, int32_t* topk_ids,
+                     float* topk_w, moe_stream stream) {
+    if (T < 0 || d_r <= 0 || d_r % 16) return MOE_ESHAPE;
+    if (E < 1 || E > 512 || k < 1 || k > 16 || k > E) return MOE_ESHAPE;
+    if (!dt_ok(h_dt) || (r_out && !dt_ok(r_dt))) return MOE_EDTYPE;
+    if (T > 0 && (!h || !W_r || !topk_ids || !topk_w)) return MOE_EINVAL;
+    if (!(eps >= 0.0f)) return MOE_EINVAL;
+    const void* ptrs[] = {h, norm_g, W_r, b_r, r_out, logits_out, topk_ids, topk_w};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if (T == 0) return MOE_OK;
+    MOE_TRY(launch_route(h, h_dt, T, d_r, norm_g, eps, apply_norm, W_r, b_r, E, k, r_out, r_dt,
+                         logits_out, topk_ids, topk_w, hs(stream)));
+    return MOE_OK;
+}
+
+// -------------------------------------------------------------- permute ----
+size_t moe_permute_workspace_size(int64_t n_assign, int32_t E) {
+    if (n_assign < 0 || E < 1) return 0;
+    return permute_ws_bytes(n_assign, E);
+}
+
+moe_status moe_permute(const int32_t* ids, int64_t n_assign, int32_t E, int64_t capacity,
+                       const void* src, moe_dtype dt, int64_t width, int32_t src_div, void* dst,
+                       int64_t R_phys, int32_t* slot_row, int32_t* row_src, int32_t* counts,
+                       int32_t* offsets, int64_t* n_dropped, void* ws, size_t ws_bytes,
+                       moe_stream stream) {
+    if (E < 1 || E > 1024) return MOE_ESHAPE;
+    if (n_assign < 0 || n_assign >= ((int64_t)1 << 31) || R_phys < 0) return MOE_ESHAPE;
+    const int64_t max_kept = capacity < 0 ? n_assign
+                                          : (capacity * E < n_assign ? capacity * E : n_assign);
+    if (R_phys < max_kept || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!counts || !offsets || !n_dropped) return MOE_EINVAL;
+    if (n_assign > 0 && (!ids || !slot_row)) return MOE_EINVAL;
+    if (R_phys > 0 && !row_src) return MOE_EINVAL;
+    if ((src == nullptr) != (dst == nullptr)) return MOE_EINVAL;
+    if (src) {
+        if (!dt_ok(dt)) return MOE_EDTYPE;
+        if (width <= 0 || (width * esize(dt)) % 16 || src_div < 1) return MOE_ESHAPE;
+    }
+    const void* ptrs[] = {ids, src, dst, slot_row, row_src, counts, offsets, n_dropped, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if (!ws || ws_bytes < permute_ws_bytes(n_assign, E)) return MOE_EWORKSPACE;
+    MOE_TRY(launch_permute(ids, n_assign, E, capacity, src, src ? esize(dt) : 0, width, src_div,
+                           dst, R_phys, slot_row, row_src, counts, offsets, n_dropped, nullptr, 0,
+                           ws, hs(stream)));
+    return MOE_OK;
+}
+
+// ---------------------------------------------------------- grouped FFN ----
+size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt) {
+    if (E < 1 || R_phys < 0 || H <= 0 || !dt_ok(dt)) return 0;
+    Carver cv(nullptr);
+    cv.take<int32_t>((size_t)(E + 1) * 4);
+    cv.take<char>((size_t)R_phys * H * esize(dt));
+    return cv.off;
+}
+
+moe_status moe_grouped_ffn(const void* X, const int32_t* offsets, int32_t E, int64_t R_phys,
+                           const void* W_gu, const void* W_d, int64_t d, int64_t H, moe_dtype dt,
+                           void* Y, void* ws, size_t ws_bytes, moe_stream stream) {
+    if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (d <= 0 || H <= 0 || d % 32 || H % 32) return MOE_ESHAPE;
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (!offsets || !W_gu || !W_d || (R_phys > 0 && (!X || !Y))) return MOE_EINVAL;
+    const void* ptrs[] = {X, offsets, W_gu, W_d, Y, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    const size_t need = moe_grouped_ffn_workspace_size(E, R_phys, H, dt);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    Carver cv(ws);
+    int32_t* tp = cv.take<int32_t>((size_t)(E + 1) * 4);
+    void* h = cv.take<char>((size_t)R_phys * H * esize(dt));
+    hipStream_t s = hs(stream);
+    MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tp, s));
+    moe_status st = grouped_ffn_impl(X, d, nullptr, 1, offsets, tp, E, R_phys, W_gu, W_d, d, H, dt,
+                                     h, Y, s);
+    if (st != MOE_OK) return st;
+    return grouped_down_impl(h, offsets, tp, E, R_phys, W_d, d, H, dt, Y, s);
+}
+
+// -------------------------------------------------------------- combine ----
+moe_status moe_combine(const void* Y, moe_dtype dt, const int32_t* slot_row, const float* w,
+                       int64_t T, int32_t k, int64_t width, void* out, int32_t flags,
+                       moe_stream stream) {
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (T < 0 || k < 1 || k > 64 || width <= 0 || (width * esize(dt)) % 16) return MOE_ESHAPE;
+    if (flags & ~MOE_COMBINE_KEEP_UNROUTED) return MOE_EINVAL;
+    if (T > 0 && (!Y || !slot_row || !out)) return MOE_EINVAL;
+    const void* ptrs[] = {Y, slot_row, w, out};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    MOE_TRY(launch_combine(Y, dt, slot_row, w, T, k, width, out, flags, hs(stream)));
+    return MOE_OK;
+}
+
+// ----------------------------------------------------------- full layer ----
+size_t moe_layer_workspace_size(const moe_layer_desc* d) {
+    if (!d || d->T < 0 || d->E < 1 || d->k < 1 || !dt_ok(d->dtype)) return 0;
+    size_t total = 0;
+    carve_layer(d, nullptr, &total);
+    return total;
+}
+
+moe_status moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* W, const void* x,
+                         void* y, const moe_layer_aux* aux, void* ws, size_t ws_bytes,
+                         moe_stream stream) {
+    moe_status st = check_layer(d, W, x, y);
+    if (st != MOE_OK) return st;
+    if (aux) {
+        const void* ptrs[] = {aux->logits, aux->ids, aux->w, aux->counts, aux->offsets,
+                              aux->n_dropped, aux->slot_row};
+        for (const void* p : ptrs)
+            if (p && !aligned16(p)) return MOE_EALIGN;
+    }
+    size_t need = 0;
+    carve_layer(d, nullptr, &need);
+    if (!ws || ws_bytes < need || !aligned16(ws)) return MOE_EWORKSPACE;
+    if (d->T == 0) return MOE_OK;
+
+    size_t dummy;
+    LayerBufs b = carve_layer(d, ws, &dummy);
+    hipStream_t s = hs(stream);
+    const moe_dtype dt = d->dtype;
+    const int64_t T = d->T, D = d->D, L = d->L, H = d->H, Hs = d->Hs;
+    const int E = d->E, k = d->k, ns = d->n_shared;
+    const int64_t R = T * k;
+    const int64_t de = L > 0 ? L : D;
+    const int es = esize(dt);
+    float* logits = (aux && aux->logits) ? aux->logits : nullptr;
+    int32_t* ids = (aux && aux->ids) ? aux->ids : b.ids;
+    float* w = (aux && aux->w) ? aux->w : b.w;
+    int32_t* counts = (aux && aux->counts) ? aux->counts : b.counts;
+    int32_t* offsets = (aux && aux->offsets) ? aux->offsets : b.offsets;
+    int64_t* n_dropped = (aux && aux->n_dropped) ? aux->n_dropped : b.n_dropped;
+    int32_t* slot_row = (aux && aux->slot_row) ? aux->slot_row : b.slot_row;
+    void** ev = (aux && aux->events) ? aux->events : nullptr;
+    auto mark = [&](int i) -> bool {
+        return !ev || hipEventRecord((hipEvent_t)ev[i], s) == hipSuccess;
+    };
+
+    if (!mark(MOE_EV_START)) return MOE_ELAUNCH;
+    // 1. down-projection to the latent (float32 out, normalised by the router)
+    if (L > 0) {
+        GemmParams p = gemm_base();
+        p.M = T;
+        p.N = L;
+        p.seg[0] = GemmSeg{x, D, W->W_dn, D, (int32_t)D};
+        p.nseg = 1;
+        p.C = b.z_pre;
+        p.ldc = L;
+        MOE_TRY(launch_gemm(p, dt, true, EPI_STORE, dense_tiles(T, L, EPI_STORE), s));
+    }
+    if (!mark(MOE_EV_DOWNPROJ)) return MOE_ELAUNCH;
+    // 2. RMSNorm + router + top-k; the normalised latent is stored in dt for the experts
+    const void* e_in = L > 0 ? b.z_e : x;
+    MOE_TRY(launch_route(L > 0 ? (const void*)b.z_pre : x, L > 0 ? MOE_F32 : dt, T, de, W->norm_g,
+                         d->eps, L > 0 ? 1 : 0, W->W_r, W->b_r, E, k, L > 0 ? b.z_e : nullptr, dt,
+                         logits, ids, w, s));
+    if (!mark(MOE_EV_ROUTE)) return MOE_ELAUNCH;
+    // 3. group by expert (no row copy: the expert GEMM gathers its rows)
+    MOE_TRY(launch_permute(ids, R, E, d->capacity, nullptr, 0, 0, 1, nullptr, R, slot_row,
+                           b.row_src, counts, offsets, n_dropped, b.tile_prefix, gemm_block_m(),
+                           b.perm_ws, s));
+    if (!mark(MOE_EV_PERMUTE)) return MOE_ELAUNCH;
+    // 4-5. routed experts
+    st = grouped_ffn_impl(e_in, de, b.row_src, k, offsets, b.tile_prefix, E, R, W->W_gu, W->W_d,
+                          de, H, dt, b.h, b.Y, s);
+    if (st != MOE_OK) return st;
+    if (!mark(MOE_EV_GEMM1)) return MOE_ELAUNCH;
+    st = grouped_down_impl(b.h, offsets, b.tile_prefix, E, R, W->W_d, de, H, dt, b.Y, s);
+    if (st != MOE_OK) return st;
+    if (!mark(MOE_EV_GEMM2)) return MOE_ELAUNCH;
+    // 6. ordered weighted combine (straight into y when nothing follows)
+    const bool c_is_y = (L == 0 && ns == 0);
+    MOE_TRY(launch_combine(b.Y, dt, slot_row, w, T, k, de, c_is_y ? y : b.c, 0, s));
+    if (!mark(MOE_EV_COMBINE)) return MOE_ELAUNCH;
+    // 7. shared experts' gate/up + SwiGLU, all shared experts in one GEMM
+    if (ns > 0) {
+        GemmParams p = gemm_base();
+        p.M = T;
+        p.N = ns * Hs;
+        p.n_per = Hs;
+        p.seg[0] = GemmSeg{x, D, W->W_gu_s, D, (int32_t)D};
+        p.nseg = 1;
+        p.C = b.h_s;
+        p.ldc = ns * Hs;
+        MOE_TRY(launch_gemm(p, dt, false, EPI_SWIGLU, dense_tiles(T, ns * Hs, EPI_SWIGLU), s));
+    }
+    if (!mark(MOE_EV_SHARED)) return MOE_ELAUNCH;
+    // 8. y = c W_up^T + sum_i h_s,i W_d_s,i^T in one K-concatenated GEMM (one
+    //    rounding of y); without a latent, y = c + shared part.
+    if (!c_is_y) {
+        GemmParams p = gemm_base();
+        p.M = T;
+        p.N = D;
+        int nseg = 0;
+        if (L > 0) p.seg[nseg++] = GemmSeg{b.c, L, W->W_up, L, (int32_t)L};
+        for (int i = 0; i < ns; i++)
+            p.seg[nseg++] = GemmSeg{(const char*)b.h_s + (size_t)i * Hs * es, ns * Hs,
+                                    (const char*)W->W_d_s + (size_t)i * D * Hs * es, Hs,
+                                    (int32_t)Hs};
+        p.nseg = nseg;
+        p.C = y;
+        p.ldc = D;
+        int epi = EPI_STORE;
+        if (L == 0) {
+            epi = EPI_ADD;
+            p.addend = b.c;
+            p.ld_add = D;
+        }
+        MOE_TRY(launch_gemm(p, dt, dt == MOE_F32, epi, dense_tiles(T, D, epi), s));
+    }
+    if (!mark(MOE_EV_OUTPUT)) return MOE_ELAUNCH;
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,68 @@
+// Internal launch interface between the C-ABI layer (abi.hip) and the kernels.
+// Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// ------------------------------------------------------------------ GEMM ---
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ADD = 2 };
+constexpr int kMaxSeg = 4;
+
+struct GemmSeg {
+    const void* A;     // A row r: A + r * lda (elements)
+    int64_t lda;
+    const void* B;     // B row n: B + n * ldb (elements)
+    int64_t ldb;
+    int32_t K;         // reduction length of this segment (multiple of 64 bytes)
+};
+
+// C[r, n] = epi(sum over segments s of A_s[arow(r), :] . B_s[brow(g, n), :]).
+struct GemmParams {
+    int64_t M;                   // rows when offsets == nullptr
+    const int32_t* offsets;      // [G+1] row groups (device) or nullptr
+    const int32_t* tile_prefix;  // [G+1] row-tile prefix for the GEMM's BM (device)
+    int32_t G;
+    int64_t b_group_rows;        // B rows between consecutive groups' weights
+    const int32_t* a_rows;       // gather: A row of output row r = a_rows[r] / a_div
+    int32_t a_div;
+    int64_t N;                   // output columns
+    int64_t n_per;               // SwiGLU: hidden columns per [gate; up] block of B
+    int32_t group_m;             // row tiles per swizzle group
+    GemmSeg seg[kMaxSeg];
+    int32_t nseg;
+    void* C;                     // output row r: C + r * ldc
+    int64_t ldc;
+    const void* addend;          // EPI_ADD: added row r: addend + r * ld_add
+    int64_t ld_add;
+};
+
+int gemm_block_m();
+int gemm_cols_per_tile(int epi);
+hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp, hipStream_t s);
+hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,
+                       int64_t max_tiles, hipStream_t s);
+
+// ----------------------------------------------------------------- route ---
+hipError_t launch_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d, const float* g,
+                        float eps, int apply_norm, const float* W_r, const float* b_r, int E,
+                        int k, void* r_out, moe_dtype r_dt, float* logits, int32_t* ids, float* w,
+                        hipStream_t s);
+
+// --------------------------------------------------------------- permute ---
+size_t permute_ws_bytes(int64_t n, int E);
+hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity, const void* src,
+                          int elem_bytes, int64_t width, int src_div, void* dst, int64_t R_phys,
+                          int32_t* slot_row, int32_t* row_src, int32_t* counts, int32_t* offsets,
+                          int64_t* n_dropped, int32_t* tile_prefix, int tile_bm, void* ws,
+                          hipStream_t s);
+
+// --------------------------------------------------------------- combine ---
+hipError_t launch_combine(const void* Y, moe_dtype dt, const int32_t* slot_row, const float* w,
+                          int64_t T, int k, int64_t width, void* out, int flags, hipStream_t s);
+
+}  // namespace moe

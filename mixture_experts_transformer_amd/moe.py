@@ -1,0 +1,224 @@
+"""Thin Python binding of libmoe's C ABI (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe.so.  torch supplies device memory and the current HIP stream.  If the
+library is not built this module fails to import -- there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -m mixture_experts_transformer_amd.build`"
+                      " (or __graft_entry__.build()); there is no non-HIP fallback")
+_lib = C.CDLL(LIB_PATH)
+
+MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_ELAUNCH = range(7)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_COMBINE_KEEP_UNROUTED = 1
+EV_NAMES = ["start", "downproj", "route", "permute", "gemm1", "gemm2", "combine", "shared",
+            "output"]
+MOE_EV_COUNT = len(EV_NAMES)
+
+_vp, _i32, _i64, _f32, _sz = C.c_void_p, C.c_int32, C.c_int64, C.c_float, C.c_size_t
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("T", _i64), ("D", _i64), ("L", _i64), ("E", _i32), ("k", _i32), ("H", _i64),
+                ("n_shared", _i32), ("Hs", _i64), ("dtype", C.c_int), ("eps", _f32),
+                ("capacity", _i64)]
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, _vp) for n in ["W_dn", "norm_g", "W_r", "b_r", "W_gu", "W_d", "W_up",
+                                   "W_gu_s", "W_d_s"]]
+
+
+class LayerAux(C.Structure):
+    _fields_ = [("logits", _vp), ("ids", _vp), ("w", _vp), ("counts", _vp), ("offsets", _vp),
+                ("n_dropped", _vp), ("slot_row", _vp), ("events", _vp)]
+
+
+_lib.moe_abi_version.restype = C.c_int
+_lib.moe_status_str.restype = C.c_char_p
+_lib.moe_status_str.argtypes = [C.c_int]
+_lib.moe_route.restype = C.c_int
+_lib.moe_route.argtypes = [_vp, C.c_int, _i64, _i64, _vp, _f32, _i32, _vp, _vp, _i32, _i32, _vp,
+                           C.c_int, _vp, _vp, _vp, _vp]
+_lib.moe_permute.restype = C.c_int
+_lib.moe_permute.argtypes = [_vp, _i64, _i32, _i64, _vp, C.c_int, _i64, _i32, _vp, _i64, _vp, _vp,
+                             _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_permute_workspace_size.restype = _sz
+_lib.moe_permute_workspace_size.argtypes = [_i64, _i32]
+_lib.moe_grouped_ffn.restype = C.c_int
+_lib.moe_grouped_ffn.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, C.c_int, _vp, _vp,
+                                 _sz, _vp]
+_lib.moe_grouped_ffn_workspace_size.restype = _sz
+_lib.moe_grouped_ffn_workspace_size.argtypes = [_i32, _i64, _i64, C.c_int]
+_lib.moe_combine.restype = C.c_int
+_lib.moe_combine.argtypes = [_vp, C.c_int, _vp, _vp, _i64, _i32, _i64, _vp, _i32, _vp]
+_lib.moe_layer_fwd.restype = C.c_int
+_lib.moe_layer_fwd.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerWeights), _vp, _vp,
+                               C.POINTER(LayerAux), _vp, _sz, _vp]
+_lib.moe_layer_workspace_size.restype = _sz
+_lib.moe_layer_workspace_size.argtypes = [C.POINTER(LayerDesc)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.moe_status_str(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"libmoe takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoe takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoe takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes: int, device, ws):
+    if ws is not None:
+        return ws
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def abi_version() -> int:
+    return _lib.moe_abi_version()
+
+
+def status_str(s: int) -> str:
+    return _lib.moe_status_str(s).decode()
+
+
+# --------------------------------------------------------------------- route --
+def moe_route(h, W_r, k, b_r=None, norm_g=None, eps=1e-5, apply_norm=False, r_out=None,
+              logits_out=None, topk_ids=None, topk_w=None):
+    """Router on h [T, d_r].  Returns (topk_ids [T,k] int32, topk_w [T,k] float32)."""
+    T, d = h.shape
+    E = W_r.shape[0]
+    if topk_ids is None:
+        topk_ids = torch.empty((T, k), dtype=torch.int32, device=h.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=h.device)
+    r_dt = _dt(r_out) if r_out is not None else MOE_F32
+    _check(_lib.moe_route(_ptr(h), _dt(h), T, d, _ptr(norm_g), eps, int(bool(apply_norm)),
+                          _ptr(W_r), _ptr(b_r), E, k, _ptr(r_out), r_dt, _ptr(logits_out),
+                          _ptr(topk_ids), _ptr(topk_w), _stream()), "moe_route")
+    return topk_ids, topk_w
+
+
+# ------------------------------------------------------------------- permute --
+def moe_permute_workspace_size(n_assign: int, E: int) -> int:
+    return int(_lib.moe_permute_workspace_size(n_assign, E))
+
+
+def moe_permute(ids, E, capacity=-1, src=None, src_div=1, dst=None, R_phys=None, ws=None):
+    """Group assignments by expert.  Returns dict(slot_row, row_src, counts, offsets,
+    n_dropped) of device tensors (and fills dst if given)."""
+    ids = ids.reshape(-1)
+    n = ids.numel()
+    R_phys = n if R_phys is None else R_phys
+    dev = ids.device
+    out = dict(slot_row=torch.empty(n, dtype=torch.int32, device=dev),
+               row_src=torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev),
+               counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    need = moe_permute_workspace_size(n, E)
+    ws = _ws(need, dev, ws)
+    width = src.shape[-1] if src is not None else 0
+    dt = _dt(src) if src is not None else MOE_F32
+    _check(_lib.moe_permute(_ptr(ids), n, E, capacity, _ptr(src), dt, width, src_div, _ptr(dst),
+                            R_phys, _ptr(out["slot_row"]), _ptr(out["row_src"]),
+                            _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["n_dropped"]),
+                            _ptr(ws), ws.numel(), _stream()), "moe_permute")
+    out["row_src"] = out["row_src"][:R_phys]
+    return out
+
+
+# --------------------------------------------------------------- grouped FFN --
+def moe_grouped_ffn_workspace_size(E: int, R_phys: int, H: int, dtype: torch.dtype) -> int:
+    return int(_lib.moe_grouped_ffn_workspace_size(E, R_phys, H, _dt(torch.empty(0, dtype=dtype))))
+
+
+def moe_grouped_ffn(X, offsets, W_gu, W_d, Y=None, ws=None):
+    """Y[rows of e] = W_d[e] SwiGLU(W_gu[e] X[rows of e]) for row groups `offsets`."""
+    R, d = X.shape
+    E, twoH, d2 = W_gu.shape
+    H = twoH // 2
+    if Y is None:
+        Y = torch.empty_like(X)
+    ws = _ws(moe_grouped_ffn_workspace_size(E, R, H, X.dtype), X.device, ws)
+    _check(_lib.moe_grouped_ffn(_ptr(X), _ptr(offsets), E, R, _ptr(W_gu), _ptr(W_d), d, H, _dt(X),
+                                _ptr(Y), _ptr(ws), ws.numel(), _stream()), "moe_grouped_ffn")
+    return Y
+
+
+# ------------------------------------------------------------------- combine --
+def moe_combine(Y, slot_row, w, T, k, out=None, flags=0):
+    width = Y.shape[1]
+    if out is None:
+        out = torch.empty((T, width), dtype=Y.dtype, device=Y.device)
+    _check(_lib.moe_combine(_ptr(Y), _dt(Y), _ptr(slot_row), _ptr(w), T, k, width, _ptr(out),
+                            flags, _stream()), "moe_combine")
+    return out
+
+
+# ---------------------------------------------------------------- full layer --
+def layer_desc(T, D, L, E, k, H, n_shared, Hs, dtype, eps=1e-5, capacity=-1) -> LayerDesc:
+    dt = MOE_BF16 if dtype in (torch.bfloat16, "bf16") else MOE_F32
+    return LayerDesc(T, D, L, E, k, H, n_shared, Hs, dt, eps, capacity)
+
+
+def moe_layer_workspace_size(desc: LayerDesc) -> int:
+    return int(_lib.moe_layer_workspace_size(C.byref(desc)))
+
+
+def moe_layer_fwd(desc: LayerDesc, W: dict, x, y=None, aux: dict | None = None, ws=None,
+                  events=None):
+    """Whole layer forward.  W holds device tensors named as moe_layer_weights;
+    aux (optional) maps logits/ids/w/counts/offsets/n_dropped/slot_row to output
+    tensors; events (optional) is a list of MOE_EV_COUNT raw hipEvent_t handles."""
+    if y is None:
+        y = torch.empty_like(x)
+    ws = _ws(moe_layer_workspace_size(desc), x.device, ws)
+    wts = LayerWeights(*[_ptr(W.get(n)) for n, _ in LayerWeights._fields_])
+    ev_arr = None
+    auxs = None
+    if aux is not None or events is not None:
+        aux = aux or {}
+        if events is not None:
+            ev_arr = (C.c_void_p * MOE_EV_COUNT)(*events)
+        auxs = LayerAux(*[_ptr(aux.get(n)) for n, _ in LayerAux._fields_[:-1]],
+                        C.cast(ev_arr, C.c_void_p) if ev_arr is not None else None)
+    _check(_lib.moe_layer_fwd(C.byref(desc), C.byref(wts), _ptr(x), _ptr(y),
+                              C.byref(auxs) if auxs is not None else None, _ptr(ws), ws.numel(),
+                              _stream()), "moe_layer_fwd")
+    return y

@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every function include/moe.h declares, and
+rejects bad arguments on the host before anything is enqueued (no GPU needed:
+every call here fails validation, so no HIP call is made)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "mixture_experts_transformer_amd", "libmoe.so")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from mixture_experts_transformer_amd import build as B
+        B.build()
+    return C.CDLL(LIB)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_fwd"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_status_strings(lib):
+    lib.moe_status_str.restype = C.c_char_p
+    assert lib.moe_status_str(0) == b"ok"
+    assert lib.moe_status_str(5) == b"workspace too small"
+    assert lib.moe_abi_version() == 1
+
+
+def _route(lib, T=4, d=16, E=8, k=2, h=1, W=1, ids=1, w=1, hdt=0):
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+    lib.moe_route.argtypes = [vp, C.c_int, i64, i64, vp, C.c_float, i32, vp, vp, i32, i32, vp,
+                              C.c_int, vp, vp, vp, vp]
+    p = lambda x: None if not x else 4096 * x
+    return lib.moe_route(p(h), hdt, T, d, None, 1e-5, 0, p(W), None, E, k, None, 0, None,
+                         p(ids), p(w), None)
+
+
+def test_route_rejects_bad_arguments(lib):
+    assert _route(lib, k=9) == 2          # k > E
+    assert _route(lib, E=513) == 2        # E above the limit
+    assert _route(lib, k=17, E=64) == 2   # k above 16
+    assert _route(lib, d=24) == 2         # d_r not a multiple of 16
+    assert _route(lib, h=0) == 1          # null input
+    assert _route(lib, hdt=7) == 3        # bad dtype
+    assert _route(lib, T=0, h=0, W=0, ids=0, w=0) == 0   # nothing to do
+
+
+def test_permute_rejects_bad_arguments(lib):
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+    lib.moe_permute.argtypes = [vp, i64, i32, i64, vp, C.c_int, i64, i32, vp, i64, vp, vp, vp, vp,
+                                vp, vp, C.c_size_t, vp]
+    lib.moe_permute_workspace_size.restype = C.c_size_t
+    lib.moe_permute_workspace_size.argtypes = [i64, i32]
+    a = 4096
+    need = lib.moe_permute_workspace_size(1000, 16)
+    assert need > 0
+    call = lambda **kw: lib.moe_permute(
+        kw.get("ids", a), kw.get("n", 1000), kw.get("E", 16), kw.get("cap", -1), kw.get("src"),
+        1, kw.get("width", 0), 1, kw.get("dst"), kw.get("R", 1000), a, a, a, a, a,
+        kw.get("ws", a), kw.get("wsb", need), None)
+    assert call(E=0) == 2
+    assert call(E=1025) == 2
+    assert call(R=999) == 2                # fewer rows than could be kept
+    assert call(wsb=need - 1) == 5         # workspace too small
+    assert call(ws=0) == 5
+    assert call(src=a) == 1                # src without dst
+    assert call(src=a, dst=a, width=12) == 2   # row not a multiple of 16 bytes
+    assert call(ids=4100) == 4             # misaligned
+
+
+def test_layer_rejects_bad_descriptors(lib):
+    import mixture_experts_transformer_amd.moe as B
+    d = B.layer_desc(64, 128, 64, 8, 2, 64, 1, 64, "bf16")
+    W = B.LayerWeights(4096, 0, 4096, 0, 4096, 4096, 4096, 4096, 4096)
+    call = lambda desc, W=W, ws=4096, wsb=1 << 30: B._lib.moe_layer_fwd(
+        C.byref(desc), C.byref(W), 4096, 8192, None, ws, wsb, None)
+    bad = B.layer_desc(64, 128, 64, 8, 9, 64, 1, 64, "bf16")       # k > E
+    assert call(bad) == 2
+    bad = B.layer_desc(64, 100, 64, 8, 2, 64, 1, 64, "bf16")       # D not a multiple of 32
+    assert call(bad) == 2
+    bad = B.layer_desc(64, 128, 64, 8, 2, 64, 4, 64, "bf16")       # too many shared experts
+    assert call(bad) == 2
+    assert call(d, wsb=16) == 5                                    # workspace too small
+    W2 = B.LayerWeights(0, 0, 4096, 0, 4096, 4096, 4096, 4096, 4096)   # latent without W_dn
+    assert call(d, W=W2) == 1
+    need = B.moe_layer_workspace_size(d)
+    assert need > 64 * 2 * 64 * 2

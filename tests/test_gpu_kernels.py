@@ -1,0 +1,274 @@
+"""Per-entry-point parity of the HIP path against the CPU oracle, through the C ABI.
+
+Integer work (top-k ids given identical float32 logits, permutation, offsets,
+drops) must match bit for bit; float outputs within the spec's tolerance:
+max |err| <= 2e-2 x RMS(ref) for bfloat16 storage, <= 1e-5 x RMS(ref) for float32.
+Inputs are seeded synthetic data from moe_synth or built here from closed forms.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from oracle import torch_bridge as TB
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mixture_experts_transformer_amd as m
+    return m
+
+
+def _rms(a):
+    return float(np.sqrt(np.mean(np.square(a, dtype=np.float64))))
+
+
+def _assert_close(got, ref, tol, what):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = _rms(ref)
+    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
+    assert err <= tol * rms, f"{what}: max|err| {err:.3e} > {tol:g} x RMS {rms:.3e}"
+    return err / rms if rms > 0 else 0.0
+
+
+# ---------------------------------------------------------------- route ----
+
+ROUTE_SHAPES = [  # T, d_r, E, k
+    (1, 16, 1, 1),
+    (33, 64, 16, 2),        # ragged token tile
+    (1000, 128, 64, 4),
+    (8192, 64, 384, 8),     # 535B router width and expert count, full token count
+    (300, 32, 512, 16),     # largest E and k
+]
+
+
+@pytest.mark.parametrize("T,d,E,k", ROUTE_SHAPES)
+@pytest.mark.parametrize("hdt", ["f32", "bf16"])
+def test_route_topk_bit_exact_on_exact_logits(M, T, d, E, k, hdt):
+    """Integer-valued router inputs make every float32 logit exact whatever the
+    summation order, so GPU and oracle select from identical logits: ids must be
+    identical (heavy ties exercise the lower-id rule) and weights within 1e-6."""
+    g = torch.Generator().manual_seed(T * 7 + E)
+    h = torch.randint(-2, 3, (T, d), generator=g).to(TDT[hdt])
+    W = torch.randint(-3, 4, (E, d), generator=g).float()
+    b = torch.randint(-2, 3, (E,), generator=g).float() * 0.5
+    exact = (h.double() @ W.double().T + b.double()).float().numpy()
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    ids, w = M.moe_route(h.to(DEV), W.to(DEV), k, b_r=b.to(DEV), logits_out=logits)
+    torch.cuda.synchronize()
+    assert np.array_equal(logits.cpu().numpy(), exact)
+    ref_ids, ref_w = O.topk(exact, k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+
+
+def test_route_signed_zero_and_ties(M):
+    h = torch.ones((1, 16), dtype=torch.float32)
+    W = torch.zeros((8, 16))
+    W[3, 0] = -0.0
+    W[5, 0] = 1.0
+    W[6, 0] = 1.0
+    b = torch.tensor([0.0, -0.0, -1.0, 0.0, 0.0, 0.0, 0.0, -2.0])
+    ids, w = M.moe_route(h.to(DEV), W.to(DEV), 5, b_r=b.to(DEV))
+    torch.cuda.synchronize()
+    exact = (h.double() @ W.double().T + b.double()).float().numpy()
+    ref_ids, _ = O.topk(exact, 5)
+    assert ids.cpu().numpy().tolist() == ref_ids.tolist() == [[5, 6, 0, 1, 3]]
+
+
+@pytest.mark.parametrize("T,d,E,k,hdt,rdt", [(777, 3072, 384, 8, "f32", "bf16"),
+                                              (256, 128, 16, 2, "f32", "f32"),
+                                              (500, 2048, 64, 4, "bf16", "f32")])
+def test_route_rmsnorm_router_on_real_distribution(M, T, d, E, k, hdt, rdt):
+    """RMSNorm + router on Gaussian inputs: normalised rows within one storage
+    rounding, logits within float32 accumulation error, ids equal wherever the
+    oracle's k-th/(k+1)-th logit gap exceeds twice that error."""
+    g = torch.Generator().manual_seed(d + T)
+    h = (torch.randn((T, d), generator=g) * 3).to(TDT[hdt])
+    gain = (1 + 0.1 * torch.randn(d, generator=g)).float()
+    W = (torch.randn((E, d), generator=g) / math.sqrt(d)).float()
+    b = 0.1 * torch.randn(E, generator=g)
+    r_out = torch.empty((T, d), dtype=TDT[rdt], device=DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    ids, w = M.moe_route(h.to(DEV), W.to(DEV), k, b_r=b.to(DEV), norm_g=gain.to(DEV), eps=1e-5,
+                         apply_norm=True, r_out=r_out, logits_out=logits)
+    torch.cuda.synchronize()
+    # oracle: z = RMSNorm(h) * g in double, logits from float32(z)
+    hd = TB.host(h)
+    hv = O.bf16_to_f64(hd) if hdt == "bf16" else hd.astype(np.float64)
+    z = np.stack([O.rmsnorm_row(hv[t], gain.numpy(), 1e-5) for t in range(T)])
+    lg64 = z.astype(np.float32).astype(np.float64) @ W.double().numpy().T + b.double().numpy()
+    lg32 = lg64.astype(np.float32)
+    zg = r_out.float().cpu().numpy()
+    ulp = 2.0 ** -7 if rdt == "bf16" else 1e-5
+    assert np.all(np.abs(zg - z) <= ulp * np.abs(z) + 1e-30)
+    tol_l = 2e-5 * max(1.0, _rms(lg64))
+    lgg = logits.cpu().numpy()
+    assert np.max(np.abs(lgg - lg64)) <= tol_l
+    ref_ids, ref_w = O.topk(lg32, k)
+    srt = -np.sort(-lg64, axis=1)
+    clear = (srt[:, k - 1] - srt[:, k]) > 2 * tol_l if k < E else np.ones(T, bool)
+    gi = ids.cpu().numpy()
+    assert clear.mean() > 0.9
+    assert np.array_equal(gi[clear], ref_ids[clear])
+    np.testing.assert_allclose(w.cpu().numpy()[clear], ref_w[clear], rtol=0, atol=4 * tol_l)
+    # the rest is valid: every chosen expert is within the tolerance of the k-th logit
+    for t in np.flatnonzero(~clear):
+        assert np.all(lg64[t, gi[t]] >= srt[t, k - 1] - 2 * tol_l)
+
+
+# -------------------------------------------------------------- permute ----
+
+def _ids_cases():
+    rng = np.random.default_rng(0)
+    yield "uniform", rng.integers(0, 384, 65536).astype(np.int32), 384, -1
+    p = 1 / np.arange(1, 7)
+    yield "zipf6", rng.choice(6, 57713, p=p / p.sum()).astype(np.int32), 6, -1
+    yield "one_expert", np.full(10000, 3, np.int32), 16, -1
+    yield "empty_experts", rng.choice([0, 5, 63], 4097).astype(np.int32), 64, -1
+    z = rng.choice(6, 65536, p=p / p.sum()).astype(np.int32)
+    z[rng.random(65536) < 0.12] = -1
+    yield "padding", z, 6, -1
+    u = rng.integers(0, 64, 32768).astype(np.int32)
+    yield "cap110", u, 64, O.capacity(110, 100, u.size, 64)
+    yield "cap_tight", rng.choice(16, 5000, p=np.r_[0.5, np.full(15, 0.5 / 15)]).astype(np.int32), 16, 200
+    yield "single", np.array([0], np.int32), 1, -1
+    yield "E1024", rng.integers(0, 1024, 100000).astype(np.int32), 1024, -1
+    yield "empty", np.zeros(0, np.int32), 8, -1
+
+
+@pytest.mark.parametrize("case", list(_ids_cases()), ids=lambda c: c[0])
+def test_permute_bit_exact(M, case):
+    name, ids, E, cap = case
+    n = ids.size
+    ref = O.permute(ids, E, capacity=cap, R_phys=n)
+    gi = torch.from_numpy(ids).to(DEV)
+    out = M.moe_permute(gi, E, capacity=cap, R_phys=n)
+    out2 = M.moe_permute(gi, E, capacity=cap, R_phys=n)
+    torch.cuda.synchronize()
+    for key in ["counts", "offsets", "slot_row", "row_src"]:
+        got = out[key].cpu().numpy()[: ref[key].size]
+        assert np.array_equal(got, ref[key]), key
+        assert torch.equal(out[key], out2[key]), f"{key} not deterministic"
+    assert int(out["n_dropped"].item()) == ref["n_dropped"]
+
+
+@pytest.mark.parametrize("dt,width,div", [("bf16", 3072, 8), ("f32", 128, 2), ("bf16", 64, 1)])
+def test_permute_row_copy(M, dt, width, div):
+    rng = np.random.default_rng(width)
+    n, E = 4000, 24
+    ids = rng.integers(0, E, n).astype(np.int32)
+    src = torch.randn((n // div, width), generator=torch.Generator().manual_seed(1)).to(TDT[dt])
+    dst = torch.full((n, width), -7.0, dtype=TDT[dt], device=DEV)
+    M.moe_permute(torch.from_numpy(ids).to(DEV), E, src=src.to(DEV), src_div=div, dst=dst)
+    torch.cuda.synchronize()
+    ref = O.permute(ids, E)
+    assert torch.equal(dst.cpu(), src[torch.from_numpy(ref["row_src"] // div).long()])
+
+
+# ----------------------------------------------------------- grouped FFN ----
+
+def _group_counts(rng, E, kind, scale):
+    if kind == "uniform":
+        return rng.poisson(scale, E)
+    if kind == "skewed":
+        c = rng.poisson(scale, E)
+        c[rng.choice(E, max(1, E // 10), replace=False)] *= 5
+        return c
+    if kind == "sparse":
+        c = np.zeros(E, np.int64)
+        c[rng.choice(E, 3, replace=False)] = rng.integers(1, 600, 3)
+        return c
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("dt,E,d,H,kind,scale", [
+    ("bf16", 8, 128, 64, "uniform", 40),
+    ("bf16", 16, 256, 256, "skewed", 150),     # several 256-row tiles, ragged tails
+    ("bf16", 6, 3072, 3072, "sparse", 0),      # 535B expert shape, empty groups
+    ("f32", 8, 128, 96, "uniform", 70),
+    ("f32", 5, 64, 32, "sparse", 0),
+])
+def test_grouped_ffn_parity(M, dt, E, d, H, kind, scale):
+    rng = np.random.default_rng(E * d + H)
+    counts = _group_counts(rng, E, kind, scale)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    R = int(offsets[-1])
+    R_phys = R + 37                              # spare rows must stay untouched
+    g = torch.Generator().manual_seed(5)
+    X = torch.randn((R_phys, d), generator=g).to(TDT[dt])
+    W_gu = (torch.randn((E, 2 * H, d), generator=g) / math.sqrt(d)).to(TDT[dt])
+    W_d = (torch.randn((E, d, H), generator=g) / math.sqrt(H)).to(TDT[dt])
+    Y = torch.full((R_phys, d), 3.0, dtype=TDT[dt], device=DEV)
+    M.moe_grouped_ffn(X.to(DEV), torch.from_numpy(offsets).to(DEV), W_gu.to(DEV), W_d.to(DEV), Y=Y)
+    torch.cuda.synchronize()
+    expert = np.full(R_phys, -1, np.int32)
+    for e in range(E):
+        expert[offsets[e]:offsets[e + 1]] = e
+    Xh = TB.host(X)
+    sample = np.arange(R) if R <= 3000 else np.sort(rng.choice(R, 3000, replace=False))
+    Yref = O.expert_rows(Xh[sample], expert[sample], [TB.host(W_gu[e]) for e in range(E)],
+                         [TB.host(W_d[e]) for e in range(E)], H)
+    Yg = Y.float().cpu().numpy()
+    _assert_close(Yg[sample], Yref, TOL[dt], "Y")
+    assert np.all(Yg[R:] == 3.0), "rows past offsets[E] were written"
+
+
+# --------------------------------------------------------------- combine ----
+
+@pytest.mark.parametrize("dt,T,k,width", [("bf16", 8192, 8, 3072), ("f32", 256, 2, 128),
+                                          ("bf16", 1000, 4, 2048)])
+def test_combine_parity(M, dt, T, k, width):
+    rng = np.random.default_rng(T + k)
+    slot = rng.permutation(T * k).astype(np.int32)
+    slot[rng.random(T * k) < 0.05] = -1
+    slot[:k] = -1                                     # a token with every slot dropped
+    w = rng.random((T, k)).astype(np.float32)
+    Y = torch.randn((T * k, width), generator=torch.Generator().manual_seed(3)).to(TDT[dt])
+    out = M.moe_combine(Y.to(DEV), torch.from_numpy(slot).to(DEV), torch.from_numpy(w).to(DEV),
+                        T, k)
+    out2 = M.moe_combine(Y.to(DEV), torch.from_numpy(slot).to(DEV), torch.from_numpy(w).to(DEV),
+                         T, k)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "combine not bitwise repeatable"
+    ref = O.combine(TB.host(Y), slot, w, T, k)
+    got = out.float().cpu().numpy()
+    _assert_close(got, ref, TOL[dt], "c")
+    assert np.all(got[0] == 0)
+
+
+def test_combine_unpermute_keeps_unrouted_rows(M):
+    rng = np.random.default_rng(2)
+    P, width = 5000, 256
+    slot = rng.permutation(P).astype(np.int32)
+    slot[rng.random(P) < 0.2] = -1
+    Y = torch.randn((P, width), generator=torch.Generator().manual_seed(4)).bfloat16()
+    out = torch.full((P, width), 11.0, dtype=torch.bfloat16, device=DEV)
+    M.moe_combine(Y.to(DEV), torch.from_numpy(slot).to(DEV), None, P, 1, out=out,
+                  flags=M.MOE_COMBINE_KEEP_UNROUTED)
+    torch.cuda.synchronize()
+    got = out.cpu()
+    valid = slot >= 0
+    assert torch.equal(got[torch.from_numpy(valid)], Y[torch.from_numpy(slot[valid]).long()])
+    assert torch.all(got[torch.from_numpy(~valid)] == 11.0)
+
+
+# ------------------------------------------------------------- argument checks ----
+
+def test_errors_are_reported_not_launched(M):
+    h = torch.zeros((4, 16), device=DEV)
+    W = torch.zeros((4, 16), device=DEV)
+    with pytest.raises(M.MoeError) as e:
+        M.moe_route(h, W, 5)                       # k > E
+    assert "shape" in str(e.value)
+    with pytest.raises(M.MoeError):
+        M.moe_route(torch.zeros((4, 24), device=DEV), torch.zeros((4, 24), device=DEV), 2)
