@@ -14,6 +14,8 @@ import torch
 from oracle import oracle as O
 from oracle import torch_bridge as TB
 
+from gpu_util import assert_close
+
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
@@ -29,15 +31,6 @@ def M():
 
 def _rms(a):
     return float(np.sqrt(np.mean(np.square(a, dtype=np.float64))))
-
-
-def _assert_close(got, ref, tol, what):
-    got = np.asarray(got, np.float64)
-    ref = np.asarray(ref, np.float64)
-    rms = _rms(ref)
-    err = float(np.max(np.abs(got - ref))) if got.size else 0.0
-    assert err <= tol * rms, f"{what}: max|err| {err:.3e} > {tol:g} x RMS {rms:.3e}"
-    return err / rms if rms > 0 else 0.0
 
 
 # ---------------------------------------------------------------- route ----
@@ -219,7 +212,7 @@ def test_grouped_ffn_parity(M, dt, E, d, H, kind, scale):
     Yref = O.expert_rows(Xh[sample], expert[sample], [TB.host(W_gu[e]) for e in range(E)],
                          [TB.host(W_d[e]) for e in range(E)], H)
     Yg = Y.float().cpu().numpy()
-    _assert_close(Yg[sample], Yref, TOL[dt], "Y")
+    assert_close(Yg[sample], Yref, dt, "Y")
     assert np.all(Yg[R:] == 3.0), "rows past offsets[E] were written"
 
 
@@ -242,7 +235,7 @@ def test_combine_parity(M, dt, T, k, width):
     assert torch.equal(out, out2), "combine not bitwise repeatable"
     ref = O.combine(TB.host(Y), slot, w, T, k)
     got = out.float().cpu().numpy()
-    _assert_close(got, ref, TOL[dt], "c")
+    assert_close(got, ref, dt, "c")
     assert np.all(got[0] == 0)
 
 
