@@ -7,20 +7,31 @@
 // Marin: Week of April 26th summary; Marin 535B-A23B article, section "21% to
 // 27% MFU without stopping the run"): rows [offsets[g], offsets[g+1]) use expert
 // g's weights.  Only active rows are computed: a 32-row MFMA block that lies
-// wholly past its group's end issues no loads and no MFMAs (the "mask-free"
-// ragged expert MLP of the same article section).  A rows may be gathered
-// through a row map (the layer reads its routed rows straight from the token
-// matrix instead of a permuted copy).
+// wholly past its group's end issues no MFMAs (the "mask-free" ragged expert MLP
+// of the same article section).  A rows may be gathered through a row map (the
+// layer reads its routed rows straight from the token matrix instead of a
+// permuted copy).
 //
-// Tiling: 256 threads = 4 waves as 2 x 2.  A block tile is BM rows x 128 LDS
-// columns of B; a K step is 64 bytes of every row (32 bf16 / 16 f32), staged in
-// LDS with 80-byte rows (16 bytes of padding keep the 16-byte fragment reads of
-// 16 consecutive rows on distinct banks) and double-buffered through registers.
-// Wave (wm, wn) owns the 32-row blocks wm, wm+2, ... (interleaved so both row
-// waves stay busy on a partial tile) and LDS columns [64 wn, 64 wn + 64) as two
-// 32-column MFMA blocks.  For the SwiGLU epilogue those two blocks are the gate
-// and the up rows of the same 32 hidden columns, so the activation is formed in
-// registers and neither G nor U is ever stored.
+// Tiling (one workgroup per CU): 512 threads = 8 waves (two per SIMD) as 2 x 4
+// over a 256 x 256 output tile.  Operands go straight from global memory into
+// LDS with global_load_lds_dwordx4 (no staging registers, no LDS write
+// instructions): a K step is 64 bytes of each of the 256 A rows and 256 B rows
+// (32 KB), and four such stages rotate through 128 KB of LDS, so the loads of
+// the next three steps are in flight while the matrix cores work on the current
+// one.  Within a row the four 16-byte chunks are XOR-swizzled by a function of
+// the row, chosen so that the fragment reads of 8 (or 16) consecutive rows hit
+// distinct banks; the swizzle is applied on the global side, since each DMA
+// instruction fills 1 KB of LDS contiguously.  Waits are explicit (vmcnt of the
+// stages still allowed in flight) followed by a bare s_barrier.
+//
+// Each wave owns up to 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (a 128 x 64
+// sub-tile, 128 accumulators).  The wave's 32-row blocks are interleaved (wm,
+// wm+2, ...) so both row waves stay busy on a partial tile, and the tile body is
+// specialised on how many of them are active, so each case is straight-line
+// MFMA code.  For the SwiGLU epilogue a wave's two column blocks are the gate
+// and the up rows of the same 32 hidden columns, so the activation is formed on
+// the way out and neither G nor U is ever stored.  Results leave through LDS in
+// 16-byte row chunks.
 //
 // Scheduling: a persistent grid (a multiple of 8 workgroups).  Workgroups are
 // dealt to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; each XCD
@@ -29,6 +40,10 @@
 // number of row tiles of a grouped GEMM is read from the device-side tile prefix
 // written by the kernel before it on the same stream (stream order is the fence;
 // nothing reads the boundaries before that kernel has finished).
+#include <stddef.h>
+
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -36,11 +51,55 @@ namespace moe {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBN = 128;          // LDS rows of B per tile
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kBM = 256;          // rows per tile
+constexpr int kBN = 256;          // B rows (LDS columns) per tile
 constexpr int kRowBytes = 64;     // bytes of each row per K step
-constexpr int kLdsRow = 80;       // padded LDS row stride
+constexpr int kStages = 4;        // LDS ring of K steps
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;   // 32 KB
+constexpr int kDmaPerOperand = kBM * kRowBytes / 1024 / kWaves;   // 1-KB DMAs per wave
+constexpr int kDmaPerStage = 2 * kDmaPerOperand;
 constexpr int kStageLd = 68;      // epilogue staging row stride (floats)
+
+static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
+
+// Chunk swizzle of LDS row r (r mod 32): 16-byte chunk c is stored at c ^ swz(r).
+// Fragment reads of rows r..r+7 (r..r+15) then hit distinct banks whether the
+// LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
+// expcnt and lgkmcnt left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// Workgroup barrier without a memory fence: the only cross-wave data here is
+// LDS written by the DMA loads, whose completion each wave has already waited
+// for.  The memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ void dma16(const char* g, char* l) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
+                                     (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ int find_group(const int32_t* tp, int G, int m) {
+    // largest g in [0, G) with tp[g] <= m  (tp non-decreasing, tp[0] = 0)
+    int lo = 0, hi = G;           // invariant: tp[lo] <= m < tp[hi]
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (tp[mid] <= m) lo = mid; else hi = mid;
+    }
+    return lo;
+}
 
 template <typename OutT, int kVec>
 __device__ __forceinline__ void store_vec(OutT* C, int64_t off, const float* v);
@@ -58,43 +117,32 @@ __device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* C, int64_t off, con
     *(uint4*)(C + off) = u;
 }
 
-__device__ __forceinline__ int find_group(const int32_t* tp, int G, int m) {
-    // largest g in [0, G) with tp[g] <= m  (tp non-decreasing, tp[0] = 0)
-    int lo = 0, hi = G;           // invariant: tp[lo] <= m < tp[hi]
-    while (hi - lo > 1) {
-        int mid = (lo + hi) >> 1;
-        if (tp[mid] <= m) lo = mid; else hi = mid;
-    }
-    return lo;
-}
-
-template <typename T, typename OutT, int EPI, int BM>
+template <typename T, typename OutT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr int kElem = Elem<T>::kBytes;
-    constexpr int kRB = BM / 64;                 // row blocks per wave
-    constexpr int kAChunks = BM * 4 / kThreads;  // 16-byte chunks per thread (A)
-    constexpr int kBChunks = kBN * 4 / kThreads; // (B)
-    constexpr int kSteps = kRowBytes / (Mfma<T>::kK * kElem);
+    constexpr int kSteps = kRowBytes / (Mfma<T>::kK * kElem);   // MFMA k-steps per K step
     constexpr int kColsOut = (EPI == EPI_SWIGLU) ? kBN / 2 : kBN;
 
-    __shared__ __attribute__((aligned(16))) char lds[2][(BM + kBN) * kLdsRow];
+    extern __shared__ __attribute__((aligned(16))) char lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = wave >> 2, wn = wave & 3;
 
     // ---- tile space
     const int64_t n_tiles_n = (p.N + kColsOut - 1) / kColsOut;
-    int64_t n_tiles_m;
-    if (p.offsets) n_tiles_m = p.tile_prefix[p.G];
-    else n_tiles_m = (p.M + BM - 1) / BM;
+    const int64_t n_tiles_m = p.offsets ? (int64_t)p.tile_prefix[p.G] : (p.M + kBM - 1) / kBM;
     const int64_t total = n_tiles_m * n_tiles_n;
     const int xcd = blockIdx.x % kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
     const int nslots = gridDim.x / kNumXcd;
     const int64_t lo = total * xcd / kNumXcd;
     const int64_t hi = total * (xcd + 1) / kNumXcd;
+
+    // fragment read offsets (the swizzle depends only on row % 32)
+    const int fl = swz(lane & 31);
+    const int rd_row = (lane & 31) * kRowBytes;
 
     for (int64_t t = lo + slot; t < hi; t += nslots) {
         // ---- tile coordinates (grouped swizzle along m)
@@ -111,193 +159,200 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         if (p.offsets) {
             g = find_group(p.tile_prefix, p.G, (int)tm);
             const int64_t mloc = tm - p.tile_prefix[g];
-            row0 = p.offsets[g] + mloc * BM;
-            rows_valid = min((int64_t)BM, (int64_t)p.offsets[g + 1] - row0);
+            row0 = p.offsets[g] + mloc * kBM;
+            rows_valid = min((int64_t)kBM, (int64_t)p.offsets[g + 1] - row0);
         } else {
-            row0 = tm * BM;
-            rows_valid = min((int64_t)BM, p.M - row0);
+            row0 = tm * kBM;
+            rows_valid = min((int64_t)kBM, p.M - row0);
         }
-        const int nrb_active = (int)((rows_valid + 31) >> 5);       // active 32-row blocks
-        const int n_act = (nrb_active - wm + 1) >> 1;              // this wave's active blocks
+        const int nrb = (int)((rows_valid + 31) >> 5);      // active 32-row blocks
+        const int n_act = (nrb - wm + 1) >> 1;              // this wave's active blocks
         const int64_t n0 = tn * kColsOut;
 
-        // ---- per-thread source rows
-        int64_t a_row[kAChunks];
-        bool a_ok[kAChunks];
+        // ---- DMA sources.  Wave w fills LDS rows 32 w + 16 i + lane / 4
+        // (i < 2) of each operand, chunk lane % 4, which holds logical chunk
+        // (lane % 4) ^ swz(row).  Row indices fit in 32 bits (checked on the host).
+        const int lrow = wave * (16 * kDmaPerOperand) + (lane >> 2);
+        int32_t a_src[kDmaPerOperand], b_src[kDmaPerOperand];
+        int chunk[kDmaPerOperand];
 #pragma unroll
-        for (int i = 0; i < kAChunks; i++) {
-            // rows of a 32-row block past the group's end are never loaded
-            // (wave-uniform: a wave's 16 rows of chunk i share one block);
-            // rows past the end inside a partial block read the first row
-            // instead, and their results are never stored.
-            const int r = (tid >> 2) + 64 * i;
-            a_ok[i] = (r >> 5) < nrb_active;
-            int64_t src = row0 + (r < rows_valid ? r : 0);
+        for (int i = 0; i < kDmaPerOperand; i++) {
+            const int r = lrow + 16 * i;
+            chunk[i] = ((lane & 3) ^ swz(r & 31)) * 16;
+            // rows past the group's end read the group's first row; their
+            // results are never stored
+            int32_t src = (int32_t)(row0 + (r < rows_valid ? r : 0));
             if (p.a_rows) src = p.a_rows[src] / p.a_div;
-            a_row[i] = src;
-        }
-        int64_t b_row[kBChunks];
-#pragma unroll
-        for (int i = 0; i < kBChunks; i++) {
-            const int j = (tid >> 2) + 64 * i;       // LDS row of B
+            a_src[i] = src;
             int64_t col, brow;
             if (EPI == EPI_SWIGLU) {
-                const int half = (j >> 5) & 1;
-                col = n0 + (j >> 6) * 32 + (j & 31);
+                // each 64-row slice of B: [gate 32 | up 32] of 32 hidden columns
+                const int up = (r >> 5) & 1;
+                col = n0 + (r >> 6) * 32 + (r & 31);
                 const int64_t zi = col / p.n_per, cc = col - zi * p.n_per;
-                brow = zi * 2 * p.n_per + cc + half * p.n_per;
+                brow = zi * 2 * p.n_per + cc + up * p.n_per;
             } else {
-                col = n0 + j;
+                col = n0 + r;
                 brow = col;
             }
-            b_row[i] = (col < p.N ? brow : 0) + (int64_t)g * p.b_group_rows;
+            b_src[i] = (int32_t)((col < p.N ? brow : 0) + (int64_t)g * p.b_group_rows);
         }
-        const int c16 = (tid & 3) * 16;
+        char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
+        char* const b_lds = lds + kBM * kRowBytes + (wave * kDmaPerOperand) * 1024;
 
-        floatx16 acc[kRB][2];
+        // One wave's staged 32 x W block (W = 32 hidden columns for SwiGLU, else
+        // 64 columns) leaves in 16-byte chunks of output elements.
+        auto store_block = [&](const float* stage, int rbase) __attribute__((always_inline)) {
+            OutT* C = (OutT*)p.C;
+            constexpr int W = (EPI == EPI_SWIGLU) ? 32 : 64;
+            constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
+            constexpr int kChunksPerRow = W / kVec;
+            const int64_t cbase = n0 + wn * W;
 #pragma unroll
-        for (int i = 0; i < kRB; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
-
-        // K segments run one after the other, each with its own prologue, so
-        // only the current segment's row addresses are live.
-#pragma unroll 1
-        for (int sidx = 0; sidx < p.nseg; sidx++) {
-            const char* A = (const char*)p.seg[0].A;
-            const char* B = (const char*)p.seg[0].B;
-            int64_t lda = p.seg[0].lda, ldb = p.seg[0].ldb;
-            int K = p.seg[0].K;
-#pragma unroll
-            for (int q = 1; q < kMaxSeg; q++) {
-                if (sidx == q) {
-                    A = (const char*)p.seg[q].A;
-                    B = (const char*)p.seg[q].B;
-                    lda = p.seg[q].lda;
-                    ldb = p.seg[q].ldb;
-                    K = p.seg[q].K;
-                }
-            }
-            const int nk = K * kElem / kRowBytes;
-            const char* a_ptr[kAChunks];
-            const char* b_ptr[kBChunks];
-#pragma unroll
-            for (int i = 0; i < kAChunks; i++) a_ptr[i] = A + a_row[i] * lda * kElem + c16;
-#pragma unroll
-            for (int i = 0; i < kBChunks; i++) b_ptr[i] = B + b_row[i] * ldb * kElem + c16;
-
-            uint4 ra[kAChunks], rb[kBChunks];
-            auto load_regs = [&](int kt) {
-                const int64_t koff = (int64_t)kt * kRowBytes;
-#pragma unroll
-                for (int i = 0; i < kAChunks; i++)
-                    if (a_ok[i]) ra[i] = *(const uint4*)(a_ptr[i] + koff);
-#pragma unroll
-                for (int i = 0; i < kBChunks; i++) rb[i] = *(const uint4*)(b_ptr[i] + koff);
-            };
-            auto store_lds = [&](int buf) {
-                char* As = lds[buf];
-                char* Bs = lds[buf] + BM * kLdsRow;
-#pragma unroll
-                for (int i = 0; i < kAChunks; i++) {
-                    const int r = (tid >> 2) + 64 * i;
-                    if (a_ok[i]) *(uint4*)(As + r * kLdsRow + c16) = ra[i];
-                }
-#pragma unroll
-                for (int i = 0; i < kBChunks; i++) {
-                    const int j = (tid >> 2) + 64 * i;
-                    *(uint4*)(Bs + j * kLdsRow + c16) = rb[i];
-                }
-            };
-
-            __syncthreads();      // earlier readers of LDS are done
-            load_regs(0);
-            store_lds(0);
-            __syncthreads();
-
-#pragma unroll 1
-            for (int kt = 0; kt < nk; kt++) {
-                const int buf = kt & 1;
-                if (kt + 1 < nk) load_regs(kt + 1);
-                const char* As = lds[buf];
-                const char* Bs = lds[buf] + BM * kLdsRow;
-#pragma unroll
-                for (int ks = 0; ks < kSteps; ks++) {
-                    const int kbyte =
-                        ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
-                    typename Mfma<T>::frag bfr[2];
-#pragma unroll
-                    for (int j = 0; j < 2; j++)
-                        bfr[j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32 + (lane & 31)) * kLdsRow,
-                                                   kbyte);
-#pragma unroll
-                    for (int i = 0; i < kRB; i++) {
-                        if (i < n_act) {
-                            typename Mfma<T>::frag afr = Mfma<T>::lds_frag(
-                                As + ((wm + 2 * i) * 32 + (lane & 31)) * kLdsRow, kbyte);
-                            acc[i][0] = Mfma<T>::mma(afr, bfr[0], acc[i][0]);
-                            acc[i][1] = Mfma<T>::mma(afr, bfr[1], acc[i][1]);
-                        }
-                    }
-                }
-                if (kt + 1 < nk) store_lds(buf ^ 1);
-                __syncthreads();
-            }
-        }
-
-        OutT* C = (OutT*)p.C;
-        // ---- epilogue, staged through LDS so that every global store is a
-        // 16-byte chunk of a row.  All waves walk the same number of steps (the
-        // barriers are block-wide); a wave with no active row block idles.
-        float* stage = (float*)lds[0] + wave * (32 * kStageLd);
-#pragma unroll
-        for (int i = 0; i < kRB; i++) {
-            const bool act = i < n_act;
-            const int rbase = (wm + 2 * i) * 32;
-            if (act) {
-#pragma unroll
-                for (int v = 0; v < 16; v++) {
-                    const int r = acc_row(v, lane);
+            for (int q = lane; q < 32 * kChunksPerRow; q += 64) {
+                const int r = q / kChunksPerRow;
+                const int cc = (q % kChunksPerRow) * kVec;
+                const int64_t grow = rbase + r;
+                const int64_t col = cbase + cc;
+                if (grow < rows_valid && col < p.N) {
+                    float vals[kVec];
+                    const float* srow = stage + r * kStageLd;
                     if (EPI == EPI_SWIGLU) {
-                        stage[r * kStageLd + (lane & 31)] = silu_f(acc[i][0][v]) * acc[i][1][v];
+                        // hidden column c of the wave: gate at c, up at 32 + c
+#pragma unroll
+                        for (int e = 0; e < kVec; e++)
+                            vals[e] = silu_f(srow[cc + e]) * srow[32 + cc + e];
                     } else {
-                        stage[r * kStageLd + (lane & 31)] = acc[i][0][v];
-                        stage[r * kStageLd + 32 + (lane & 31)] = acc[i][1][v];
+#pragma unroll
+                        for (int e = 0; e < kVec; e++) vals[e] = srow[cc + e];
+                    }
+                    const int64_t off = (row0 + grow) * p.ldc + col;
+                    if (EPI == EPI_ADD) {
+                        const int64_t aoff = (row0 + grow) * p.ld_add + col;
+#pragma unroll
+                        for (int e = 0; e < kVec; e++)
+                            vals[e] += Elem<OutT>::load((const OutT*)p.addend, aoff + e);
+                    }
+                    store_vec<OutT, kVec>(C, off, vals);
+                }
+            }
+        };
+
+        // The rest of the tile is specialised on the number of active row
+        // blocks of this wave: each case is straight-line MFMA code with its
+        // own accumulator set.
+        auto tile_body = [&](auto nact_c) __attribute__((always_inline)) {
+            constexpr int NACT = decltype(nact_c)::value;
+            floatx16 acc[NACT > 0 ? NACT : 1][2];
+#pragma unroll
+            for (int i = 0; i < NACT; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+            // K segments run one after the other, each with its own pipeline fill.
+#pragma unroll 1
+            for (int sidx = 0; sidx < p.nseg; sidx++) {
+                // The kernel's only argument is p, laid out at the start of the
+                // kernel-argument segment; reading the selected segment from there
+                // keeps it in scalar loads (indexing p.seg directly would copy
+                // the argument to private memory).
+                const GemmSeg* segs = (const GemmSeg*)(
+                    (const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(GemmParams, seg));
+                const char* A = (const char*)uniform64((int64_t)segs[sidx].A);
+                const char* B = (const char*)uniform64((int64_t)segs[sidx].B);
+                const int64_t lda = uniform64(segs[sidx].lda);
+                const int64_t ldb = uniform64(segs[sidx].ldb);
+                const int K = __builtin_amdgcn_readfirstlane(segs[sidx].K);
+                const int nk = __builtin_amdgcn_readfirstlane(K * kElem / kRowBytes);
+                const char* a_ptr[kDmaPerOperand];
+                const char* b_ptr[kDmaPerOperand];
+#pragma unroll
+                for (int i = 0; i < kDmaPerOperand; i++) {
+                    a_ptr[i] = A + (int64_t)a_src[i] * lda * kElem + chunk[i];
+                    b_ptr[i] = B + (int64_t)b_src[i] * ldb * kElem + chunk[i];
+                }
+                auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+                    const int64_t koff = (int64_t)kt * kRowBytes;
+#pragma unroll
+                    for (int i = 0; i < kDmaPerOperand; i++)
+                        dma16(a_ptr[i] + koff, a_lds + buf * kStageBytes + i * 1024);
+#pragma unroll
+                    for (int i = 0; i < kDmaPerOperand; i++)
+                        dma16(b_ptr[i] + koff, b_lds + buf * kStageBytes + i * 1024);
+                };
+
+                // every wave is done with LDS (previous segment, tile or epilogue)
+                __syncthreads();
+#pragma unroll
+                for (int s0 = 0; s0 < kStages - 1; s0++)
+                    if (s0 < nk) issue(s0, s0);
+
+#pragma unroll 1
+                for (int kt = 0; kt < nk; kt++) {
+                    // stage kt has landed once at most the later stages are in flight
+                    if (kt + 2 < nk) wait_vmcnt<2 * kDmaPerStage>();
+                    else if (kt + 1 < nk) wait_vmcnt<kDmaPerStage>();
+                    else wait_vmcnt<0>();
+                    bare_barrier();   // all waves' stage kt landed; stage kt-1 consumed
+                    if (kt + kStages - 1 < nk)
+                        issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
+                    if (NACT == 0) continue;
+                    const char* As = lds + (kt % kStages) * kStageBytes + rd_row;
+                    const char* Bs = As + kBM * kRowBytes;
+#pragma unroll
+                    for (int ks = 0; ks < kSteps; ks++) {
+                        const int kb =
+                            ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
+                        const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
+                        typename Mfma<T>::frag bfr[2], afr[NACT > 0 ? NACT : 1];
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            bfr[j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
+#pragma unroll
+                        for (int i = 0; i < NACT; i++)
+                            afr[i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+#pragma unroll
+                        for (int i = 0; i < NACT; i++)
+#pragma unroll
+                            for (int j = 0; j < 2; j++)
+                                acc[i][j] = Mfma<T>::mma(afr[i], bfr[j], acc[i][j]);
                     }
                 }
             }
-            __syncthreads();
-            if (act) {
-                // the wave's 32 x W block (W = 32 hidden columns for SwiGLU, else
-                // 64 columns) leaves in chunks of kVec output elements
-                constexpr int W = (EPI == EPI_SWIGLU) ? 32 : 64;
-                constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
-                constexpr int kChunksPerRow = W / kVec;
-                const int64_t cbase = (EPI == EPI_SWIGLU) ? n0 + wn * 32 : n0 + wn * 64;
+            __syncthreads();      // LDS is reused for the epilogue
+
+            // ---- epilogue, staged through LDS so that every global store is a
+            // 16-byte chunk of a row; the activation and the conversion run on
+            // the read-back side.  All waves walk the same steps (the barriers
+            // are block-wide); a wave with no active row block idles.
+            float* stage = (float*)lds + wave * (32 * kStageLd);
+            const int nsteps = (nrb + 1) >> 1;       // active blocks of wave row 0
 #pragma unroll
-                for (int q = lane; q < 32 * kChunksPerRow; q += 64) {
-                    const int r = q / kChunksPerRow;
-                    const int cc = (q % kChunksPerRow) * kVec;
-                    const int64_t grow = rbase + r;
-                    const int64_t col = cbase + cc;
-                    if (grow < rows_valid && col < p.N) {
-                        float vals[kVec];
+            for (int i = 0; i < 4; i++) {
+                if (i < nsteps) {         // block-uniform: the barriers stay uniform
+                    const int rbase = (wm + 2 * i) * 32;
+                    if (i < NACT) {
 #pragma unroll
-                        for (int e = 0; e < kVec; e++) vals[e] = stage[r * kStageLd + cc + e];
-                        const int64_t off = (row0 + grow) * p.ldc + col;
-                        if (EPI == EPI_ADD) {
-                            const int64_t aoff = (row0 + grow) * p.ld_add + col;
+                        for (int j = 0; j < 2; j++)
 #pragma unroll
-                            for (int e = 0; e < kVec; e++)
-                                vals[e] += Elem<OutT>::load((const OutT*)p.addend, aoff + e);
-                        }
-                        store_vec<OutT, kVec>(C, off, vals);
+                            for (int v = 0; v < 16; v++)
+                                stage[acc_row(v, lane) * kStageLd + j * 32 + (lane & 31)] =
+                                    acc[i < NACT ? i : 0][j][v];
                     }
+                    __syncthreads();
+                    if (i < NACT) store_block(stage, rbase);
+                    __syncthreads();
                 }
             }
-            __syncthreads();
+        };
+        switch (n_act) {
+            case 4: tile_body(std::integral_constant<int, 4>{}); break;
+            case 3: tile_body(std::integral_constant<int, 3>{}); break;
+            case 2: tile_body(std::integral_constant<int, 2>{}); break;
+            case 1: tile_body(std::integral_constant<int, 1>{}); break;
+            default: tile_body(std::integral_constant<int, 0>{}); break;
         }
     }
 }
@@ -316,15 +371,22 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* offset
     if (tid == 0) tp[G] = total;
 }
 
-template <typename T, typename OutT, int EPI, int BM>
+constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;   // 131,072 bytes
+
+template <typename T, typename OutT, int EPI>
 hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
-    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI, BM>), dim3(grid), dim3(kThreads), 0, s, p);
+    static_assert(kWaves * 32 * kStageLd * 4 <= kLdsBytes, "epilogue staging fits in LDS");
+    // opting in to more than 64 KB of dynamic LDS is idempotent and cheap
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI>), dim3(grid), dim3(kThreads), kLdsBytes, s, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int gemm_block_m() { return 256; }
+int gemm_block_m() { return kBM; }
 
 int gemm_cols_per_tile(int epi) { return epi == EPI_SWIGLU ? kBN / 2 : kBN; }
 
@@ -336,23 +398,23 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp
 hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,
                        int64_t max_tiles, hipStream_t s) {
     int dev = 0, cus = 256;
-    hipGetDevice(&dev);
-    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    int64_t grid = (int64_t)cus * 2;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return hipErrorInvalidDevice;
+    int64_t grid = cus;
     if (max_tiles < grid) grid = max_tiles;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     if (grid < kNumXcd) grid = kNumXcd;
-    constexpr int BM = 256;
     if (in_dt == MOE_BF16) {
         if (epi == EPI_STORE)
-            return out_f32 ? launch_t<bf16_t, float, EPI_STORE, BM>(p, (int)grid, s)
-                           : launch_t<bf16_t, bf16_t, EPI_STORE, BM>(p, (int)grid, s);
-        if (epi == EPI_SWIGLU) return launch_t<bf16_t, bf16_t, EPI_SWIGLU, BM>(p, (int)grid, s);
-        return launch_t<bf16_t, bf16_t, EPI_ADD, BM>(p, (int)grid, s);
+            return out_f32 ? launch_t<bf16_t, float, EPI_STORE>(p, (int)grid, s)
+                           : launch_t<bf16_t, bf16_t, EPI_STORE>(p, (int)grid, s);
+        if (epi == EPI_SWIGLU) return launch_t<bf16_t, bf16_t, EPI_SWIGLU>(p, (int)grid, s);
+        return launch_t<bf16_t, bf16_t, EPI_ADD>(p, (int)grid, s);
     }
-    if (epi == EPI_STORE) return launch_t<float, float, EPI_STORE, BM>(p, (int)grid, s);
-    if (epi == EPI_SWIGLU) return launch_t<float, float, EPI_SWIGLU, BM>(p, (int)grid, s);
-    return launch_t<float, float, EPI_ADD, BM>(p, (int)grid, s);
+    if (epi == EPI_STORE) return launch_t<float, float, EPI_STORE>(p, (int)grid, s);
+    if (epi == EPI_SWIGLU) return launch_t<float, float, EPI_SWIGLU>(p, (int)grid, s);
+    return launch_t<float, float, EPI_ADD>(p, (int)grid, s);
 }
 
 }  // namespace moe
