@@ -32,6 +32,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed steps, run one 1 GiB device copy (a kernel of known "
+                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and report "
+                         "its bandwidth")
     return ap.parse_args()
 
 
@@ -189,6 +193,18 @@ def main():
                      "bytes_per_launch": g1_bytes, "avg_launch_ms": round(g1_ms, 4),
                      "mfma_frac": round(g1_flops / (g1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
     }
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)                           # warm-up copy
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        line["copy_1GiB"] = {"ms": round(e0.elapsed_time(e1), 4),
+                             "GB_per_s": round(2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -49,11 +49,21 @@ int64_t dense_tiles(int64_t rows, int64_t N, int epi) {
     return ((rows + BM - 1) / BM) * ((N + cols - 1) / cols);
 }
 
+// Row tiles per swizzle group.  An XCD's 32 CUs work on consecutive tiles in
+// near lockstep along K, so with 8 row tiles per group each B slice is shared by
+// 8 concurrent tiles and each A slice by 4 (dense GEMMs).  Grouped GEMMs keep
+// the row tiles of one expert's weight slices together and walk the columns
+// innermost, so the expert's gathered rows stay in L2 across its column tiles
+// (measured faster than grouping at the 535B shape, where an expert has one
+// row tile).
+constexpr int kGroupDense = 8;
+constexpr int kGroupGrouped = 1;
+
 GemmParams gemm_base() {
     GemmParams p;
     memset(&p, 0, sizeof p);
     p.a_div = 1;
-    p.group_m = 1;
+    p.group_m = kGroupDense;
     return p;
 }
 
@@ -64,6 +74,7 @@ moe_status grouped_ffn_impl(const void* X, int64_t ldx, const int32_t* a_rows, i
                             int64_t R_rows, const void* W_gu, const void* W_d, int64_t d,
                             int64_t H, moe_dtype dt, void* h, void* Y, hipStream_t s) {
     GemmParams p = gemm_base();
+    p.group_m = kGroupGrouped;
     p.offsets = offsets;
     p.tile_prefix = tile_prefix;
     p.G = E;
@@ -84,6 +95,7 @@ moe_status grouped_down_impl(const void* h, const int32_t* offsets, const int32_
                              int E, int64_t R_rows, const void* W_d, int64_t d, int64_t H,
                              moe_dtype dt, void* Y, hipStream_t s) {
     GemmParams p = gemm_base();
+    p.group_m = kGroupGrouped;
     p.offsets = offsets;
     p.tile_prefix = tile_prefix;
     p.G = E;

@@ -75,10 +75,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
-// Workgroup barrier without a memory fence: the only cross-wave data here is
-// LDS written by the DMA loads, whose completion each wave has already waited
-// for.  The memory clobber keeps the compiler from moving LDS accesses across.
-__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+// Workgroup barrier without a global-memory fence: the only cross-wave data
+// here is LDS written by the DMA loads, whose completion each wave has already
+// waited for (vmcnt), and the wave's own LDS reads are drained (lgkmcnt) so no
+// read can still be pending when another wave refills the buffer.  The memory
+// clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void bare_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ void dma16(const char* g, char* l) {
     __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)g,
