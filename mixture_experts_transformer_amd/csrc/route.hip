@@ -9,10 +9,13 @@
 //      of four LDS stages with global_load_lds_dwordx4 (16 values of K per
 //      stage), as in the grouped GEMM.  Within a stage, lane half q of an MFMA
 //      takes K values 8q..8q+7 in turn (any fixed assignment of K to MFMA steps
-//      gives the same sum), so each lane fetches its eight values of a row with
-//      16-byte reads of a chunk-swizzled row; g multiplies the h operand.  While
-//      a stage sits in LDS, the workgroup also writes that slice of the
-//      normalised rows r (the experts' input) when asked;
+//      gives the same sum), so each lane fetches its values of a row with
+//      16-byte (8-byte) reads of a chunk-swizzled row; g multiplies the h
+//      operand.  Eight waves, two per SIMD: waves 0-3 take the first four MFMA
+//      steps of every stage and waves 4-7 the last four, each for a quarter of
+//      the expert columns; the two partial sums are added in a fixed order at
+//      the end.  While a stage sits in LDS, the workgroup also writes that slice
+//      of the normalised rows r (the experts' input) when asked;
 //   3. logits (scaled, plus bias) go to LDS; each wave picks the top-k of 8
 //      tokens with wavefront argmax reductions over packed (value, id) keys and
 //      forms the weights exp(l_j - l_max) / sum_sel exp(l_i - l_max), which equal
@@ -30,7 +33,8 @@ namespace moe {
 namespace {
 
 constexpr int kTok = 32;          // tokens per workgroup
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
 constexpr int kKS = 16;           // K values per stage
 constexpr int kStages = 4;
 constexpr int kMaxE = 512;
@@ -91,16 +95,17 @@ struct RouteParams {
     float* w;
 };
 
-// NB = experts padded to a multiple of 64, over 64: each wave moves NB 1-KB
+// NB = experts padded to a multiple of 128, over 128: each wave moves NB 1-KB
 // slices of W_r per stage (16 rows each), plus one slice of h (or a dummy).
 template <typename Tin, typename Tr, int NB>
 __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
     constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
     constexpr int kARow = kKS * kInB;                 // bytes of an h row per stage
     constexpr int kAInstr = kTok * kARow / 1024;      // real 1-KB h slices per stage
-    constexpr int kEPad = NB * 64;
+    constexpr int kEPad = NB * 16 * kWaves;
     constexpr int kNCB = kEPad / 32;                  // 32-expert MFMA column blocks
-    constexpr int kCBW = (kNCB + 3) / 4;              // per wave (dealt round-robin)
+    constexpr int kCBW = (kNCB + 3) / 4;              // per wave (dealt round-robin to
+                                                      // the four waves of a K half)
     constexpr int kBBytes = kEPad * 64;
     constexpr int kStageBytes = kTok * kARow + kBBytes;
     constexpr int kDma = NB + 1;                      // DMAs per wave per stage
@@ -111,13 +116,15 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wave >> 2;                         // which half of each stage's MFMA steps
+    const int wc = wave & 3;                          // which quarter of the expert columns
     const int64_t t0 = (int64_t)blockIdx.x * kTok;
     const int ntok = (int)min((int64_t)kTok, rp.T - t0);
     const int d = rp.d;
 
     // ---- 1. inverse RMS per row
     if (rp.apply_norm) {
-        for (int tt = wave; tt < kTok; tt += 4) {
+        for (int tt = wave; tt < kTok; tt += kWaves) {
             float ss = 0.0f;
             if (tt < ntok) {
                 const char* row = (const char*)rp.h + (t0 + tt) * (int64_t)d * kInB;
@@ -200,42 +207,38 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
         const char* st = lds + (kt % kStages) * kStageBytes;
         const int kb = kt * kKS;
 
-        // g for K values kb + 8q .. kb + 8q + 7 (scalar loads of the 16 values)
-        float gs[8];
+        // this wave's four MFMA steps s = 4 kh .. 4 kh + 3 use K values
+        // kb + 8q + s; g for them (scalar loads of the stage's 16 values)
+        float gs[4];
 #pragma unroll
-        for (int s = 0; s < 8; s++) {
-            const float g0 = rp.g ? rp.g[kb + s] : 1.0f;
-            const float g1 = rp.g ? rp.g[kb + 8 + s] : 1.0f;
+        for (int s = 0; s < 4; s++) {
+            const float g0 = rp.g ? rp.g[kb + 4 * kh + s] : 1.0f;
+            const float g1 = rp.g ? rp.g[kb + 8 + 4 * kh + s] : 1.0f;
             gs[s] = q ? g1 : g0;
         }
-        // this lane's 8 values of its h row
-        float a[8];
+        // this lane's 4 values of its h row
+        float a[4];
         if (kInB == 4) {
-            const float4 v0 = *(const float4*)(st + row * 64 + ((2 * q) ^ swz64(row)) * 16);
-            const float4 v1 = *(const float4*)(st + row * 64 + ((2 * q + 1) ^ swz64(row)) * 16);
+            const float4 v0 = *(const float4*)(st + row * 64 + ((2 * q + kh) ^ swz64(row)) * 16);
             a[0] = v0.x; a[1] = v0.y; a[2] = v0.z; a[3] = v0.w;
-            a[4] = v1.x; a[5] = v1.y; a[6] = v1.z; a[7] = v1.w;
         } else {
-            const uint4 u = *(const uint4*)(st + row * 32 + (q ^ swz32(row)) * 16);
-            const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                a[2 * e] = __uint_as_float(ww[e] << 16);
-                a[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
-            }
+            const uint2 u = *(const uint2*)(st + row * 32 + (q ^ swz32(row)) * 16 + kh * 8);
+            a[0] = __uint_as_float(u.x << 16);
+            a[1] = __uint_as_float(u.x & 0xffff0000u);
+            a[2] = __uint_as_float(u.y << 16);
+            a[3] = __uint_as_float(u.y & 0xffff0000u);
         }
 #pragma unroll
-        for (int s = 0; s < 8; s++) a[s] *= gs[s];
+        for (int s = 0; s < 4; s++) a[s] *= gs[s];
 #pragma unroll
         for (int i = 0; i < kCBW; i++) {
-            const int cb = wave + 4 * i;
+            const int cb = wc + 4 * i;
             if (cb < kNCB) {
                 const char* brow = st + kTok * kARow + (cb * 32 + row) * 64;
-                const float4 b0 = *(const float4*)(brow + ((2 * q) ^ swz64(row)) * 16);
-                const float4 b1 = *(const float4*)(brow + ((2 * q + 1) ^ swz64(row)) * 16);
-                const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+                const float4 b0 = *(const float4*)(brow + ((2 * q + kh) ^ swz64(row)) * 16);
+                const float b[4] = {b0.x, b0.y, b0.z, b0.w};
 #pragma unroll
-                for (int s = 0; s < 8; s++)
+                for (int s = 0; s < 4; s++)
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc[i], 0, 0, 0);
             }
         }
@@ -258,23 +261,31 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
     }
     __syncthreads();
 
-    // ---- 3. logits tile in LDS, then top-k per token
+    // ---- 3. logits tile in LDS (first K half, then the second added in a
+    // fixed order, scaled, plus bias), then top-k per token
     float* lt = (float*)lds;                 // [kTok][kEPad + 1]
     constexpr int ldl = kEPad + 1;
+    for (int half = 0; half < 2; half++) {
+        if (kh == half) {
 #pragma unroll
-    for (int i = 0; i < kCBW; i++) {
-        const int cb = wave + 4 * i;
-        if (cb < kNCB) {
-            const int e = cb * 32 + row;
-            const float bias = (rp.b_r && e < rp.E) ? rp.b_r[e] : 0.0f;
+            for (int i = 0; i < kCBW; i++) {
+                const int cb = wc + 4 * i;
+                if (cb < kNCB) {
+                    const int e = cb * 32 + row;
+                    const float bias = (rp.b_r && e < rp.E) ? rp.b_r[e] : 0.0f;
 #pragma unroll
-            for (int v = 0; v < 16; v++) {
-                const int tr = acc_row(v, lane);
-                lt[tr * ldl + e] = acc[i][v] * inv_rms[tr] + bias;
+                    for (int v = 0; v < 16; v++) {
+                        const int tr = acc_row(v, lane);
+                        if (half == 0)
+                            lt[tr * ldl + e] = acc[i][v];
+                        else
+                            lt[tr * ldl + e] = (lt[tr * ldl + e] + acc[i][v]) * inv_rms[tr] + bias;
+                    }
+                }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
     const int E = rp.E, k = rp.k;
     if (rp.logits) {
         for (int idx = tid; idx < ntok * E; idx += kThreads) {
@@ -282,7 +293,7 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
             rp.logits[(t0 + tt) * E + e] = lt[tt * ldl + e];
         }
     }
-    for (int tt = wave; tt < ntok; tt += 4) {
+    for (int tt = wave; tt < ntok; tt += kWaves) {
         // each lane holds experts lane, lane + 64, ... ; taken ones are cleared
         constexpr int kPer = kEPad / 64;
         uint64_t key[kPer];
@@ -323,8 +334,8 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
 template <typename Tin, typename Tr, int NB>
 hipError_t launch_nb(const RouteParams& rp, hipStream_t s) {
     constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
-    constexpr size_t kStage = kTok * kKS * kInB + NB * 64 * 64;
-    constexpr size_t kTile = (size_t)kTok * (NB * 64 + 1) * 4;
+    constexpr size_t kStage = kTok * kKS * kInB + NB * 16 * kWaves * 64;
+    constexpr size_t kTile = (size_t)kTok * (NB * 16 * kWaves + 1) * 4;
     const size_t lds = (kStages * kStage + 1024) > kTile ? (kStages * kStage + 1024) : kTile;
     hipError_t e = hipFuncSetAttribute((const void*)route_kernel<Tin, Tr, NB>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -337,15 +348,11 @@ hipError_t launch_nb(const RouteParams& rp, hipStream_t s) {
 
 template <typename Tin, typename Tr>
 hipError_t launch_rt(const RouteParams& rp, hipStream_t s) {
-    switch ((rp.E + 63) / 64) {
+    switch ((rp.E + 16 * kWaves - 1) / (16 * kWaves)) {
         case 1: return launch_nb<Tin, Tr, 1>(rp, s);
         case 2: return launch_nb<Tin, Tr, 2>(rp, s);
         case 3: return launch_nb<Tin, Tr, 3>(rp, s);
-        case 4: return launch_nb<Tin, Tr, 4>(rp, s);
-        case 5: return launch_nb<Tin, Tr, 5>(rp, s);
-        case 6: return launch_nb<Tin, Tr, 6>(rp, s);
-        case 7: return launch_nb<Tin, Tr, 7>(rp, s);
-        default: return launch_nb<Tin, Tr, 8>(rp, s);
+        default: return launch_nb<Tin, Tr, 4>(rp, s);
     }
 }
 
