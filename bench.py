@@ -1,17 +1,24 @@
 """Benchmark of the routed MoE layer forward on one MI355X.
 
-One step = one moe_layer_fwd over a batch of seeded synthetic inputs already in
-HBM: down-projection, RMSNorm + router + top-k, grouping, gate/up + SwiGLU and
-down grouped GEMMs, ordered combine, shared experts and the output projection.
-Prints one JSON line.  Default workload: the 535B-A23B-shaped layer (8,192
-tokens, width 6,144, latent 3,072, 384 experts top-8, two shared experts).
+One step = one pass of the whole path over a batch of seeded synthetic inputs
+already resident in HBM.  For a layer workload that is one moe_layer_fwd:
+down-projection, RMSNorm + router + top-k, grouping, gate/up + SwiGLU and down
+grouped GEMMs, ordered combine, shared experts and the output projection.  For
+the expert-parallel share (a receiver pool of rows with packed local expert
+ids) it is moe_permute (with the row copy), moe_grouped_ffn and the unpermute
+(moe_combine, k = 1).  Prints one JSON line.
+
+Default workload: the 535B-A23B-shaped layer (8,192 tokens, width 6,144,
+latent 3,072, 384 experts top-8, two shared experts).
 """
 from __future__ import annotations
 
 import argparse
 import ctypes as C
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -19,8 +26,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "marin535b_bf16_T8192_D6144_L3072_E384_k8"
-PEAK_BF16_TFLOPS = 2500.0        # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+METRIC = "MoE layer fwd TFLOP/s + tokens/s, % of bf16 MFMA peak (1 MI355X)"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0                          # MI355X HBM3E
+GEMM_TILE_M = 256                              # rows per grouped-GEMM tile
+GEMM_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
+                               "grouped_gate_up_gemm_marin535b_T8192_hbm_traffic.txt")
 
 
 def parse():
@@ -32,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-kernel-extras", action="store_true",
+                    help="skip the stand-alone permute-with-copy measurement after the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and report "
@@ -46,7 +60,6 @@ class HipEvents:
         self.hip = C.CDLL("libamdhip64.so")
         self.hip.hipEventCreate.argtypes = [C.POINTER(C.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [C.POINTER(C.c_float), C.c_void_p, C.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [C.c_void_p]
 
     def create(self, n):
         evs = []
@@ -62,17 +75,76 @@ class HipEvents:
         return ms.value
 
 
-def grouped_gemm1_bytes(cfg, counts) -> int:
-    """Algorithmic HBM bytes of the gate/up + SwiGLU grouped GEMM: the weights of
-    every expert that received a row, each routed row of the expert input once,
-    each hidden row written once."""
-    es = 2 if cfg.dtype == "bf16" else 4
-    active = int((counts > 0).sum())
-    rows = int(counts.sum())
-    return active * 2 * cfg.H * cfg.d_e * es + rows * cfg.d_e * es + rows * cfg.H * es
+def gemm_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in GEMM_SOURCES:
+        with open(os.path.join(ROOT, "mixture_experts_transformer_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
-def cpu_baseline(cfg, inp, target_s: float) -> dict:
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up grouped GEMM from the committed counter
+    summary, if it was taken on this workload with the current GEMM source."""
+    try:
+        with open(TRAFFIC_PROFILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = dict(re.findall(r"^([a-z_0-9]+):\s*(\S+)\s*$", text, flags=re.M))
+    if fields.get("workload") != workload or fields.get("gemm_source_sha256") != gemm_source_hash():
+        return None
+    try:
+        return int(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def gemm_roofline(name, flops, nbytes, ms, dtype, traffic=None) -> dict:
+    """Roofline entry for one kernel: bound by HBM or by the MFMA rate, whichever
+    its arithmetic intensity puts it under."""
+    peak_f = PEAK_TFLOPS[dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    if flops / nbytes < ridge:
+        r = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    else:
+        r = {"bound": "mfma", "achieved": round(tflops, 1), "peak": peak_f, "unit": "TFLOP/s",
+             "frac": round(tflops / peak_f, 4)}
+    r.update({"traffic": traffic, "kernel": name, "algorithmic_bytes_per_launch": int(nbytes),
+              "flops_per_launch": int(flops), "avg_launch_ms": round(ms, 4),
+              "mfma_frac": round(tflops / peak_f, 4), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+    return r
+
+
+def hbm_entry(nbytes, ms) -> dict:
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "bytes": int(nbytes), "GB_per_s": round(gbs, 1),
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def padded_rows(counts) -> int:
+    return int(sum(-(-int(c) // GEMM_TILE_M) * GEMM_TILE_M for c in counts))
+
+
+def time_ms(fn, reps=5) -> float:
+    """Mean device time of fn() over reps calls, torch events on the current stream."""
+    import torch
+    fn()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+# ---------------------------------------------------------------- CPU oracle --
+def cpu_baseline_layer(cfg, inp, target_s: float) -> dict:
     """The oracle as it stands, on a bounded sample of the same workload's tokens."""
     import numpy as np
 
@@ -98,7 +170,7 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
     spent = 0.0
     done = 0
     while spent < target_s and done < cfg.T:
-        tok = np.sort(rng.choice(cfg.T, size=n, replace=False)).astype(np.int32)
+        tok = np.sort(rng.choice(cfg.T, size=min(n, cfg.T), replace=False)).astype(np.int32)
         r = O.route_tokens(TB.dims(cfg), base, x_host, tok)
         W = weights(np.unique(r["ids"]))
         t0 = time.perf_counter()
@@ -106,37 +178,60 @@ def cpu_baseline(cfg, inp, target_s: float) -> dict:
         O.output_tokens(TB.dims(cfg), W, x_host, tok, r["ids"], r["w"])
         dt = time.perf_counter() - t0
         spent += dt
-        done += n
+        done += len(tok)
         n = max(8, int(n * min(4.0, max(1.0, (target_s - spent) / max(dt, 1e-3)))))
         n = min(n, 256)
-    return {"value": done / spent, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done / spent, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
             "sample": f"{done} random tokens of the same workload (seed 0), full layer per token "
                       f"(routing, experts, combine, up-projection, shared experts) in double "
                       f"precision; host copies of weights not timed"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for "
-              f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
-        sys.exit(2)
+def cpu_baseline_pool(cfg, pool, target_s: float) -> dict:
+    import numpy as np
+
+    from oracle import oracle as O
+    from oracle import torch_bridge as TB
+
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    ids = pool["ids"].cpu().numpy()
+    valid = np.flatnonzero(ids >= 0)
+    W_gu = [TB.host(pool["W_gu"][e]) for e in range(cfg.E)]
+    W_d = [TB.host(pool["W_d"][e]) for e in range(cfg.E)]
+    rng = np.random.default_rng(0)
+    n, spent, done = 16, 0.0, 0
+    while spent < target_s and done < len(valid):
+        rows = np.sort(rng.choice(valid, size=min(n, len(valid)), replace=False))
+        Xh = TB.host(pool["X"][rows])
+        t0 = time.perf_counter()
+        O.expert_rows(Xh, ids[rows], W_gu, W_d, cfg.H)
+        dt = time.perf_counter() - t0
+        spent += dt
+        done += len(rows)
+        n = min(1024, max(16, int(n * min(4.0, max(1.0, (target_s - spent) / max(dt, 1e-3))))))
+    return {"value": round(done / spent, 2), "unit": "rows/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} random valid pool rows (seed 0) through their local expert's "
+                      f"SwiGLU FFN in double precision; host copies not timed"}
+
+
+# ------------------------------------------------------------------ workloads --
+def bench_layer(args, cfg, M, dev):
     import numpy as np
     import torch
 
-    import mixture_experts_transformer_amd as M
-    from moe_synth import by_name, gen_layer
+    from moe_synth import gen_layer
 
-    cfg = by_name(args.workload)
-    dev = torch.device("cuda:0")
     inp = gen_layer(cfg, dev)
     desc = M.layer_desc(cfg.T, cfg.D, cfg.L, cfg.E, cfg.k, cfg.H, cfg.n_shared, cfg.Hs,
                         cfg.dtype, cfg.eps)
     ws = torch.empty(M.moe_layer_workspace_size(desc), dtype=torch.uint8, device=dev)
     y = torch.empty_like(inp["x"])
-    counts = torch.empty(cfg.E, dtype=torch.int32, device=dev)
-    n_dropped = torch.empty(1, dtype=torch.int64, device=dev)
-    aux = dict(counts=counts, n_dropped=n_dropped)
+    i32 = dict(dtype=torch.int32, device=dev)
+    aux = dict(ids=torch.empty((cfg.T, cfg.k), **i32),
+               w=torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
+               counts=torch.empty(cfg.E, **i32),
+               n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
 
     for _ in range(args.warmup):
         M.moe_layer_fwd(desc, inp, inp["x"], y=y, aux=aux, ws=ws)
@@ -157,17 +252,25 @@ def main():
             stage_ms[M.EV_NAMES[i]] += hip.elapsed_ms(evs[s][i - 1], evs[s][i]) / args.steps
     gpu_ms = sum(hip.elapsed_ms(evs[s][0], evs[s][-1]) for s in range(args.steps)) / args.steps
 
-    cnt = counts.cpu().numpy().astype(np.int64)
-    kept = int(cnt.sum()) - int(n_dropped.item())
+    cnt = aux["counts"].cpu().numpy().astype(np.int64)
+    kept = int(cnt.sum()) - int(aux["n_dropped"].item())
     ms = wall * 1e3 / args.steps
     flops = cfg.flops(kept)
     tflops = flops / (ms * 1e-3) / 1e12
-    g1_bytes = grouped_gemm1_bytes(cfg, cnt)
-    g1_ms = stage_ms["gemm1"]
-    g1_flops = 2 * kept * cfg.d_e * 2 * cfg.H
-    achieved = g1_bytes / (g1_ms * 1e-3) / 1e9
+    pad = padded_rows(cnt)
+    hw_flops = cfg.flops(kept) + 2 * (pad - kept) * cfg.d_e * cfg.H * 3
+    es = 2 if cfg.dtype == "bf16" else 4
+    de, H, T, k = cfg.d_e, cfg.H, cfg.T, cfg.k
+    active = int((cnt > 0).sum())
+    # gate/up + SwiGLU: every active expert's [2H, de] weights, each routed row of
+    # the expert input read once, each hidden row written once.
+    g1_bytes = active * 2 * H * de * es + kept * de * es + kept * H * es
+    g1_flops = 2 * kept * de * 2 * H
+    g2_bytes = active * de * H * es + kept * H * es + kept * de * es
+    g2_flops = 2 * kept * H * de
+    traffic = measured_traffic(cfg.name)
     line = {
-        "metric": "MoE layer fwd TFLOP/s + tokens/s, % of bf16 MFMA peak (1 MI355X)",
+        "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s (model FLOPs)",
         "n_gpus": 1,
@@ -179,34 +282,159 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded; x ~ N(0,1), weights ~ N(0,1/fan_in))",
-        "config": {"workload": cfg.name, "tokens": cfg.T, "d_model": cfg.D, "latent": cfg.L,
-                   "experts": cfg.E, "top_k": cfg.k, "expert_hidden": cfg.H,
+        "config": {"workload": cfg.name, "tokens": T, "d_model": cfg.D, "latent": cfg.L,
+                   "experts": cfg.E, "top_k": k, "expert_hidden": H,
                    "shared_experts": cfg.n_shared, "shared_hidden": cfg.Hs, "router": "f32",
                    "parallelism": "none (1 GPU)"},
-        "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
-        "pct_bf16_mfma_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
+        "hw_tflops": round(hw_flops / (ms * 1e-3) / 1e12, 2),
         "gpu_ms_per_step_events": round(gpu_ms, 4),
-        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
-        "roofline": {"kernel": "grouped gate/up + SwiGLU GEMM", "bound": "hbm",
-                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
-                     "bytes_per_launch": g1_bytes, "avg_launch_ms": round(g1_ms, 4),
-                     "mfma_frac": round(g1_flops / (g1_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)},
+        "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "roofline": gemm_roofline("grouped gate/up + SwiGLU GEMM", g1_flops, g1_bytes,
+                                  stage_ms["gemm1"], cfg.dtype, traffic),
+        "grouped_down_gemm": gemm_roofline("grouped down GEMM", g2_flops, g2_bytes,
+                                           stage_ms["gemm2"], cfg.dtype),
+        "routed_rows": {"kept": kept, "padded_to_tiles": pad, "active_experts": active,
+                        "max_per_expert": int(cnt.max()), "min_per_expert": int(cnt.min())},
     }
+    # ordered combine: every kept Y row read once, slot_row and weights, c written once
+    comb_bytes = kept * de * es + T * k * 8 + T * de * es
+    hbm = {"combine": hbm_entry(comb_bytes, stage_ms["combine"])}
+    if not args.no_kernel_extras:
+        # The layer's grouping copies no rows (the expert GEMM gathers them); the
+        # stand-alone moe_permute with the row copy is timed here at the same shape.
+        src = torch.randn((T, de), device=dev).to(inp["x"].dtype)
+        dst = torch.empty((T * k, de), dtype=src.dtype, device=dev)
+        pws = torch.empty(M.moe_permute_workspace_size(T * k, cfg.E), dtype=torch.uint8,
+                          device=dev)
+        pout = dict(slot_row=torch.empty(T * k, **i32), row_src=torch.empty(T * k, **i32),
+                    counts=torch.empty(cfg.E, **i32), offsets=torch.empty(cfg.E + 1, **i32),
+                    n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+        pms = time_ms(lambda: M.moe_permute(aux["ids"], cfg.E, src=src, src_div=k, dst=dst,
+                                            ws=pws, out=pout))
+        perm_bytes = T * de * es + T * k * de * es + T * k * 4 * 4
+        hbm["permute_with_row_copy"] = hbm_entry(perm_bytes, pms)
+        hbm["permute_grouping_only"] = {"ms": round(stage_ms["permute"], 4),
+                                        "bytes": T * k * 4 * 4}
+        del src, dst
+    line["hbm_kernels"] = hbm
+    return line, inp
+
+
+def bench_pool(args, cfg, M, dev):
+    import numpy as np
+    import torch
+
+    from moe_synth import gen_pool
+
+    pool = gen_pool(cfg, dev)
+    P, L, H, E = cfg.P, cfg.L, cfg.H, cfg.E
+    ids = pool["ids"]
+    i32 = dict(dtype=torch.int32, device=dev)
+    X_perm = torch.empty((P, L), dtype=torch.bfloat16, device=dev)
+    Y_perm = torch.empty_like(X_perm)
+    out = torch.full((P, L), 0.0, dtype=torch.bfloat16, device=dev)
+    pws = torch.empty(M.moe_permute_workspace_size(P, E), dtype=torch.uint8, device=dev)
+    fws = torch.empty(M.moe_grouped_ffn_workspace_size(E, P, H, torch.bfloat16),
+                      dtype=torch.uint8, device=dev)
+    g = dict(slot_row=torch.empty(P, **i32), row_src=torch.empty(P, **i32),
+             counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+             n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        M.moe_permute(ids, E, src=pool["X"], src_div=1, dst=X_perm, R_phys=P, ws=pws, out=g)
+        if ev:
+            ev[1].record()
+        M.moe_grouped_ffn(X_perm, g["offsets"], pool["W_gu"], pool["W_d"], Y=Y_perm, ws=fws)
+        if ev:
+            ev[2].record()
+        M.moe_combine(Y_perm, g["slot_row"], None, P, 1, out=out,
+                      flags=M.MOE_COMBINE_KEEP_UNROUTED)
+        if ev:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["permute", "grouped_ffn", "unpermute"]
+    stage_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, n in enumerate(names)}
+    cnt = g["counts"].cpu().numpy().astype(np.int64)
+    valid = int(cnt.sum())
+    ms = wall * 1e3 / args.steps
+    flops = cfg.flops(valid)
+    tflops = flops / (ms * 1e-3) / 1e12
+    es = 2
+    ffn_bytes = E * 3 * H * L * es + valid * (L + H + H + L) * es
+    perm_bytes = P * 4 + valid * L * es * 2 + valid * 4 * 2 + P * 4
+    unperm_bytes = valid * L * es * 2 + P * 4
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (model FLOPs)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded receiver pool; rows ~ N(0,1) at unit RMS, Zipf(1) local "
+                "expert ids, weights ~ N(0,1/fan_in))",
+        "config": {"workload": cfg.name, "pool_rows": P, "valid_rows": valid, "latent": L,
+                   "local_experts": E, "expert_hidden": H, "parallelism": "none (1 GPU)"},
+        "rows_per_s": round(valid / (ms * 1e-3), 1),
+        "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
+        "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "roofline": gemm_roofline("grouped FFN (gate/up + SwiGLU and down GEMMs)", flops,
+                                  ffn_bytes, stage_ms["grouped_ffn"], cfg.dtype),
+        "hbm_kernels": {"permute_with_row_copy": hbm_entry(perm_bytes, stage_ms["permute"]),
+                        "unpermute": hbm_entry(unperm_bytes, stage_ms["unpermute"])},
+        "routed_rows": {"valid": valid, "padded_to_tiles": padded_rows(cnt),
+                        "per_expert": cnt.tolist()},
+    }
+    return line, pool
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this library has no multi-GPU path (asked for "
+              f"--gpus {args.gpus}); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mixture_experts_transformer_amd as M
+    from moe_synth import PoolConfig, by_name
+
+    cfg = by_name(args.workload)
+    dev = torch.device("cuda:0")
+    if isinstance(cfg, PoolConfig):
+        line, data = bench_pool(args, cfg, M, dev)
+    else:
+        line, data = bench_layer(args, cfg, M, dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)                           # warm-up copy
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        line["copy_1GiB"] = {"ms": round(e0.elapsed_time(e1), 4),
-                             "GB_per_s": round(2 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)}
+        cms = time_ms(lambda: dst.copy_(src), reps=1)
+        line["copy_1GiB"] = {"ms": round(cms, 4),
+                             "GB_per_s": round(2 * (1 << 30) / (cms * 1e-3) / 1e9, 1)}
+        del src, dst
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        if isinstance(cfg, PoolConfig):
+            line["cpu_baseline"] = cpu_baseline_pool(cfg, data, args.cpu_seconds)
+        else:
+            line["cpu_baseline"] = cpu_baseline_layer(cfg, data, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -16,9 +16,10 @@
 // over a 256 x 256 output tile.  Operands go straight from global memory into
 // LDS with global_load_lds_dwordx4 (no staging registers, no LDS write
 // instructions): a K step is 64 bytes of each of the 256 A rows and 256 B rows
-// (32 KB), and four such stages rotate through 128 KB of LDS, so the loads of
-// the next three steps are in flight while the matrix cores work on the current
-// one.  Within a row the four 16-byte chunks are XOR-swizzled by a function of
+// (32 KB), and four such stages rotate through 128 KB of LDS.  The fragments of
+// a K step are read in two halves, each while the MFMAs of the previous half
+// run, so a buffer is free again as soon as both halves are in registers and
+// the loads of the next three steps are in flight meanwhile.  Within a row the four 16-byte chunks are XOR-swizzled by a function of
 // the row, chosen so that the fragment reads of 8 (or 16) consecutive rows hit
 // distinct banks; the swizzle is applied on the global side, since each DMA
 // instruction fills 1 KB of LDS contiguously.  Waits are explicit (vmcnt of the
@@ -63,6 +64,7 @@ constexpr int kDmaPerStage = 2 * kDmaPerOperand;
 constexpr int kStageLd = 68;      // epilogue staging row stride (floats)
 
 static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
+static_assert((kStages & (kStages - 1)) == 0, "the ring index is a mask");
 
 // Chunk swizzle of LDS row r (r mod 32): 16-byte chunk c is stored at c ^ swz(r).
 // Fragment reads of rows r..r+7 (r..r+15) then hit distinct banks whether the
@@ -81,7 +83,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 // read can still be pending when another wave refills the buffer.  The memory
 // clobber keeps the compiler from moving LDS accesses across.
 __device__ __forceinline__ void bare_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    // lgkmcnt(0) through the builtin, so the compiler's own wait insertion knows
+    // every earlier LDS read has completed and adds no wait for them later
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 __device__ __forceinline__ void dma16(const char* g, char* l) {
@@ -125,6 +132,8 @@ template <typename T, typename OutT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr int kElem = Elem<T>::kBytes;
     constexpr int kSteps = kRowBytes / (Mfma<T>::kK * kElem);   // MFMA k-steps per K step
+    constexpr int kHalf = kSteps / 2;                            // k-steps per half step
+    static_assert(kSteps % 2 == 0, "a K step splits into two halves");
     constexpr int kColsOut = (EPI == EPI_SWIGLU) ? kBN / 2 : kBN;
 
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -247,7 +256,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // own accumulator set.
         auto tile_body = [&](auto nact_c) __attribute__((always_inline)) {
             constexpr int NACT = decltype(nact_c)::value;
-            floatx16 acc[NACT > 0 ? NACT : 1][2];
+            constexpr int NA = NACT > 0 ? NACT : 1;
+            typedef typename Mfma<T>::frag Frag;
+            floatx16 acc[NA][2];
 #pragma unroll
             for (int i = 0; i < NACT; i++)
 #pragma unroll
@@ -286,43 +297,96 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                     for (int i = 0; i < kDmaPerOperand; i++)
                         dma16(b_ptr[i] + koff, b_lds + buf * kStageBytes + i * 1024);
                 };
-
-                // every wave is done with LDS (previous segment, tile or epilogue)
-                __syncthreads();
-#pragma unroll
-                for (int s0 = 0; s0 < kStages - 1; s0++)
-                    if (s0 < nk) issue(s0, s0);
-
-#pragma unroll 1
-                for (int kt = 0; kt < nk; kt++) {
-                    // stage kt has landed once at most the later stages are in flight
-                    if (kt + 2 < nk) wait_vmcnt<2 * kDmaPerStage>();
-                    else if (kt + 1 < nk) wait_vmcnt<kDmaPerStage>();
-                    else wait_vmcnt<0>();
-                    bare_barrier();   // all waves' stage kt landed; stage kt-1 consumed
-                    if (kt + kStages - 1 < nk)
-                        issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-                    if (NACT == 0) continue;
-                    const char* As = lds + (kt % kStages) * kStageBytes + rd_row;
+                // Fragments of one half of a K step (kHalf MFMA k-steps).
+                auto load_half = [&](int buf, int half, Frag (&fa)[kHalf][NA], Frag (&fb)[kHalf][2])
+                    __attribute__((always_inline)) {
+                    const char* As = lds + buf * kStageBytes + rd_row;
                     const char* Bs = As + kBM * kRowBytes;
 #pragma unroll
-                    for (int ks = 0; ks < kSteps; ks++) {
+                    for (int hs = 0; hs < kHalf; hs++) {
+                        const int ks = half * kHalf + hs;
                         const int kb =
                             ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
                         const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
-                        typename Mfma<T>::frag bfr[2], afr[NACT > 0 ? NACT : 1];
 #pragma unroll
                         for (int j = 0; j < 2; j++)
-                            bfr[j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
+                            fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
 #pragma unroll
                         for (int i = 0; i < NACT; i++)
-                            afr[i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+                            fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+                    }
+                };
+                auto mma_half = [&](Frag (&fa)[kHalf][NA], Frag (&fb)[kHalf][2])
+                    __attribute__((always_inline)) {
+#pragma unroll
+                    for (int hs = 0; hs < kHalf; hs++)
 #pragma unroll
                         for (int i = 0; i < NACT; i++)
 #pragma unroll
                             for (int j = 0; j < 2; j++)
-                                acc[i][j] = Mfma<T>::mma(afr[i], bfr[j], acc[i][j]);
+                                acc[i][j] = Mfma<T>::mma(fa[hs][i], fb[hs][j], acc[i][j]);
+                };
+                // Instruction order within a half step: one MFMA, then the
+                // fragment reads of the next half, then the remaining MFMAs, so
+                // the reads have the whole half step to complete.
+                auto order_half = [&]() __attribute__((always_inline)) {
+                    constexpr int kReads = kHalf * (NACT + 2);
+                    constexpr int kMfmas = kHalf * NACT * 2;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 1, 0);
+                };
+                // every wave is done with LDS (previous segment, tile or epilogue)
+                __syncthreads();
+#pragma unroll
+                for (int s0 = 0; s0 < kStages; s0++)
+                    if (s0 < nk) issue(s0, s0);
+                // stage 0 has landed once at most the other issued stages are in flight
+                switch (min(nk, kStages) - 1) {
+                    case 0: wait_vmcnt<0>(); break;
+                    case 1: wait_vmcnt<kDmaPerStage>(); break;
+                    case 2: wait_vmcnt<2 * kDmaPerStage>(); break;
+                    default: wait_vmcnt<3 * kDmaPerStage>(); break;
+                }
+                bare_barrier();
+                Frag f0a[kHalf][NA], f0b[kHalf][2], f1a[kHalf][NA], f1b[kHalf][2];
+                if (NACT > 0) load_half(0, 0, f0a, f0b);
+
+                // Software pipeline over K steps: the second half of step kt is
+                // read while the first half's MFMAs run, and the first half of
+                // step kt+1 is read (after the barrier that makes it visible)
+                // while the second half's MFMAs run, so the matrix cores never
+                // wait for a fragment read after a barrier.  A buffer is refilled
+                // as soon as both of its halves are in registers, four steps ahead.
+#pragma unroll 1
+                for (int kt = 0; kt + 1 < nk; kt++) {
+                    const int buf = kt & (kStages - 1);
+                    if (NACT > 0) {
+                        load_half(buf, 1, f1a, f1b);
+                        mma_half(f0a, f0b);
+                        order_half();
                     }
+                    // step kt+1 has landed once at most the later issued steps
+                    // (kt+2, kt+3) are in flight
+                    const int later = min(nk, kt + kStages) - (kt + 2);
+                    if (later >= 2) wait_vmcnt<2 * kDmaPerStage>();
+                    else if (later == 1) wait_vmcnt<kDmaPerStage>();
+                    else wait_vmcnt<0>();
+                    // all waves' step kt+1 landed, and every read of buffer buf
+                    // (both halves of step kt) has completed
+                    bare_barrier();
+                    if (kt + kStages < nk) issue(kt + kStages, buf);
+                    if (NACT > 0) {
+                        load_half((kt + 1) & (kStages - 1), 0, f0a, f0b);
+                        mma_half(f1a, f1b);
+                        order_half();
+                    }
+                }
+                // last step (its first half is already in registers)
+                if (NACT > 0) {
+                    load_half((nk - 1) & (kStages - 1), 1, f1a, f1b);
+                    mma_half(f0a, f0b);
+                    mma_half(f1a, f1b);
                 }
             }
             __syncthreads();      // LDS is reused for the epilogue

@@ -139,18 +139,26 @@ def moe_permute_workspace_size(n_assign: int, E: int) -> int:
     return int(_lib.moe_permute_workspace_size(n_assign, E))
 
 
-def moe_permute(ids, E, capacity=-1, src=None, src_div=1, dst=None, R_phys=None, ws=None):
+def moe_permute(ids, E, capacity=-1, src=None, src_div=1, dst=None, R_phys=None, ws=None,
+                out=None):
     """Group assignments by expert.  Returns dict(slot_row, row_src, counts, offsets,
-    n_dropped) of device tensors (and fills dst if given)."""
+    n_dropped) of device tensors (and fills dst if given).  `out` may supply those
+    tensors (row_src with at least max(R_phys, 1) entries)."""
     ids = ids.reshape(-1)
     n = ids.numel()
     R_phys = n if R_phys is None else R_phys
     dev = ids.device
-    out = dict(slot_row=torch.empty(n, dtype=torch.int32, device=dev),
-               row_src=torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev),
-               counts=torch.empty(E, dtype=torch.int32, device=dev),
-               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-               n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    if out is None:
+        out = dict(slot_row=torch.empty(n, dtype=torch.int32, device=dev),
+                   row_src=torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev),
+                   counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    else:
+        out = dict(out)
+        if (out["slot_row"].numel() < n or out["row_src"].numel() < max(R_phys, 1)
+                or out["counts"].numel() < E or out["offsets"].numel() < E + 1):
+            raise ValueError("moe_permute: an `out` tensor is too small")
     need = moe_permute_workspace_size(n, E)
     ws = _ws(need, dev, ws)
     width = src.shape[-1] if src is not None else 0
