@@ -129,7 +129,9 @@ size_t moe_permute_workspace_size(int64_t n_assign, int32_t E);
  *   Y      (device) [R_phys, d] in dt
  *   ws     (device) moe_grouped_ffn_workspace_size(E, R_phys, H, dt) bytes
  * Accumulation is float32; the hidden h is stored in dt.
- * Limits: d and H multiples of 32, E <= 1024. */
+ * Limits: d and H multiples of 64 for MOE_BF16 and of 32 for MOE_F32 (whole
+ * 128-byte steps along each reduction), E <= 1024, and every expert's weight
+ * matrix under 4 GiB; otherwise MOE_ESHAPE. */
 moe_status moe_grouped_ffn(const void *X, const int32_t *offsets, int32_t E, int64_t R_phys,
                            const void *W_gu, const void *W_d, int64_t d, int64_t H,
                            moe_dtype dt, void *Y, void *ws, size_t ws_bytes, moe_stream stream);
@@ -207,7 +209,9 @@ typedef struct {
 /* The whole layer forward.  x (device) [T, D] dtype -> y (device) [T, D] dtype.
  * aux may be NULL; each of its pointers may be NULL.  ws: device workspace of
  * moe_layer_workspace_size(d) bytes.  Limits: those of the parts, plus D, L, H,
- * Hs multiples of 32 and n_shared <= 3. */
+ * Hs multiples of 64 for MOE_BF16 and of 32 for MOE_F32, n_shared <= 3, and the
+ * expert input [T, L] (or [T, D] without a latent) under 4 GiB; otherwise
+ * MOE_ESHAPE. */
 moe_status moe_layer_fwd(const moe_layer_desc *d, const moe_layer_weights *W, const void *x,
                          void *y, const moe_layer_aux *aux, void *ws, size_t ws_bytes,
                          moe_stream stream);

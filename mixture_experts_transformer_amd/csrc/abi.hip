@@ -18,6 +18,14 @@ inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline int esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
 inline bool dt_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 inline hipStream_t hs(moe_stream s) { return (hipStream_t)s; }
+// A GEMM reduction or output width: whole 128-byte K steps and 32-column blocks.
+inline bool width_ok(int64_t w, moe_dtype dt) {
+    return w > 0 && w % 32 == 0 && (w * esize(dt)) % gemm_k_bytes() == 0;
+}
+// Every DMA source offset of the GEMMs is a 32-bit byte offset from a base.
+inline bool under4g(int64_t rows, int64_t width, moe_dtype dt) {
+    return rows * width * esize(dt) < ((int64_t)1 << 32);
+}
 
 #define MOE_TRY(expr)                              \
     do {                                           \
@@ -70,11 +78,13 @@ GemmParams gemm_base() {
 // Grouped gated MLP over row groups: h = SwiGLU(X W_gu[g]^T), Y = h W_d[g]^T.
 // X rows optionally gathered (a_rows / a_div).
 moe_status grouped_ffn_impl(const void* X, int64_t ldx, const int32_t* a_rows, int a_div,
-                            const int32_t* offsets, const int32_t* tile_prefix, int E,
-                            int64_t R_rows, const void* W_gu, const void* W_d, int64_t d,
-                            int64_t H, moe_dtype dt, void* h, void* Y, hipStream_t s) {
+                            int64_t a_src_rows, const int32_t* offsets,
+                            const int32_t* tile_prefix, int E, int64_t R_rows, const void* W_gu,
+                            const void* W_d, int64_t d, int64_t H, moe_dtype dt, void* h,
+                            void* Y, hipStream_t s) {
     GemmParams p = gemm_base();
     p.group_m = kGroupGrouped;
+    p.a_src_rows = a_src_rows;
     p.offsets = offsets;
     p.tile_prefix = tile_prefix;
     p.G = E;
@@ -162,7 +172,17 @@ moe_status check_layer(const moe_layer_desc* d, const moe_layer_weights* W, cons
     if (d->T < 0 || d->D <= 0 || d->L < 0 || d->H <= 0) return MOE_ESHAPE;
     if (d->E < 1 || d->E > 512 || d->k < 1 || d->k > 16 || d->k > d->E) return MOE_ESHAPE;
     if (d->n_shared < 0 || d->n_shared > 3 || (d->n_shared > 0 && d->Hs <= 0)) return MOE_ESHAPE;
-    if (d->D % 32 || d->L % 32 || d->H % 32 || (d->n_shared > 0 && d->Hs % 32)) return MOE_ESHAPE;
+    if (!width_ok(d->D, d->dtype) || (d->L > 0 && !width_ok(d->L, d->dtype)) ||
+        !width_ok(d->H, d->dtype) || (d->n_shared > 0 && !width_ok(d->Hs, d->dtype)))
+        return MOE_ESHAPE;
+    {
+        const int64_t de = d->L > 0 ? d->L : d->D;
+        // the routed GEMM gathers its rows from the [T, de] expert input, and an
+        // expert's weights span 2H rows
+        if (!under4g(d->T + 1, de, d->dtype) || !under4g(2 * d->H + 1, de, d->dtype) ||
+            !under4g(de + 1, d->H, d->dtype))
+            return MOE_ESHAPE;
+    }
     if (d->T * d->k >= ((int64_t)1 << 31)) return MOE_ESHAPE;
     if (!(d->eps >= 0.0f)) return MOE_EINVAL;
     if (!W->W_r || !W->W_gu || !W->W_d) return MOE_EINVAL;
@@ -260,8 +280,9 @@ moe_status moe_grouped_ffn(const void* X, const int32_t* offsets, int32_t E, int
                            const void* W_gu, const void* W_d, int64_t d, int64_t H, moe_dtype dt,
                            void* Y, void* ws, size_t ws_bytes, moe_stream stream) {
     if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
-    if (d <= 0 || H <= 0 || d % 32 || H % 32) return MOE_ESHAPE;
     if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (!width_ok(d, dt) || !width_ok(H, dt)) return MOE_ESHAPE;
+    if (!under4g(2 * H + 1, d, dt) || !under4g(d + 1, H, dt)) return MOE_ESHAPE;
     if (!offsets || !W_gu || !W_d || (R_phys > 0 && (!X || !Y))) return MOE_EINVAL;
     const void* ptrs[] = {X, offsets, W_gu, W_d, Y, ws};
     for (const void* p : ptrs)
@@ -273,8 +294,8 @@ moe_status moe_grouped_ffn(const void* X, const int32_t* offsets, int32_t E, int
     void* h = cv.take<char>((size_t)R_phys * H * esize(dt));
     hipStream_t s = hs(stream);
     MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tp, s));
-    moe_status st = grouped_ffn_impl(X, d, nullptr, 1, offsets, tp, E, R_phys, W_gu, W_d, d, H, dt,
-                                     h, Y, s);
+    moe_status st = grouped_ffn_impl(X, d, nullptr, 1, 0, offsets, tp, E, R_phys, W_gu, W_d, d,
+                                     H, dt, h, Y, s);
     if (st != MOE_OK) return st;
     return grouped_down_impl(h, offsets, tp, E, R_phys, W_d, d, H, dt, Y, s);
 }
@@ -364,8 +385,8 @@ moe_status moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* W, co
                            b.perm_ws, s));
     if (!mark(MOE_EV_PERMUTE)) return MOE_ELAUNCH;
     // 4-5. routed experts
-    st = grouped_ffn_impl(e_in, de, b.row_src, k, offsets, b.tile_prefix, E, R, W->W_gu, W->W_d,
-                          de, H, dt, b.h, b.Y, s);
+    st = grouped_ffn_impl(e_in, de, b.row_src, k, T, offsets, b.tile_prefix, E, R, W->W_gu,
+                          W->W_d, de, H, dt, b.h, b.Y, s);
     if (st != MOE_OK) return st;
     if (!mark(MOE_EV_GEMM1)) return MOE_ELAUNCH;
     st = grouped_down_impl(b.h, offsets, b.tile_prefix, E, R, W->W_d, de, H, dt, b.Y, s);

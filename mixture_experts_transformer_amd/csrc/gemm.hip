@@ -15,15 +15,18 @@
 // Tiling (one workgroup per CU): 512 threads = 8 waves (two per SIMD) as 2 x 4
 // over a 256 x 256 output tile.  Operands go straight from global memory into
 // LDS with global_load_lds_dwordx4 (no staging registers, no LDS write
-// instructions): a K step is 64 bytes of each of the 256 A rows and 256 B rows
-// (32 KB), and four such stages rotate through 128 KB of LDS.  The fragments of
-// a K step are read in two halves, each while the MFMAs of the previous half
-// run, so a buffer is free again as soon as both halves are in registers and
-// the loads of the next three steps are in flight meanwhile.  Within a row the four 16-byte chunks are XOR-swizzled by a function of
-// the row, chosen so that the fragment reads of 8 (or 16) consecutive rows hit
-// distinct banks; the swizzle is applied on the global side, since each DMA
-// instruction fills 1 KB of LDS contiguously.  Waits are explicit (vmcnt of the
-// stages still allowed in flight) followed by a bare s_barrier.
+// instructions).  A K step is 128 bytes -- one whole cache line -- of each of the
+// 256 A rows and 256 B rows (64 KB): with 64-byte row pieces every DMA
+// instruction would touch half of each of 16 lines and the L2-to-LDS rate
+// halves.  Two such steps alternate in LDS.  The fragments of a K step are read
+// in four quarters, each while the MFMAs of the previous quarter run, so the
+// barrier at the end of a step finds the buffer fully read and it is refilled
+// at once, two steps ahead.  Within a row the eight 16-byte chunks are
+// XOR-swizzled by a function of the row, chosen so that the fragment reads of 8
+// (or 16) consecutive rows hit distinct banks; the swizzle is applied on the
+// global side, since each DMA instruction fills 1 KB of LDS contiguously.  Each
+// DMA source is a wave-uniform base plus a 32-bit per-lane offset.  Waits are
+// explicit (vmcnt) followed by a bare s_barrier.
 //
 // Each wave owns up to 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (a 128 x 64
 // sub-tile, 128 accumulators).  The wave's 32-row blocks are interleaved (wm,
@@ -56,20 +59,19 @@ constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 constexpr int kBM = 256;          // rows per tile
 constexpr int kBN = 256;          // B rows (LDS columns) per tile
-constexpr int kRowBytes = 64;     // bytes of each row per K step
-constexpr int kStages = 4;        // LDS ring of K steps
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;   // 32 KB
+constexpr int kRowBytes = 128;    // bytes of each row per K step: whole cache lines
+constexpr int kStages = 2;        // LDS double buffer of K steps
+constexpr int kStageBytes = (kBM + kBN) * kRowBytes;   // 64 KB
 constexpr int kDmaPerOperand = kBM * kRowBytes / 1024 / kWaves;   // 1-KB DMAs per wave
 constexpr int kDmaPerStage = 2 * kDmaPerOperand;
 constexpr int kStageLd = 68;      // epilogue staging row stride (floats)
 
 static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
-static_assert((kStages & (kStages - 1)) == 0, "the ring index is a mask");
 
-// Chunk swizzle of LDS row r (r mod 32): 16-byte chunk c is stored at c ^ swz(r).
-// Fragment reads of rows r..r+7 (r..r+15) then hit distinct banks whether the
-// LDS serves 8 or 16 lanes of a 16-byte read per cycle.
-__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+// Chunk swizzle of LDS row r (128-byte rows, eight 16-byte chunks): chunk c is
+// stored at c ^ swz(r).  Fragment reads of rows r..r+7 (r..r+15) then hit
+// distinct banks whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
+__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
 // expcnt and lgkmcnt left at "no wait").
@@ -132,8 +134,8 @@ template <typename T, typename OutT, int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr int kElem = Elem<T>::kBytes;
     constexpr int kSteps = kRowBytes / (Mfma<T>::kK * kElem);   // MFMA k-steps per K step
-    constexpr int kHalf = kSteps / 2;                            // k-steps per half step
-    static_assert(kSteps % 2 == 0, "a K step splits into two halves");
+    constexpr int kSub = kSteps / 4;                             // k-steps per quarter step
+    static_assert(kSteps % 4 == 0, "a K step splits into four quarters");
     constexpr int kColsOut = (EPI == EPI_SWIGLU) ? kBN / 2 : kBN;
 
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -182,21 +184,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         const int n_act = (nrb - wm + 1) >> 1;              // this wave's active blocks
         const int64_t n0 = tn * kColsOut;
 
-        // ---- DMA sources.  Wave w fills LDS rows 32 w + 16 i + lane / 4
-        // (i < 2) of each operand, chunk lane % 4, which holds logical chunk
-        // (lane % 4) ^ swz(row).  Row indices fit in 32 bits (checked on the host).
-        const int lrow = wave * (16 * kDmaPerOperand) + (lane >> 2);
+        // ---- DMA sources.  Wave w fills LDS rows 32 w + 8 i + lane / 8
+        // (i < 4) of each operand, chunk lane % 8, which holds logical chunk
+        // (lane % 8) ^ swz(row).  Each source is a wave-uniform base (A's tile
+        // or gather base, B's group) plus a 32-bit per-lane byte offset; the
+        // host checks that every offset fits.
+        constexpr int kLanesPerRow = kRowBytes / 16;
+        const int lrow = wave * ((64 / kLanesPerRow) * kDmaPerOperand) + lane / kLanesPerRow;
         int32_t a_src[kDmaPerOperand], b_src[kDmaPerOperand];
         int chunk[kDmaPerOperand];
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++) {
-            const int r = lrow + 16 * i;
-            chunk[i] = ((lane & 3) ^ swz(r & 31)) * 16;
-            // rows past the group's end read the group's first row; their
+            const int r = lrow + (64 / kLanesPerRow) * i;
+            chunk[i] = ((lane % kLanesPerRow) ^ swz(r & 31)) * 16;
+            // rows past the group's end read the tile's first row; their
             // results are never stored
-            int32_t src = (int32_t)(row0 + (r < rows_valid ? r : 0));
-            if (p.a_rows) src = p.a_rows[src] / p.a_div;
-            a_src[i] = src;
+            const int rl = r < rows_valid ? r : 0;
+            // gathered: the source row itself; else the row within the tile
+            a_src[i] = p.a_rows ? p.a_rows[row0 + rl] / p.a_div : rl;
             int64_t col, brow;
             if (EPI == EPI_SWIGLU) {
                 // each 64-row slice of B: [gate 32 | up 32] of 32 hidden columns
@@ -208,8 +213,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 col = n0 + r;
                 brow = col;
             }
-            b_src[i] = (int32_t)((col < p.N ? brow : 0) + (int64_t)g * p.b_group_rows);
+            b_src[i] = (int32_t)(col < p.N ? brow : 0);     // row within the group
         }
+        const int64_t a_row_base = p.a_rows ? 0 : row0;
+        const int64_t b_row_base = (int64_t)g * p.b_group_rows;
         char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
         char* const b_lds = lds + kBM * kRowBytes + (wave * kDmaPerOperand) * 1024;
 
@@ -281,30 +288,34 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 const int64_t ldb = uniform64(segs[sidx].ldb);
                 const int K = __builtin_amdgcn_readfirstlane(segs[sidx].K);
                 const int nk = __builtin_amdgcn_readfirstlane(K * kElem / kRowBytes);
-                const char* a_ptr[kDmaPerOperand];
-                const char* b_ptr[kDmaPerOperand];
+                const char* const A_t = (const char*)uniform64(
+                    (int64_t)(A + a_row_base * lda * kElem));
+                const char* const B_t = (const char*)uniform64(
+                    (int64_t)(B + b_row_base * ldb * kElem));
+                uint32_t a_off[kDmaPerOperand], b_off[kDmaPerOperand];
 #pragma unroll
                 for (int i = 0; i < kDmaPerOperand; i++) {
-                    a_ptr[i] = A + (int64_t)a_src[i] * lda * kElem + chunk[i];
-                    b_ptr[i] = B + (int64_t)b_src[i] * ldb * kElem + chunk[i];
+                    a_off[i] = (uint32_t)((int64_t)a_src[i] * lda * kElem) + chunk[i];
+                    b_off[i] = (uint32_t)((int64_t)b_src[i] * ldb * kElem) + chunk[i];
                 }
                 auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
-                    const int64_t koff = (int64_t)kt * kRowBytes;
+                    const char* const Ak = A_t + (int64_t)kt * kRowBytes;
+                    const char* const Bk = B_t + (int64_t)kt * kRowBytes;
 #pragma unroll
                     for (int i = 0; i < kDmaPerOperand; i++)
-                        dma16(a_ptr[i] + koff, a_lds + buf * kStageBytes + i * 1024);
+                        dma16(Ak + a_off[i], a_lds + buf * kStageBytes + i * 1024);
 #pragma unroll
                     for (int i = 0; i < kDmaPerOperand; i++)
-                        dma16(b_ptr[i] + koff, b_lds + buf * kStageBytes + i * 1024);
+                        dma16(Bk + b_off[i], b_lds + buf * kStageBytes + i * 1024);
                 };
-                // Fragments of one half of a K step (kHalf MFMA k-steps).
-                auto load_half = [&](int buf, int half, Frag (&fa)[kHalf][NA], Frag (&fb)[kHalf][2])
+                // Fragments of one quarter of a K step (kSub MFMA k-steps).
+                auto load_sub = [&](int buf, int q, Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
                     __attribute__((always_inline)) {
                     const char* As = lds + buf * kStageBytes + rd_row;
                     const char* Bs = As + kBM * kRowBytes;
 #pragma unroll
-                    for (int hs = 0; hs < kHalf; hs++) {
-                        const int ks = half * kHalf + hs;
+                    for (int hs = 0; hs < kSub; hs++) {
+                        const int ks = q * kSub + hs;
                         const int kb =
                             ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
                         const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
@@ -316,77 +327,79 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                             fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
                     }
                 };
-                auto mma_half = [&](Frag (&fa)[kHalf][NA], Frag (&fb)[kHalf][2])
+                auto mma_sub = [&](Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
                     __attribute__((always_inline)) {
 #pragma unroll
-                    for (int hs = 0; hs < kHalf; hs++)
+                    for (int hs = 0; hs < kSub; hs++)
 #pragma unroll
                         for (int i = 0; i < NACT; i++)
 #pragma unroll
                             for (int j = 0; j < 2; j++)
                                 acc[i][j] = Mfma<T>::mma(fa[hs][i], fb[hs][j], acc[i][j]);
                 };
-                // Instruction order within a half step: one MFMA, then the
-                // fragment reads of the next half, then the remaining MFMAs, so
-                // the reads have the whole half step to complete.
-                auto order_half = [&]() __attribute__((always_inline)) {
-                    constexpr int kReads = kHalf * (NACT + 2);
-                    constexpr int kMfmas = kHalf * NACT * 2;
+                // Instruction order within a quarter step: one MFMA, then the
+                // fragment reads of the next quarter, then the remaining MFMAs, so
+                // the reads have the whole quarter step to complete.
+                auto order_sub = [&]() __attribute__((always_inline)) {
+                    constexpr int kReads = kSub * (NACT + 2);
+                    constexpr int kMfmas = kSub * NACT * 2;
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
                     __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 1, 0);
                 };
                 // every wave is done with LDS (previous segment, tile or epilogue)
                 __syncthreads();
-#pragma unroll
-                for (int s0 = 0; s0 < kStages; s0++)
-                    if (s0 < nk) issue(s0, s0);
-                // stage 0 has landed once at most the other issued stages are in flight
-                switch (min(nk, kStages) - 1) {
-                    case 0: wait_vmcnt<0>(); break;
-                    case 1: wait_vmcnt<kDmaPerStage>(); break;
-                    case 2: wait_vmcnt<2 * kDmaPerStage>(); break;
-                    default: wait_vmcnt<3 * kDmaPerStage>(); break;
+                static_assert(kStages == 2, "the waits below are written for a double buffer");
+                issue(0, 0);
+                if (nk > 1) {
+                    issue(1, 1);
+                    wait_vmcnt<kDmaPerStage>();      // step 0 landed, step 1 in flight
+                } else {
+                    wait_vmcnt<0>();
                 }
                 bare_barrier();
-                Frag f0a[kHalf][NA], f0b[kHalf][2], f1a[kHalf][NA], f1b[kHalf][2];
-                if (NACT > 0) load_half(0, 0, f0a, f0b);
+                Frag f0a[kSub][NA], f0b[kSub][2], f1a[kSub][NA], f1b[kSub][2];
+                if (NACT > 0) load_sub(0, 0, f0a, f0b);
 
-                // Software pipeline over K steps: the second half of step kt is
-                // read while the first half's MFMAs run, and the first half of
-                // step kt+1 is read (after the barrier that makes it visible)
-                // while the second half's MFMAs run, so the matrix cores never
-                // wait for a fragment read after a barrier.  A buffer is refilled
-                // as soon as both of its halves are in registers, four steps ahead.
+                // Software pipeline over the quarters of the K steps: each
+                // quarter's fragments are read while the MFMAs of the previous one
+                // run.  After the third quarter's reads the wave waits for step
+                // kt+1 to land and meets the others at the barrier; by then every
+                // read of step kt's buffer has completed, so the buffer is
+                // refilled with step kt+2 straight away.
+                int buf = 0;                  // buffer of step kt
 #pragma unroll 1
                 for (int kt = 0; kt + 1 < nk; kt++) {
-                    const int buf = kt & (kStages - 1);
                     if (NACT > 0) {
-                        load_half(buf, 1, f1a, f1b);
-                        mma_half(f0a, f0b);
-                        order_half();
+                        load_sub(buf, 1, f1a, f1b);
+                        mma_sub(f0a, f0b);
+                        order_sub();
+                        load_sub(buf, 2, f0a, f0b);
+                        mma_sub(f1a, f1b);
+                        order_sub();
+                        load_sub(buf, 3, f1a, f1b);
+                        mma_sub(f0a, f0b);
+                        order_sub();
                     }
-                    // step kt+1 has landed once at most the later issued steps
-                    // (kt+2, kt+3) are in flight
-                    const int later = min(nk, kt + kStages) - (kt + 2);
-                    if (later >= 2) wait_vmcnt<2 * kDmaPerStage>();
-                    else if (later == 1) wait_vmcnt<kDmaPerStage>();
-                    else wait_vmcnt<0>();
-                    // all waves' step kt+1 landed, and every read of buffer buf
-                    // (both halves of step kt) has completed
+                    wait_vmcnt<0>();          // step kt+1 (the only one in flight) landed
                     bare_barrier();
-                    if (kt + kStages < nk) issue(kt + kStages, buf);
+                    if (kt + 2 < nk) issue(kt + 2, buf);
+                    buf ^= 1;
                     if (NACT > 0) {
-                        load_half((kt + 1) & (kStages - 1), 0, f0a, f0b);
-                        mma_half(f1a, f1b);
-                        order_half();
+                        load_sub(buf, 0, f0a, f0b);
+                        mma_sub(f1a, f1b);
+                        order_sub();
                     }
                 }
-                // last step (its first half is already in registers)
+                // last step (its first quarter is already in registers)
                 if (NACT > 0) {
-                    load_half((nk - 1) & (kStages - 1), 1, f1a, f1b);
-                    mma_half(f0a, f0b);
-                    mma_half(f1a, f1b);
+                    load_sub(buf, 1, f1a, f1b);
+                    mma_sub(f0a, f0b);
+                    load_sub(buf, 2, f0a, f0b);
+                    mma_sub(f1a, f1b);
+                    load_sub(buf, 3, f1a, f1b);
+                    mma_sub(f0a, f0b);
+                    mma_sub(f1a, f1b);
                 }
             }
             __syncthreads();      // LDS is reused for the epilogue
@@ -456,6 +469,23 @@ hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
 
 int gemm_block_m() { return kBM; }
 
+int gemm_k_bytes() { return kRowBytes; }
+
+bool gemm_offsets_fit(const GemmParams& p, int es) {
+    const int64_t lim = (int64_t)1 << 32;
+    for (int s = 0; s < p.nseg; s++) {
+        const GemmSeg& g = p.seg[s];
+        // A: offsets from the gather base (any source row) or from the tile's row 0
+        const int64_t a_rows = p.a_rows ? p.a_src_rows : kBM;
+        if ((a_rows * g.lda + g.K) * es >= lim) return false;
+        // B: offsets from the group's first row (a dense SwiGLU B has 2N rows)
+        const int64_t b_rows = p.offsets ? p.b_group_rows : 2 * p.N;
+        if ((b_rows * g.ldb + g.K) * es >= lim) return false;
+        if (((int64_t)g.K * es) % kRowBytes) return false;
+    }
+    return true;
+}
+
 int gemm_cols_per_tile(int epi) { return epi == EPI_SWIGLU ? kBN / 2 : kBN; }
 
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp, hipStream_t s) {
@@ -465,6 +495,8 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp
 
 hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,
                        int64_t max_tiles, hipStream_t s) {
+    // the C ABI has checked these already; a violation here is a library bug
+    if (!gemm_offsets_fit(p, in_dt == MOE_BF16 ? 2 : 4)) return hipErrorInvalidValue;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)

@@ -32,6 +32,7 @@ struct GemmParams {
     int32_t a_div;
     int64_t N;                   // output columns
     int64_t n_per;               // SwiGLU: hidden columns per [gate; up] block of B
+    int64_t a_src_rows;          // gather: rows of the A matrix a_rows indexes (host check)
     int32_t group_m;             // row tiles per swizzle group
     GemmSeg seg[kMaxSeg];
     int32_t nseg;
@@ -42,6 +43,11 @@ struct GemmParams {
 };
 
 int gemm_block_m();
+// Bytes of each row per K step: every segment's K * element size must be a
+// multiple of it.
+int gemm_k_bytes();
+// True if every per-lane DMA byte offset of the GEMM fits in 32 bits.
+bool gemm_offsets_fit(const GemmParams& p, int elem_bytes);
 int gemm_cols_per_tile(int epi);
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,

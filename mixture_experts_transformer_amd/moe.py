@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built: run `python -m mixture_experts_transformer_amd.build`"
+    raise ImportError(f"{LIB_PATH} is not built: run `python mixture_experts_transformer_amd/build.py`"
                       " (or __graft_entry__.build()); there is no non-HIP fallback")
 _lib = C.CDLL(LIB_PATH)
 

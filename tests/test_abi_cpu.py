@@ -96,6 +96,12 @@ def test_layer_rejects_bad_descriptors(lib):
     assert call(bad) == 2
     bad = B.layer_desc(64, 100, 64, 8, 2, 64, 1, 64, "bf16")       # D not a multiple of 32
     assert call(bad) == 2
+    bad = B.layer_desc(64, 128, 64, 8, 2, 96, 1, 64, "bf16")       # bf16 H: 192-byte rows
+    assert call(bad) == 2
+    ok_f32 = B.layer_desc(64, 128, 64, 8, 2, 96, 1, 64, "f32")     # f32 H = 96: 384 bytes
+    assert call(ok_f32, ws=4096, wsb=16) == 5                       # passes the shape checks
+    big = B.layer_desc(1 << 20, 4096, 2048, 8, 2, 64, 1, 64, "bf16")   # [T, L] input of 4 GiB
+    assert call(big) == 2
     bad = B.layer_desc(64, 128, 64, 8, 2, 64, 4, 64, "bf16")       # too many shared experts
     assert call(bad) == 2
     assert call(d, wsb=16) == 5                                    # workspace too small
