@@ -61,9 +61,10 @@ int64_t dense_tiles(int64_t rows, int64_t N, int epi) {
 // near lockstep along K, so with 8 row tiles per group each B slice is shared by
 // 8 concurrent tiles and each A slice by 4 (dense GEMMs).  Grouped GEMMs keep
 // the row tiles of one expert's weight slices together and walk the columns
-// innermost, so the expert's gathered rows stay in L2 across its column tiles
-// (measured faster than grouping at the 535B shape, where an expert has one
-// row tile).
+// innermost, so the expert's rows stay in L2 across its column tiles while its
+// weights stream past.  Measured faster than grouping by 8 both at the 535B
+// shape, where an expert has one row tile, and on the 6-expert receiver pool,
+// where it has dozens (3.17 vs 3.38 ms for the pool's two grouped GEMMs).
 constexpr int kGroupDense = 8;
 constexpr int kGroupGrouped = 1;
 
