@@ -18,10 +18,11 @@
 // instructions).  A K step is 128 bytes -- one whole cache line -- of each of the
 // 256 A rows and 256 B rows (64 KB): with 64-byte row pieces every DMA
 // instruction would touch half of each of 16 lines and the L2-to-LDS rate
-// halves.  Two such steps alternate in LDS.  The fragments of a K step are read
-// in four quarters, each while the MFMAs of the previous quarter run, so the
-// barrier at the end of a step finds the buffer fully read and it is refilled
-// at once, two steps ahead.  Within a row the eight 16-byte chunks are
+// halves.  A's steps alternate in two LDS slots and B's (the weights, streamed
+// from HBM in the grouped GEMMs) rotate through three, so B runs two steps
+// ahead: all 160 KB of LDS.  The fragments of a K step are read in four
+// quarters, each while the MFMAs of the previous quarter run, so the barrier at
+// the end of a step finds its slots fully read and they are refilled at once.  Within a row the eight 16-byte chunks are
 // XOR-swizzled by a function of the row, chosen so that the fragment reads of 8
 // (or 16) consecutive rows hit distinct banks; the swizzle is applied on the
 // global side, since each DMA instruction fills 1 KB of LDS contiguously.  Each
@@ -60,10 +61,11 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kBM = 256;          // rows per tile
 constexpr int kBN = 256;          // B rows (LDS columns) per tile
 constexpr int kRowBytes = 128;    // bytes of each row per K step: whole cache lines
-constexpr int kStages = 2;        // LDS double buffer of K steps
-constexpr int kStageBytes = (kBM + kBN) * kRowBytes;   // 64 KB
+constexpr int kOpBytes = kBM * kRowBytes;              // one operand's K step: 32 KB
+constexpr int kSlotsA = 2;        // LDS ring of A steps
+constexpr int kSlotsB = 3;        // LDS ring of B steps (the streamed weights run further ahead)
+constexpr int kBBase = kSlotsA * kOpBytes;             // B ring offset in LDS
 constexpr int kDmaPerOperand = kBM * kRowBytes / 1024 / kWaves;   // 1-KB DMAs per wave
-constexpr int kDmaPerStage = 2 * kDmaPerOperand;
 constexpr int kStageLd = 68;      // epilogue staging row stride (floats)
 
 static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         const int64_t a_row_base = p.a_rows ? 0 : row0;
         const int64_t b_row_base = (int64_t)g * p.b_group_rows;
         char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
-        char* const b_lds = lds + kBM * kRowBytes + (wave * kDmaPerOperand) * 1024;
+        char* const b_lds = lds + kBBase + (wave * kDmaPerOperand) * 1024;
 
         // One wave's staged 32 x W block (W = 32 hidden columns for SwiGLU, else
         // 64 columns) leaves in 16-byte chunks of output elements.
@@ -298,21 +300,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                     a_off[i] = (uint32_t)((int64_t)a_src[i] * lda * kElem) + chunk[i];
                     b_off[i] = (uint32_t)((int64_t)b_src[i] * ldb * kElem) + chunk[i];
                 }
-                auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+                auto issue_a = [&](int kt, int slot) __attribute__((always_inline)) {
                     const char* const Ak = A_t + (int64_t)kt * kRowBytes;
+#pragma unroll
+                    for (int i = 0; i < kDmaPerOperand; i++)
+                        dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
+                };
+                auto issue_b = [&](int kt, int slot) __attribute__((always_inline)) {
                     const char* const Bk = B_t + (int64_t)kt * kRowBytes;
 #pragma unroll
                     for (int i = 0; i < kDmaPerOperand; i++)
-                        dma16(Ak + a_off[i], a_lds + buf * kStageBytes + i * 1024);
-#pragma unroll
-                    for (int i = 0; i < kDmaPerOperand; i++)
-                        dma16(Bk + b_off[i], b_lds + buf * kStageBytes + i * 1024);
+                        dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
                 };
                 // Fragments of one quarter of a K step (kSub MFMA k-steps).
-                auto load_sub = [&](int buf, int q, Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
-                    __attribute__((always_inline)) {
-                    const char* As = lds + buf * kStageBytes + rd_row;
-                    const char* Bs = As + kBM * kRowBytes;
+                auto load_sub = [&](int sa, int sb, int q, Frag (&fa)[kSub][NA],
+                                    Frag (&fb)[kSub][2]) __attribute__((always_inline)) {
+                    const char* As = lds + sa * kOpBytes + rd_row;
+                    const char* Bs = lds + kBBase + sb * kOpBytes + rd_row;
 #pragma unroll
                     for (int hs = 0; hs < kSub; hs++) {
                         const int ks = q * kSub + hs;
@@ -349,55 +353,64 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 };
                 // every wave is done with LDS (previous segment, tile or epilogue)
                 __syncthreads();
-                static_assert(kStages == 2, "the waits below are written for a double buffer");
-                issue(0, 0);
+                // Issue order, per wave: B0 A0 B1 A1 B2, then after each step kt's
+                // barrier A(kt+2) B(kt+3).  When step kt+1 is needed, the only
+                // younger loads are B(kt+2)'s, so the wait is a constant
+                // kDmaPerOperand while the weights run two steps ahead.
+                issue_b(0, 0);
+                issue_a(0, 0);
                 if (nk > 1) {
-                    issue(1, 1);
-                    wait_vmcnt<kDmaPerStage>();      // step 0 landed, step 1 in flight
-                } else {
-                    wait_vmcnt<0>();
+                    issue_b(1, 1);
+                    issue_a(1, 1);
                 }
+                if (nk > 2) issue_b(2, 2);
+                if (nk > 2) wait_vmcnt<3 * kDmaPerOperand>();       // step 0 landed
+                else if (nk > 1) wait_vmcnt<2 * kDmaPerOperand>();
+                else wait_vmcnt<0>();
                 bare_barrier();
                 Frag f0a[kSub][NA], f0b[kSub][2], f1a[kSub][NA], f1b[kSub][2];
-                if (NACT > 0) load_sub(0, 0, f0a, f0b);
+                if (NACT > 0) load_sub(0, 0, 0, f0a, f0b);
 
                 // Software pipeline over the quarters of the K steps: each
                 // quarter's fragments are read while the MFMAs of the previous one
                 // run.  After the third quarter's reads the wave waits for step
                 // kt+1 to land and meets the others at the barrier; by then every
-                // read of step kt's buffer has completed, so the buffer is
-                // refilled with step kt+2 straight away.
-                int buf = 0;                  // buffer of step kt
+                // read of step kt's slots has completed, so they are refilled at
+                // once (A with step kt+2, B with step kt+3).
+                int sa = 0, sb = 0;           // slots of step kt
 #pragma unroll 1
                 for (int kt = 0; kt + 1 < nk; kt++) {
                     if (NACT > 0) {
-                        load_sub(buf, 1, f1a, f1b);
+                        load_sub(sa, sb, 1, f1a, f1b);
                         mma_sub(f0a, f0b);
                         order_sub();
-                        load_sub(buf, 2, f0a, f0b);
+                        load_sub(sa, sb, 2, f0a, f0b);
                         mma_sub(f1a, f1b);
                         order_sub();
-                        load_sub(buf, 3, f1a, f1b);
+                        load_sub(sa, sb, 3, f1a, f1b);
                         mma_sub(f0a, f0b);
                         order_sub();
                     }
-                    wait_vmcnt<0>();          // step kt+1 (the only one in flight) landed
+                    if (kt + 2 < nk) wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
+                    else wait_vmcnt<0>();
                     bare_barrier();
-                    if (kt + 2 < nk) issue(kt + 2, buf);
-                    buf ^= 1;
+                    if (kt + 2 < nk) issue_a(kt + 2, sa);
+                    if (kt + 3 < nk) issue_b(kt + 3, sb);
+                    sa ^= 1;
+                    sb = sb == kSlotsB - 1 ? 0 : sb + 1;
                     if (NACT > 0) {
-                        load_sub(buf, 0, f0a, f0b);
+                        load_sub(sa, sb, 0, f0a, f0b);
                         mma_sub(f1a, f1b);
                         order_sub();
                     }
                 }
                 // last step (its first quarter is already in registers)
                 if (NACT > 0) {
-                    load_sub(buf, 1, f1a, f1b);
+                    load_sub(sa, sb, 1, f1a, f1b);
                     mma_sub(f0a, f0b);
-                    load_sub(buf, 2, f0a, f0b);
+                    load_sub(sa, sb, 2, f0a, f0b);
                     mma_sub(f1a, f1b);
-                    load_sub(buf, 3, f1a, f1b);
+                    load_sub(sa, sb, 3, f1a, f1b);
                     mma_sub(f0a, f0b);
                     mma_sub(f1a, f1b);
                 }
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* offset
     if (tid == 0) tp[G] = total;
 }
 
-constexpr size_t kLdsBytes = (size_t)kStages * kStageBytes;   // 131,072 bytes
+constexpr size_t kLdsBytes = (size_t)(kSlotsA + kSlotsB) * kOpBytes;   // 163,840 bytes
 
 template <typename T, typename OutT, int EPI>
 hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
