@@ -306,11 +306,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                     for (int i = 0; i < kDmaPerOperand; i++)
                         dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
                 };
-                auto issue_b = [&](int kt, int slot) __attribute__((always_inline)) {
+                // B DMAs i0, i0+1, ... (n of them) of step kt
+                auto issue_b = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
                     const char* const Bk = B_t + (int64_t)kt * kRowBytes;
 #pragma unroll
                     for (int i = 0; i < kDmaPerOperand; i++)
-                        dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
+                        if (i >= i0 && i < i0 + n)
+                            dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
                 };
                 // Fragments of one quarter of a K step (kSub MFMA k-steps).
                 auto load_sub = [&](int sa, int sb, int q, Frag (&fa)[kSub][NA],
@@ -342,31 +344,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                                 acc[i][j] = Mfma<T>::mma(fa[hs][i], fb[hs][j], acc[i][j]);
                 };
                 // Instruction order within a quarter step: one MFMA, then the
-                // fragment reads of the next quarter, then the remaining MFMAs, so
-                // the reads have the whole quarter step to complete.
-                auto order_sub = [&]() __attribute__((always_inline)) {
+                // fragment reads of the next quarter, then the remaining MFMAs with
+                // NV DMA instructions interleaved, so the reads have the whole
+                // quarter step to complete and the DMA issue never holds up the
+                // matrix cores for long.
+                auto order_sub = [&](auto nv_c) __attribute__((always_inline)) {
+                    constexpr int NV = decltype(nv_c)::value;
                     constexpr int kReads = kSub * (NACT + 2);
                     constexpr int kMfmas = kSub * NACT * 2;
+                    constexpr int kPair = NV < kMfmas - 1 ? NV : kMfmas - 1;
                     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
                     __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 1, 0);
+#pragma unroll
+                    for (int v = 0; v < kPair; v++) {
+                        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    }
+                    if (NV > kPair) __builtin_amdgcn_sched_group_barrier(0x010, NV - kPair, 0);
+                    if (kMfmas - 1 - kPair > 0)
+                        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 1 - kPair, 0);
                 };
+                using V0 = std::integral_constant<int, 0>;
+                using V2 = std::integral_constant<int, 2>;
+                using VA = std::integral_constant<int, kDmaPerOperand>;
                 // every wave is done with LDS (previous segment, tile or epilogue)
                 __syncthreads();
-                // Issue order, per wave: B0 A0 B1 A1 B2, then after each step kt's
-                // barrier A(kt+2) B(kt+3).  When step kt+1 is needed, the only
-                // younger loads are B(kt+2)'s, so the wait is a constant
-                // kDmaPerOperand while the weights run two steps ahead.
-                issue_b(0, 0);
+                // Issue order, per wave: B0 A0 B1 A1, then during step kt's
+                // quarters 1-2 B(kt+2), and after step kt's barrier A(kt+2).  When
+                // step kt+1 is needed, the only younger loads are B(kt+2)'s, so the
+                // wait is a constant kDmaPerOperand while the weights run two steps
+                // ahead.  Past the last step, the same DMAs re-read the last step
+                // into slots nothing reads any more, which keeps the count fixed.
+                issue_b(0, 0, 0, kDmaPerOperand);
                 issue_a(0, 0);
                 if (nk > 1) {
-                    issue_b(1, 1);
+                    issue_b(1, 1, 0, kDmaPerOperand);
                     issue_a(1, 1);
+                    wait_vmcnt<2 * kDmaPerOperand>();       // step 0 landed
+                } else {
+                    wait_vmcnt<0>();
                 }
-                if (nk > 2) issue_b(2, 2);
-                if (nk > 2) wait_vmcnt<3 * kDmaPerOperand>();       // step 0 landed
-                else if (nk > 1) wait_vmcnt<2 * kDmaPerOperand>();
-                else wait_vmcnt<0>();
                 bare_barrier();
                 Frag f0a[kSub][NA], f0b[kSub][2], f1a[kSub][NA], f1b[kSub][2];
                 if (NACT > 0) load_sub(0, 0, 0, f0a, f0b);
@@ -375,34 +392,43 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 // quarter's fragments are read while the MFMAs of the previous one
                 // run.  After the third quarter's reads the wave waits for step
                 // kt+1 to land and meets the others at the barrier; by then every
-                // read of step kt's slots has completed, so they are refilled at
-                // once (A with step kt+2, B with step kt+3).
+                // read of step kt's slots has completed, so A's is refilled at once
+                // with step kt+2 and B's during the next step with step kt+3.
                 int sa = 0, sb = 0;           // slots of step kt
 #pragma unroll 1
                 for (int kt = 0; kt + 1 < nk; kt++) {
+                    const int kb2 = min(kt + 2, nk - 1);            // B step issued now
+                    const int sb2 = sb == 0 ? kSlotsB - 1 : sb - 1;  // its slot, (kt + 2) % 3
                     if (NACT > 0) {
                         load_sub(sa, sb, 1, f1a, f1b);
                         mma_sub(f0a, f0b);
-                        order_sub();
+                        issue_b(kb2, sb2, 0, kDmaPerOperand / 2);
+                        order_sub(V2{});
                         load_sub(sa, sb, 2, f0a, f0b);
                         mma_sub(f1a, f1b);
-                        order_sub();
+                        issue_b(kb2, sb2, kDmaPerOperand / 2, kDmaPerOperand / 2);
+                        order_sub(V2{});
                         load_sub(sa, sb, 3, f1a, f1b);
                         mma_sub(f0a, f0b);
-                        order_sub();
+                        order_sub(V0{});
+                    } else {
+                        issue_b(kb2, sb2, 0, kDmaPerOperand);
                     }
-                    if (kt + 2 < nk) wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
-                    else wait_vmcnt<0>();
+                    // keep this step's MFMAs ahead of the wait, so they run while
+                    // the wave waits at the barrier
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
                     bare_barrier();
-                    if (kt + 2 < nk) issue_a(kt + 2, sa);
-                    if (kt + 3 < nk) issue_b(kt + 3, sb);
-                    sa ^= 1;
                     sb = sb == kSlotsB - 1 ? 0 : sb + 1;
                     if (NACT > 0) {
-                        load_sub(sa, sb, 0, f0a, f0b);
+                        load_sub(sa ^ 1, sb, 0, f0a, f0b);
                         mma_sub(f1a, f1b);
-                        order_sub();
+                        issue_a(min(kt + 2, nk - 1), sa);
+                        order_sub(VA{});
+                    } else {
+                        issue_a(min(kt + 2, nk - 1), sa);
                     }
+                    sa ^= 1;
                 }
                 // last step (its first quarter is already in registers)
                 if (NACT > 0) {
