@@ -35,8 +35,8 @@
 // specialised on how many of them are active, so each case is straight-line
 // MFMA code.  For the SwiGLU epilogue a wave's two column blocks are the gate
 // and the up rows of the same 32 hidden columns, so the activation is formed on
-// the way out and neither G nor U is ever stored.  Results leave through LDS in
-// 16-byte row chunks.
+// the way out and neither G nor U is ever stored.  Results leave through a
+// per-wave LDS piece in 16-byte row chunks, with no block-wide barrier.
 //
 // Scheduling: a persistent grid (a multiple of 8 workgroups).  Workgroups are
 // dealt to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; each XCD
@@ -66,7 +66,6 @@ constexpr int kSlotsA = 2;        // LDS ring of A steps
 constexpr int kSlotsB = 3;        // LDS ring of B steps (the streamed weights run further ahead)
 constexpr int kBBase = kSlotsA * kOpBytes;             // B ring offset in LDS
 constexpr int kDmaPerOperand = kBM * kRowBytes / 1024 / kWaves;   // 1-KB DMAs per wave
-constexpr int kStageLd = 68;      // epilogue staging row stride (floats)
 
 static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
 
@@ -161,8 +160,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int fl = swz(lane & 31);
     const int rd_row = (lane & 31) * kRowBytes;
 
-    for (int64_t t = lo + slot; t < hi; t += nslots) {
-        // ---- tile coordinates (grouped swizzle along m)
+    // ---- a tile: its rows, columns and expert
+    struct Tile {
+        int64_t row0, rows_valid, n0;
+        int g, nrb;
+    };
+    auto tile_at = [&](int64_t t) __attribute__((always_inline)) {
+        // grouped swizzle along m
         const int64_t gsz = (int64_t)p.group_m * n_tiles_n;
         const int64_t super = t / gsz;
         const int64_t within = t - super * gsz;
@@ -170,309 +174,348 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         const int64_t gm = min((int64_t)p.group_m, n_tiles_m - m_first);
         const int64_t tm = m_first + within % gm;
         const int64_t tn = within / gm;
-
-        int g = 0;
-        int64_t row0, rows_valid;
+        Tile tl;
+        tl.g = 0;
         if (p.offsets) {
-            g = find_group(p.tile_prefix, p.G, (int)tm);
-            const int64_t mloc = tm - p.tile_prefix[g];
-            row0 = p.offsets[g] + mloc * kBM;
-            rows_valid = min((int64_t)kBM, (int64_t)p.offsets[g + 1] - row0);
+            tl.g = find_group(p.tile_prefix, p.G, (int)tm);
+            const int64_t mloc = tm - p.tile_prefix[tl.g];
+            tl.row0 = p.offsets[tl.g] + mloc * kBM;
+            tl.rows_valid = min((int64_t)kBM, (int64_t)p.offsets[tl.g + 1] - tl.row0);
         } else {
-            row0 = tm * kBM;
-            rows_valid = min((int64_t)kBM, p.M - row0);
+            tl.row0 = tm * kBM;
+            tl.rows_valid = min((int64_t)kBM, p.M - tl.row0);
         }
-        const int nrb = (int)((rows_valid + 31) >> 5);      // active 32-row blocks
-        const int n_act = (nrb - wm + 1) >> 1;              // this wave's active blocks
-        const int64_t n0 = tn * kColsOut;
+        tl.nrb = (int)((tl.rows_valid + 31) >> 5);       // active 32-row blocks
+        tl.n0 = tn * kColsOut;
+        return tl;
+    };
 
-        // ---- DMA sources.  Wave w fills LDS rows 32 w + 8 i + lane / 8
-        // (i < 4) of each operand, chunk lane % 8, which holds logical chunk
-        // (lane % 8) ^ swz(row).  Each source is a wave-uniform base (A's tile
-        // or gather base, B's group) plus a 32-bit per-lane byte offset; the
-        // host checks that every offset fits.
-        constexpr int kLanesPerRow = kRowBytes / 16;
-        const int lrow = wave * ((64 / kLanesPerRow) * kDmaPerOperand) + lane / kLanesPerRow;
-        int32_t a_src[kDmaPerOperand], b_src[kDmaPerOperand];
-        int chunk[kDmaPerOperand];
+    // ---- DMA sources.  Wave w fills LDS rows 32 w + 8 i + lane / 8 (i < 4)
+    // of each operand, chunk lane % 8, which holds logical chunk (lane % 8) ^
+    // swz(row).  Each source is a wave-uniform base (A's tile or gather base,
+    // B's group) plus a 32-bit per-lane byte offset; the host checks that every
+    // offset fits.
+    constexpr int kLanesPerRow = kRowBytes / 16;
+    const int lrow = wave * ((64 / kLanesPerRow) * kDmaPerOperand) + lane / kLanesPerRow;
+    int chunk[kDmaPerOperand];
+#pragma unroll
+    for (int i = 0; i < kDmaPerOperand; i++)
+        chunk[i] = ((lane % kLanesPerRow) ^ swz((lrow + (64 / kLanesPerRow) * i) & 31)) * 16;
+    int32_t a_src[kDmaPerOperand], b_src[kDmaPerOperand];
+    auto set_sources = [&](const Tile& tl) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++) {
             const int r = lrow + (64 / kLanesPerRow) * i;
-            chunk[i] = ((lane % kLanesPerRow) ^ swz(r & 31)) * 16;
             // rows past the group's end read the tile's first row; their
             // results are never stored
-            const int rl = r < rows_valid ? r : 0;
+            const int rl = r < tl.rows_valid ? r : 0;
             // gathered: the source row itself; else the row within the tile
-            a_src[i] = p.a_rows ? p.a_rows[row0 + rl] / p.a_div : rl;
+            a_src[i] = p.a_rows ? p.a_rows[tl.row0 + rl] / p.a_div : rl;
             int64_t col, brow;
             if (EPI == EPI_SWIGLU) {
                 // each 64-row slice of B: [gate 32 | up 32] of 32 hidden columns
                 const int up = (r >> 5) & 1;
-                col = n0 + (r >> 6) * 32 + (r & 31);
+                col = tl.n0 + (r >> 6) * 32 + (r & 31);
                 const int64_t zi = col / p.n_per, cc = col - zi * p.n_per;
                 brow = zi * 2 * p.n_per + cc + up * p.n_per;
             } else {
-                col = n0 + r;
+                col = tl.n0 + r;
                 brow = col;
             }
             b_src[i] = (int32_t)(col < p.N ? brow : 0);     // row within the group
         }
-        const int64_t a_row_base = p.a_rows ? 0 : row0;
-        const int64_t b_row_base = (int64_t)g * p.b_group_rows;
-        char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
-        char* const b_lds = lds + kBBase + (wave * kDmaPerOperand) * 1024;
-
-        // One wave's staged 32 x W block (W = 32 hidden columns for SwiGLU, else
-        // 64 columns) leaves in 16-byte chunks of output elements.
-        auto store_block = [&](const float* stage, int rbase) __attribute__((always_inline)) {
-            OutT* C = (OutT*)p.C;
-            constexpr int W = (EPI == EPI_SWIGLU) ? 32 : 64;
-            constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
-            constexpr int kChunksPerRow = W / kVec;
-            const int64_t cbase = n0 + wn * W;
+    };
+    // one K segment's bases and offsets for a tile
+    const char* A_t = nullptr;
+    const char* B_t = nullptr;
+    int nk = 0;
+    uint32_t a_off[kDmaPerOperand], b_off[kDmaPerOperand];
+    auto set_segment = [&](const Tile& tl, int sidx) __attribute__((always_inline)) {
+        // The kernel's only argument is p, laid out at the start of the
+        // kernel-argument segment; reading the selected segment from there keeps
+        // it in scalar loads (indexing p.seg directly would copy the argument to
+        // private memory).
+        const GemmSeg* segs = (const GemmSeg*)(
+            (const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(GemmParams, seg));
+        const char* A = (const char*)uniform64((int64_t)segs[sidx].A);
+        const char* B = (const char*)uniform64((int64_t)segs[sidx].B);
+        const int64_t lda = uniform64(segs[sidx].lda);
+        const int64_t ldb = uniform64(segs[sidx].ldb);
+        const int K = __builtin_amdgcn_readfirstlane(segs[sidx].K);
+        nk = __builtin_amdgcn_readfirstlane(K * kElem / kRowBytes);
+        const int64_t a_row_base = p.a_rows ? 0 : tl.row0;
+        const int64_t b_row_base = (int64_t)tl.g * p.b_group_rows;
+        A_t = (const char*)uniform64((int64_t)(A + a_row_base * lda * kElem));
+        B_t = (const char*)uniform64((int64_t)(B + b_row_base * ldb * kElem));
 #pragma unroll
-            for (int q = lane; q < 32 * kChunksPerRow; q += 64) {
-                const int r = q / kChunksPerRow;
-                const int cc = (q % kChunksPerRow) * kVec;
+        for (int i = 0; i < kDmaPerOperand; i++) {
+            a_off[i] = (uint32_t)((int64_t)a_src[i] * lda * kElem) + chunk[i];
+            b_off[i] = (uint32_t)((int64_t)b_src[i] * ldb * kElem) + chunk[i];
+        }
+    };
+    char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
+    char* const b_lds = lds + kBBase + (wave * kDmaPerOperand) * 1024;
+    auto issue_a = [&](int kt, int slot) __attribute__((always_inline)) {
+        const char* const Ak = A_t + (int64_t)kt * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kDmaPerOperand; i++)
+            dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
+    };
+    // B DMAs i0, i0+1, ... (n of them) of step kt
+    auto issue_b = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
+        const char* const Bk = B_t + (int64_t)kt * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kDmaPerOperand; i++)
+            if (i >= i0 && i < i0 + n) dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
+    };
+    // Issue order, per wave: B0 A0 B1 A1 (this prologue), then during step kt's
+    // quarters 1-2 B(kt+2), and after step kt's barrier A(kt+2).  When step kt+1
+    // is needed, the only younger loads are B(kt+2)'s, so the wait is a constant
+    // kDmaPerOperand while the weights run two steps ahead.  Past the last step,
+    // the same DMAs re-read the last step into slots nothing reads any more,
+    // which keeps the count fixed.
+    auto prologue = [&]() __attribute__((always_inline)) {
+        issue_b(0, 0, 0, kDmaPerOperand);
+        issue_a(0, 0);
+        if (nk > 1) {
+            issue_b(1, 1, 0, kDmaPerOperand);
+            issue_a(1, 1);
+        }
+    };
+
+    // Epilogue staging: each wave owns a 4 KB piece of the third B slot, which
+    // the next tile's first loads (slots A0, A1, B0, B1) leave alone.
+    float* const stage = (float*)(lds + kBBase + 2 * kOpBytes + wave * 4096);
+    static_assert(kSlotsB == 3 && kWaves * 4096 == kOpBytes, "staging layout");
+
+    int64_t t = lo + slot;
+    if (t >= hi) return;
+    Tile cur = tile_at(t);
+    set_sources(cur);
+    set_segment(cur, 0);
+    __syncthreads();
+    prologue();
+
+    // The rest of a tile is specialised on the number of active row blocks of
+    // this wave: each case is straight-line MFMA code with its own accumulator
+    // set.  It ends by issuing the next tile's first loads and reports whether
+    // there is a next tile.  (Issuing them before the epilogue measured slower.)
+    auto tile_body = [&](auto nact_c) __attribute__((always_inline)) -> bool {
+        constexpr int NACT = decltype(nact_c)::value;
+        constexpr int NA = NACT > 0 ? NACT : 1;
+        typedef typename Mfma<T>::frag Frag;
+        floatx16 acc[NA][2];
+#pragma unroll
+        for (int i = 0; i < NACT; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
+
+        // Fragments of one quarter of a K step (kSub MFMA k-steps).
+        auto load_sub = [&](int sa, int sb, int q, Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
+            __attribute__((always_inline)) {
+            const char* As = lds + sa * kOpBytes + rd_row;
+            const char* Bs = lds + kBBase + sb * kOpBytes + rd_row;
+#pragma unroll
+            for (int hs = 0; hs < kSub; hs++) {
+                const int ks = q * kSub + hs;
+                const int kb = ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
+                const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
+#pragma unroll
+                for (int i = 0; i < NACT; i++)
+                    fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+            }
+        };
+        auto mma_sub = [&](Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
+            __attribute__((always_inline)) {
+#pragma unroll
+            for (int hs = 0; hs < kSub; hs++)
+#pragma unroll
+                for (int i = 0; i < NACT; i++)
+#pragma unroll
+                    for (int j = 0; j < 2; j++)
+                        acc[i][j] = Mfma<T>::mma(fa[hs][i], fb[hs][j], acc[i][j]);
+        };
+        // Instruction order within a quarter step: one MFMA, then the fragment
+        // reads of the next quarter, then the remaining MFMAs with NV DMA
+        // instructions interleaved, so the reads have the whole quarter step to
+        // complete and the DMA issue never holds up the matrix cores for long.
+        auto order_sub = [&](auto nv_c) __attribute__((always_inline)) {
+            constexpr int NV = decltype(nv_c)::value;
+            constexpr int kReads = kSub * (NACT + 2);
+            constexpr int kMfmas = kSub * NACT * 2;
+            constexpr int kPair = NV < kMfmas - 1 ? NV : kMfmas - 1;
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
+#pragma unroll
+            for (int v = 0; v < kPair; v++) {
+                __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            }
+            if (NV > kPair) __builtin_amdgcn_sched_group_barrier(0x010, NV - kPair, 0);
+            if (kMfmas - 1 - kPair > 0)
+                __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 1 - kPair, 0);
+        };
+        using V0 = std::integral_constant<int, 0>;
+        using V2 = std::integral_constant<int, 2>;
+        using VA = std::integral_constant<int, kDmaPerOperand>;
+
+        // K segments run one after the other, each with its own pipeline fill
+        // (the first one's loads are already in flight).
+#pragma unroll 1
+        for (int sidx = 0; sidx < p.nseg; sidx++) {
+            if (sidx > 0) {
+                __syncthreads();          // every wave is done with the slots
+                set_segment(cur, sidx);
+                prologue();
+            }
+            // step 0 landed once at most step 1's loads are outstanding (the
+            // previous tile's stores are older still)
+            if (nk > 1) wait_vmcnt<2 * kDmaPerOperand>();
+            else wait_vmcnt<0>();
+            bare_barrier();
+            Frag f0a[kSub][NA], f0b[kSub][2], f1a[kSub][NA], f1b[kSub][2];
+            if (NACT > 0) load_sub(0, 0, 0, f0a, f0b);
+
+            // Software pipeline over the quarters of the K steps: each quarter's
+            // fragments are read while the MFMAs of the previous one run.  After
+            // the third quarter's reads the wave waits for step kt+1 to land and
+            // meets the others at the barrier; by then every read of step kt's
+            // slots has completed, so A's is refilled at once with step kt+2 and
+            // B's during the next step with step kt+3.
+            int sa = 0, sb = 0;           // slots of step kt
+#pragma unroll 1
+            for (int kt = 0; kt + 1 < nk; kt++) {
+                const int kb2 = min(kt + 2, nk - 1);            // B step issued now
+                const int sb2 = sb == 0 ? kSlotsB - 1 : sb - 1;  // its slot, (kt + 2) % 3
+                if (NACT > 0) {
+                    load_sub(sa, sb, 1, f1a, f1b);
+                    mma_sub(f0a, f0b);
+                    issue_b(kb2, sb2, 0, kDmaPerOperand / 2);
+                    order_sub(V2{});
+                    load_sub(sa, sb, 2, f0a, f0b);
+                    mma_sub(f1a, f1b);
+                    issue_b(kb2, sb2, kDmaPerOperand / 2, kDmaPerOperand / 2);
+                    order_sub(V2{});
+                    load_sub(sa, sb, 3, f1a, f1b);
+                    mma_sub(f0a, f0b);
+                    order_sub(V0{});
+                } else {
+                    issue_b(kb2, sb2, 0, kDmaPerOperand);
+                }
+                // keep this step's MFMAs ahead of the wait, so they run while the
+                // wave waits at the barrier
+                __builtin_amdgcn_sched_barrier(0);
+                wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
+                bare_barrier();
+                sb = sb == kSlotsB - 1 ? 0 : sb + 1;
+                if (NACT > 0) {
+                    load_sub(sa ^ 1, sb, 0, f0a, f0b);
+                    mma_sub(f1a, f1b);
+                    issue_a(min(kt + 2, nk - 1), sa);
+                    order_sub(VA{});
+                } else {
+                    issue_a(min(kt + 2, nk - 1), sa);
+                }
+                sa ^= 1;
+            }
+            // last step (its first quarter is already in registers)
+            if (NACT > 0) {
+                load_sub(sa, sb, 1, f1a, f1b);
+                mma_sub(f0a, f0b);
+                load_sub(sa, sb, 2, f0a, f0b);
+                mma_sub(f1a, f1b);
+                load_sub(sa, sb, 3, f1a, f1b);
+                mma_sub(f0a, f0b);
+                mma_sub(f1a, f1b);
+            }
+        }
+        // every wave is done reading the slots and every DMA has landed
+        __syncthreads();
+
+        const Tile done = cur;
+        const bool more = t + nslots < hi;
+
+        // ---- epilogue.  Each 32-row block of the wave is staged through its
+        // own LDS piece (no block-wide barrier: only the wave reads what it
+        // wrote) so that every global store is a 16-byte chunk of a row.  For
+        // SwiGLU a wave's two column blocks are the gate and the up rows of the
+        // same hidden columns, so h = silu(G) * U is formed in registers first.
+        OutT* const C = (OutT*)p.C;
+        constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
+        // write back R staged rows of W columns starting at tile row rbase
+        auto store_rows = [&](auto r_c, auto w_c, int rbase, int64_t cbase)
+            __attribute__((always_inline)) {
+            constexpr int R = decltype(r_c)::value, W = decltype(w_c)::value;
+            constexpr int kChunks = W / kVec;
+#pragma unroll
+            for (int q = lane; q < R * kChunks; q += 64) {
+                const int r = q / kChunks;
+                const int cc = (q % kChunks) * kVec;
                 const int64_t grow = rbase + r;
                 const int64_t col = cbase + cc;
-                if (grow < rows_valid && col < p.N) {
+                if (grow < done.rows_valid && col < p.N) {
                     float vals[kVec];
-                    const float* srow = stage + r * kStageLd;
-                    if (EPI == EPI_SWIGLU) {
-                        // hidden column c of the wave: gate at c, up at 32 + c
 #pragma unroll
-                        for (int e = 0; e < kVec; e++)
-                            vals[e] = silu_f(srow[cc + e]) * srow[32 + cc + e];
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < kVec; e++) vals[e] = srow[cc + e];
-                    }
-                    const int64_t off = (row0 + grow) * p.ldc + col;
+                    for (int e = 0; e < kVec; e++) vals[e] = stage[r * W + cc + e];
                     if (EPI == EPI_ADD) {
-                        const int64_t aoff = (row0 + grow) * p.ld_add + col;
+                        const int64_t aoff = (done.row0 + grow) * p.ld_add + col;
 #pragma unroll
                         for (int e = 0; e < kVec; e++)
                             vals[e] += Elem<OutT>::load((const OutT*)p.addend, aoff + e);
                     }
-                    store_vec<OutT, kVec>(C, off, vals);
+                    store_vec<OutT, kVec>(C, (done.row0 + grow) * p.ldc + col, vals);
                 }
             }
         };
-
-        // The rest of the tile is specialised on the number of active row
-        // blocks of this wave: each case is straight-line MFMA code with its
-        // own accumulator set.
-        auto tile_body = [&](auto nact_c) __attribute__((always_inline)) {
-            constexpr int NACT = decltype(nact_c)::value;
-            constexpr int NA = NACT > 0 ? NACT : 1;
-            typedef typename Mfma<T>::frag Frag;
-            floatx16 acc[NA][2];
+        using I16 = std::integral_constant<int, 16>;
+        using I32 = std::integral_constant<int, 32>;
+        using I64 = std::integral_constant<int, 64>;
 #pragma unroll
-            for (int i = 0; i < NACT; i++)
+        for (int i = 0; i < NACT; i++) {
+            const int rbase = (wm + 2 * i) * 32;
+            if (EPI == EPI_SWIGLU) {
 #pragma unroll
-                for (int j = 0; j < 2; j++)
+                for (int v = 0; v < 16; v++)
+                    stage[acc_row(v, lane) * 32 + (lane & 31)] =
+                        silu_f(acc[i][0][v]) * acc[i][1][v];
+                store_rows(I32{}, I32{}, rbase, done.n0 + wn * 32);
+            } else {
+                // two halves of 16 rows: registers v < 8 hold rows 0-15
 #pragma unroll
-                    for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
-
-            // K segments run one after the other, each with its own pipeline fill.
-#pragma unroll 1
-            for (int sidx = 0; sidx < p.nseg; sidx++) {
-                // The kernel's only argument is p, laid out at the start of the
-                // kernel-argument segment; reading the selected segment from there
-                // keeps it in scalar loads (indexing p.seg directly would copy
-                // the argument to private memory).
-                const GemmSeg* segs = (const GemmSeg*)(
-                    (const char*)__builtin_amdgcn_kernarg_segment_ptr() + offsetof(GemmParams, seg));
-                const char* A = (const char*)uniform64((int64_t)segs[sidx].A);
-                const char* B = (const char*)uniform64((int64_t)segs[sidx].B);
-                const int64_t lda = uniform64(segs[sidx].lda);
-                const int64_t ldb = uniform64(segs[sidx].ldb);
-                const int K = __builtin_amdgcn_readfirstlane(segs[sidx].K);
-                const int nk = __builtin_amdgcn_readfirstlane(K * kElem / kRowBytes);
-                const char* const A_t = (const char*)uniform64(
-                    (int64_t)(A + a_row_base * lda * kElem));
-                const char* const B_t = (const char*)uniform64(
-                    (int64_t)(B + b_row_base * ldb * kElem));
-                uint32_t a_off[kDmaPerOperand], b_off[kDmaPerOperand];
+                for (int h = 0; h < 2; h++) {
 #pragma unroll
-                for (int i = 0; i < kDmaPerOperand; i++) {
-                    a_off[i] = (uint32_t)((int64_t)a_src[i] * lda * kElem) + chunk[i];
-                    b_off[i] = (uint32_t)((int64_t)b_src[i] * ldb * kElem) + chunk[i];
-                }
-                auto issue_a = [&](int kt, int slot) __attribute__((always_inline)) {
-                    const char* const Ak = A_t + (int64_t)kt * kRowBytes;
+                    for (int j = 0; j < 2; j++)
 #pragma unroll
-                    for (int i = 0; i < kDmaPerOperand; i++)
-                        dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
-                };
-                // B DMAs i0, i0+1, ... (n of them) of step kt
-                auto issue_b = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
-                    const char* const Bk = B_t + (int64_t)kt * kRowBytes;
-#pragma unroll
-                    for (int i = 0; i < kDmaPerOperand; i++)
-                        if (i >= i0 && i < i0 + n)
-                            dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
-                };
-                // Fragments of one quarter of a K step (kSub MFMA k-steps).
-                auto load_sub = [&](int sa, int sb, int q, Frag (&fa)[kSub][NA],
-                                    Frag (&fb)[kSub][2]) __attribute__((always_inline)) {
-                    const char* As = lds + sa * kOpBytes + rd_row;
-                    const char* Bs = lds + kBBase + sb * kOpBytes + rd_row;
-#pragma unroll
-                    for (int hs = 0; hs < kSub; hs++) {
-                        const int ks = q * kSub + hs;
-                        const int kb =
-                            ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
-                        const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
-#pragma unroll
-                        for (int j = 0; j < 2; j++)
-                            fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
-#pragma unroll
-                        for (int i = 0; i < NACT; i++)
-                            fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
-                    }
-                };
-                auto mma_sub = [&](Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
-                    __attribute__((always_inline)) {
-#pragma unroll
-                    for (int hs = 0; hs < kSub; hs++)
-#pragma unroll
-                        for (int i = 0; i < NACT; i++)
-#pragma unroll
-                            for (int j = 0; j < 2; j++)
-                                acc[i][j] = Mfma<T>::mma(fa[hs][i], fb[hs][j], acc[i][j]);
-                };
-                // Instruction order within a quarter step: one MFMA, then the
-                // fragment reads of the next quarter, then the remaining MFMAs with
-                // NV DMA instructions interleaved, so the reads have the whole
-                // quarter step to complete and the DMA issue never holds up the
-                // matrix cores for long.
-                auto order_sub = [&](auto nv_c) __attribute__((always_inline)) {
-                    constexpr int NV = decltype(nv_c)::value;
-                    constexpr int kReads = kSub * (NACT + 2);
-                    constexpr int kMfmas = kSub * NACT * 2;
-                    constexpr int kPair = NV < kMfmas - 1 ? NV : kMfmas - 1;
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
-#pragma unroll
-                    for (int v = 0; v < kPair; v++) {
-                        __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    }
-                    if (NV > kPair) __builtin_amdgcn_sched_group_barrier(0x010, NV - kPair, 0);
-                    if (kMfmas - 1 - kPair > 0)
-                        __builtin_amdgcn_sched_group_barrier(0x008, kMfmas - 1 - kPair, 0);
-                };
-                using V0 = std::integral_constant<int, 0>;
-                using V2 = std::integral_constant<int, 2>;
-                using VA = std::integral_constant<int, kDmaPerOperand>;
-                // every wave is done with LDS (previous segment, tile or epilogue)
-                __syncthreads();
-                // Issue order, per wave: B0 A0 B1 A1, then during step kt's
-                // quarters 1-2 B(kt+2), and after step kt's barrier A(kt+2).  When
-                // step kt+1 is needed, the only younger loads are B(kt+2)'s, so the
-                // wait is a constant kDmaPerOperand while the weights run two steps
-                // ahead.  Past the last step, the same DMAs re-read the last step
-                // into slots nothing reads any more, which keeps the count fixed.
-                issue_b(0, 0, 0, kDmaPerOperand);
-                issue_a(0, 0);
-                if (nk > 1) {
-                    issue_b(1, 1, 0, kDmaPerOperand);
-                    issue_a(1, 1);
-                    wait_vmcnt<2 * kDmaPerOperand>();       // step 0 landed
-                } else {
-                    wait_vmcnt<0>();
-                }
-                bare_barrier();
-                Frag f0a[kSub][NA], f0b[kSub][2], f1a[kSub][NA], f1b[kSub][2];
-                if (NACT > 0) load_sub(0, 0, 0, f0a, f0b);
-
-                // Software pipeline over the quarters of the K steps: each
-                // quarter's fragments are read while the MFMAs of the previous one
-                // run.  After the third quarter's reads the wave waits for step
-                // kt+1 to land and meets the others at the barrier; by then every
-                // read of step kt's slots has completed, so A's is refilled at once
-                // with step kt+2 and B's during the next step with step kt+3.
-                int sa = 0, sb = 0;           // slots of step kt
-#pragma unroll 1
-                for (int kt = 0; kt + 1 < nk; kt++) {
-                    const int kb2 = min(kt + 2, nk - 1);            // B step issued now
-                    const int sb2 = sb == 0 ? kSlotsB - 1 : sb - 1;  // its slot, (kt + 2) % 3
-                    if (NACT > 0) {
-                        load_sub(sa, sb, 1, f1a, f1b);
-                        mma_sub(f0a, f0b);
-                        issue_b(kb2, sb2, 0, kDmaPerOperand / 2);
-                        order_sub(V2{});
-                        load_sub(sa, sb, 2, f0a, f0b);
-                        mma_sub(f1a, f1b);
-                        issue_b(kb2, sb2, kDmaPerOperand / 2, kDmaPerOperand / 2);
-                        order_sub(V2{});
-                        load_sub(sa, sb, 3, f1a, f1b);
-                        mma_sub(f0a, f0b);
-                        order_sub(V0{});
-                    } else {
-                        issue_b(kb2, sb2, 0, kDmaPerOperand);
-                    }
-                    // keep this step's MFMAs ahead of the wait, so they run while
-                    // the wave waits at the barrier
-                    __builtin_amdgcn_sched_barrier(0);
-                    wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
-                    bare_barrier();
-                    sb = sb == kSlotsB - 1 ? 0 : sb + 1;
-                    if (NACT > 0) {
-                        load_sub(sa ^ 1, sb, 0, f0a, f0b);
-                        mma_sub(f1a, f1b);
-                        issue_a(min(kt + 2, nk - 1), sa);
-                        order_sub(VA{});
-                    } else {
-                        issue_a(min(kt + 2, nk - 1), sa);
-                    }
-                    sa ^= 1;
-                }
-                // last step (its first quarter is already in registers)
-                if (NACT > 0) {
-                    load_sub(sa, sb, 1, f1a, f1b);
-                    mma_sub(f0a, f0b);
-                    load_sub(sa, sb, 2, f0a, f0b);
-                    mma_sub(f1a, f1b);
-                    load_sub(sa, sb, 3, f1a, f1b);
-                    mma_sub(f0a, f0b);
-                    mma_sub(f1a, f1b);
+                        for (int v = 0; v < 8; v++)
+                            stage[(acc_row(v, lane)) * 64 + j * 32 + (lane & 31)] =
+                                acc[i][j][v + 8 * h];
+                    store_rows(I16{}, I64{}, rbase + 16 * h, done.n0 + wn * 64);
                 }
             }
-            __syncthreads();      // LDS is reused for the epilogue
+        }
+        if (more) {
+            t += nslots;
+            cur = tile_at(t);
+            set_sources(cur);
+            set_segment(cur, 0);
+            prologue();
+        }
+        return more;
+    };
 
-            // ---- epilogue, staged through LDS so that every global store is a
-            // 16-byte chunk of a row; the activation and the conversion run on
-            // the read-back side.  All waves walk the same steps (the barriers
-            // are block-wide); a wave with no active row block idles.
-            float* stage = (float*)lds + wave * (32 * kStageLd);
-            const int nsteps = (nrb + 1) >> 1;       // active blocks of wave row 0
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (i < nsteps) {         // block-uniform: the barriers stay uniform
-                    const int rbase = (wm + 2 * i) * 32;
-                    if (i < NACT) {
-#pragma unroll
-                        for (int j = 0; j < 2; j++)
-#pragma unroll
-                            for (int v = 0; v < 16; v++)
-                                stage[acc_row(v, lane) * kStageLd + j * 32 + (lane & 31)] =
-                                    acc[i < NACT ? i : 0][j][v];
-                    }
-                    __syncthreads();
-                    if (i < NACT) store_block(stage, rbase);
-                    __syncthreads();
-                }
-            }
-        };
-        switch (n_act) {
-            case 4: tile_body(std::integral_constant<int, 4>{}); break;
-            case 3: tile_body(std::integral_constant<int, 3>{}); break;
-            case 2: tile_body(std::integral_constant<int, 2>{}); break;
-            case 1: tile_body(std::integral_constant<int, 1>{}); break;
-            default: tile_body(std::integral_constant<int, 0>{}); break;
+    bool more = true;
+    while (more) {
+        switch ((cur.nrb - wm + 1) >> 1) {       // this wave's active blocks
+            case 4: more = tile_body(std::integral_constant<int, 4>{}); break;
+            case 3: more = tile_body(std::integral_constant<int, 3>{}); break;
+            case 2: more = tile_body(std::integral_constant<int, 2>{}); break;
+            case 1: more = tile_body(std::integral_constant<int, 1>{}); break;
+            default: more = tile_body(std::integral_constant<int, 0>{}); break;
         }
     }
 }
@@ -495,7 +538,6 @@ constexpr size_t kLdsBytes = (size_t)(kSlotsA + kSlotsB) * kOpBytes;   // 163,84
 
 template <typename T, typename OutT, int EPI>
 hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
-    static_assert(kWaves * 32 * kStageLd * 4 <= kLdsBytes, "epilogue staging fits in LDS");
     // opting in to more than 64 KB of dynamic LDS is idempotent and cheap
     hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
