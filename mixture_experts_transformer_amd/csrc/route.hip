@@ -4,19 +4,22 @@
 // Each workgroup owns 32 tokens and every expert.  With r = h * inv_rms * g the
 // logits are l = inv_rms * ((h * g) W_r^T) + b, so the row scale is applied once
 // to the accumulators and the K loop reads h as stored:
-//   1. inverse RMS of the 32 rows (one wave per 8 rows, float32 sums);
+//   1. inverse RMS of the 32 rows (one wave per 4 rows, float32 sums); the same
+//      pass writes the normalised rows r (the experts' input) when asked, from
+//      the row values it holds in registers;
 //   2. the logits GEMM on v_mfma_f32_32x32x2_f32.  h and W_r stream into a ring
-//      of four LDS stages with global_load_lds_dwordx4 (16 values of K per
-//      stage), as in the grouped GEMM.  Within a stage, lane half q of an MFMA
-//      takes K values 8q..8q+7 in turn (any fixed assignment of K to MFMA steps
-//      gives the same sum), so each lane fetches its values of a row with
-//      16-byte (8-byte) reads of a chunk-swizzled row; g multiplies the h
-//      operand.  Eight waves, two per SIMD: waves 0-3 take the first four MFMA
-//      steps of every stage and waves 4-7 the last four, each for a quarter of
-//      the expert columns; the two partial sums are added in a fixed order at
-//      the end.  While a stage sits in LDS, the workgroup also writes that slice
-//      of the normalised rows r (the experts' input) when asked;
-//   3. logits (scaled, plus bias) go to LDS; each wave picks the top-k of 8
+//      of LDS stages with global_load_lds_dwordx4, 32 values of K per stage so
+//      that a float32 row piece is a whole 128-byte cache line.  Within a
+//      stage, lane half q of an MFMA takes K values 16q..16q+15 in turn (any
+//      fixed assignment of K to MFMA steps gives the same sum), so each lane
+//      fetches its values of a row with 16-byte reads of a chunk-swizzled row;
+//      g multiplies the h operand (scalar loads).  Eight waves, two per SIMD:
+//      waves 0-3 take the first eight MFMA steps of every stage and waves 4-7
+//      the last eight, each for a quarter of the expert columns; the two
+//      partial sums are added in a fixed order at the end.  The K loop issues
+//      no vector memory access besides the DMAs, so each wait only covers the
+//      stage it needs;
+//   3. logits (scaled, plus bias) go to LDS; each wave picks the top-k of 4
 //      tokens with wavefront argmax reductions over packed (value, id) keys and
 //      forms the weights exp(l_j - l_max) / sum_sel exp(l_i - l_max), which equal
 //      softmax over all experts renormalised over the selected ones.
@@ -35,8 +38,7 @@ namespace {
 constexpr int kTok = 32;          // tokens per workgroup
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kKS = 16;           // K values per stage
-constexpr int kStages = 4;
+constexpr int kKS = 32;           // K values per stage
 constexpr int kMaxE = 512;
 
 // s_waitcnt vmcnt(N); see the grouped GEMM for the encoding.
@@ -53,10 +55,10 @@ __device__ __forceinline__ void dma16(const void* g, void* l) {
 }
 
 // Chunk swizzles (16-byte chunk c of row r stored at c ^ swz): conflict-free
-// 16-byte reads of 32 consecutive rows for 64-byte rows (float32 W_r, float32
-// h) and for 32-byte rows (bfloat16 h).
+// 16-byte reads of 8 (16) consecutive rows for 128-byte rows (float32 W_r,
+// float32 h) and for 64-byte rows (bfloat16 h).
+__device__ __forceinline__ int swz128(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int swz64(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int swz32(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 // Orderable 32-bit key of a float: larger float -> larger key; -0 == +0;
 // NaN below everything.
@@ -95,19 +97,25 @@ struct RouteParams {
     float* w;
 };
 
-// NB = experts padded to a multiple of 128, over 128: each wave moves NB 1-KB
-// slices of W_r per stage (16 rows each), plus one slice of h (or a dummy).
-template <typename Tin, typename Tr, int NB>
+// NH = experts padded to a multiple of 128, over 128.  A stage holds 32 K values
+// of the 32 h rows and of the 128 NH W_r rows; each wave moves 2 NH 1-KB slices
+// of W_r (8 rows each) per stage, plus one slice of h (or a dummy).
+template <int NH>
+constexpr int route_stages() { return NH <= 3 ? 3 : 2; }
+
+template <typename Tin, typename Tr, int NH>
 __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
     constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
     constexpr int kARow = kKS * kInB;                 // bytes of an h row per stage
+    constexpr int kAChunks = kARow / 16;
     constexpr int kAInstr = kTok * kARow / 1024;      // real 1-KB h slices per stage
-    constexpr int kEPad = NB * 16 * kWaves;
+    constexpr int NB = 2 * NH;                        // W_r slices per wave per stage
+    constexpr int kEPad = 128 * NH;
     constexpr int kNCB = kEPad / 32;                  // 32-expert MFMA column blocks
-    constexpr int kCBW = (kNCB + 3) / 4;              // per wave (dealt round-robin to
+    constexpr int kCBW = NH;                          // per wave (dealt round-robin to
                                                       // the four waves of a K half)
-    constexpr int kBBytes = kEPad * 64;
-    constexpr int kStageBytes = kTok * kARow + kBBytes;
+    constexpr int kStages = route_stages<NH>();
+    constexpr int kStageBytes = kTok * kARow + kEPad * 128;
     constexpr int kDma = NB + 1;                      // DMAs per wave per stage
 
     extern __shared__ __attribute__((aligned(16))) char lds[];
@@ -122,12 +130,14 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
     const int ntok = (int)min((int64_t)kTok, rp.T - t0);
     const int d = rp.d;
 
-    // ---- 1. inverse RMS per row
-    if (rp.apply_norm) {
-        for (int tt = wave; tt < kTok; tt += kWaves) {
+    // ---- 1. inverse RMS per row (1 without the norm); then, if asked, the
+    // normalised rows
+    for (int tt = wave; tt < kTok; tt += kWaves) {
+        const char* row = (const char*)rp.h + (t0 + tt) * (int64_t)d * kInB;
+        float ir = 1.0f;
+        if (rp.apply_norm) {
             float ss = 0.0f;
             if (tt < ntok) {
-                const char* row = (const char*)rp.h + (t0 + tt) * (int64_t)d * kInB;
                 for (int c = lane * (16 / kInB); c < d; c += 64 * (16 / kInB)) {
                     const uint4 u = *(const uint4*)(row + (int64_t)c * kInB);
                     if (kInB == 4) {
@@ -148,40 +158,78 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
             }
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-            if (lane == 0) inv_rms[tt] = 1.0f / sqrtf(ss / (float)d + rp.eps);
+            ir = 1.0f / sqrtf(ss / (float)d + rp.eps);
         }
-    } else if (tid < kTok) {
-        inv_rms[tid] = 1.0f;
+        if (lane == 0) inv_rms[tt] = ir;
+        if (rp.r_out && tt < ntok) {
+            // the row again (from L2), 4 values per lane per step
+            for (int c = lane * 4; c < d; c += 256) {
+                float v[4];
+                if (kInB == 4) {
+                    const float4 f = *(const float4*)(row + (int64_t)c * 4);
+                    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+                } else {
+                    const uint2 u = *(const uint2*)(row + (int64_t)c * 2);
+                    v[0] = __uint_as_float(u.x << 16);
+                    v[1] = __uint_as_float(u.x & 0xffff0000u);
+                    v[2] = __uint_as_float(u.y << 16);
+                    v[3] = __uint_as_float(u.y & 0xffff0000u);
+                }
+                const float4 gg = rp.g ? *(const float4*)(rp.g + c) : make_float4(1, 1, 1, 1);
+                v[0] *= ir * gg.x;
+                v[1] *= ir * gg.y;
+                v[2] *= ir * gg.z;
+                v[3] *= ir * gg.w;
+                const int64_t o = (t0 + tt) * (int64_t)d + c;
+                if (sizeof(typename Elem<Tr>::store_t) == 4) {
+                    *(float4*)((float*)rp.r_out + o) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    uint2 u;
+                    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+                    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+                    *(uint2*)((u16*)rp.r_out + o) = u;
+                }
+            }
+        }
     }
 
-    // ---- 2. DMA sources (per lane, per stage offset kt * kKS elements)
-    // h: slice i holds rows (1024 / kARow) * i + lane / (kARow / 16)
+    // ---- 2. DMA sources (per lane, per stage offset kt * kKS elements).  When
+    // d is an odd multiple of 16 the last stage holds 16 K values: lanes of the
+    // missing half re-read the present half (their products are zeroed).
+    const int nk = (d + kKS - 1) / kKS;
+    const bool tail16 = (d % kKS) != 0;
     const char* a_src;
     char* a_dst;
+    int a_tail;                              // byte shift of this lane's chunk in the tail stage
     {
-        constexpr int kChunks = kARow / 16;
         const int slice = wave < kAInstr ? wave : 0;
-        const int r = slice * (1024 / kARow) + lane / kChunks;
-        const int c = lane % kChunks;
-        const int pc = kChunks == 4 ? (c ^ swz64(r)) : (c ^ swz32(r));
+        const int r = slice * (1024 / kARow) + lane / kAChunks;
+        const int c = lane % kAChunks;
+        const int pc = kAChunks == 8 ? (c ^ swz128(r)) : (c ^ swz64(r));
         const int rr = r < ntok ? r : 0;
         a_src = (const char*)rp.h + ((t0 + rr) * (int64_t)d) * kInB + pc * 16;
         a_dst = wave < kAInstr ? lds + slice * 1024 : dummy;
+        a_tail = pc >= kAChunks / 2 ? -(kAChunks / 2) * 16 : 0;
     }
     const char* b_src[NB];
+    int b_tail[NB];
 #pragma unroll
     for (int i = 0; i < NB; i++) {
-        const int r = (wave * NB + i) * 16 + (lane >> 2);
-        const int pc = (lane & 3) ^ swz64(r & 31);
+        const int r = (wave * NB + i) * 8 + (lane >> 3);
+        const int pc = (lane & 7) ^ swz128(r & 31);
         const int e = r < rp.E ? r : 0;
         b_src[i] = (const char*)(rp.W_r + (int64_t)e * d) + pc * 16;
+        b_tail[i] = pc >= 4 ? -64 : 0;
     }
     auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
         char* st = lds + buf * kStageBytes;
-        dma16(a_src + (int64_t)kt * kARow, a_dst == dummy ? dummy : st + (a_dst - lds));
+        const bool tl = tail16 && kt == nk - 1;
+        dma16(a_src + (int64_t)kt * kARow + (tl ? a_tail : 0),
+              a_dst == dummy ? dummy : st + (a_dst - lds));
 #pragma unroll
         for (int i = 0; i < NB; i++)
-            dma16(b_src[i] + (int64_t)kt * 64, st + kTok * kARow + (wave * NB + i) * 1024);
+            dma16(b_src[i] + (int64_t)kt * 128 + (tl ? b_tail[i] : 0),
+                  st + kTok * kARow + (wave * NB + i) * 1024);
     };
 
     floatx16 acc[kCBW];
@@ -190,7 +238,6 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
 #pragma unroll
         for (int v = 0; v < 16; v++) acc[i][v] = 0.0f;
 
-    const int nk = d / kKS;
     const int q = lane >> 5;                // which half of the stage's K this lane takes
     const int row = lane & 31;
     __syncthreads();                        // inv_rms visible
@@ -198,64 +245,62 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
     for (int s0 = 0; s0 < kStages - 1; s0++)
         if (s0 < nk) issue(s0, s0);
 
+    int buf = 0;
     for (int kt = 0; kt < nk; kt++) {
-        if (kt + 2 < nk) wait_vmcnt<2 * kDma>();
-        else if (kt + 1 < nk) wait_vmcnt<kDma>();
+        // stage kt has landed once at most the later issued stages are in flight
+        if (kStages == 3 && kt + 1 < nk) wait_vmcnt<kDma>();
         else wait_vmcnt<0>();
         bare_barrier();
-        if (kt + kStages - 1 < nk) issue(kt + kStages - 1, (kt + kStages - 1) % kStages);
-        const char* st = lds + (kt % kStages) * kStageBytes;
+        {
+            const int nb = buf == 0 ? kStages - 1 : buf - 1;   // slot of stage kt-1
+            if (kt + kStages - 1 < nk) issue(kt + kStages - 1, nb);
+        }
+        const char* st = lds + buf * kStageBytes;
+        buf = buf + 1 == kStages ? 0 : buf + 1;
         const int kb = kt * kKS;
 
-        // this wave's four MFMA steps s = 4 kh .. 4 kh + 3 use K values
-        // kb + 8q + s; g for them (scalar loads of the stage's 16 values)
-        float gs[4];
+        // this wave's eight MFMA steps s = 8 kh .. 8 kh + 7 use K values
+        // kb + 16 q + 8 kh + s; g for them (scalar loads of the stage's values)
+        const bool dead = tail16 && kt == nk - 1 && q == 1;
+        float gs[8];
 #pragma unroll
-        for (int s = 0; s < 4; s++) {
-            const float g0 = rp.g ? rp.g[kb + 4 * kh + s] : 1.0f;
-            const float g1 = rp.g ? rp.g[kb + 8 + 4 * kh + s] : 1.0f;
-            gs[s] = q ? g1 : g0;
+        for (int s2 = 0; s2 < 8; s2++) {
+            const float g0 = rp.g ? rp.g[kb + 8 * kh + s2] : 1.0f;
+            const float g1 = (rp.g && !(tail16 && kt == nk - 1)) ? rp.g[kb + 16 + 8 * kh + s2]
+                                                                  : 1.0f;
+            gs[s2] = dead ? 0.0f : (q ? g1 : g0);
         }
-        // this lane's 4 values of its h row
-        float a[4];
+        // this lane's 8 values of its h row
+        float a[8];
         if (kInB == 4) {
-            const float4 v0 = *(const float4*)(st + row * 64 + ((2 * q + kh) ^ swz64(row)) * 16);
+            const int c0 = 4 * q + 2 * kh;
+            const float4 v0 = *(const float4*)(st + row * 128 + ((c0) ^ swz128(row)) * 16);
+            const float4 v1 = *(const float4*)(st + row * 128 + ((c0 + 1) ^ swz128(row)) * 16);
             a[0] = v0.x; a[1] = v0.y; a[2] = v0.z; a[3] = v0.w;
+            a[4] = v1.x; a[5] = v1.y; a[6] = v1.z; a[7] = v1.w;
         } else {
-            const uint2 u = *(const uint2*)(st + row * 32 + (q ^ swz32(row)) * 16 + kh * 8);
-            a[0] = __uint_as_float(u.x << 16);
-            a[1] = __uint_as_float(u.x & 0xffff0000u);
-            a[2] = __uint_as_float(u.y << 16);
-            a[3] = __uint_as_float(u.y & 0xffff0000u);
+            const uint4 u = *(const uint4*)(st + row * 64 + ((2 * q + kh) ^ swz64(row)) * 16);
+            const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                a[2 * e] = __uint_as_float(ww[e] << 16);
+                a[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
+            }
         }
 #pragma unroll
-        for (int s = 0; s < 4; s++) a[s] *= gs[s];
+        for (int s2 = 0; s2 < 8; s2++) a[s2] *= gs[s2];
 #pragma unroll
         for (int i = 0; i < kCBW; i++) {
             const int cb = wc + 4 * i;
             if (cb < kNCB) {
-                const char* brow = st + kTok * kARow + (cb * 32 + row) * 64;
-                const float4 b0 = *(const float4*)(brow + ((2 * q + kh) ^ swz64(row)) * 16);
-                const float b[4] = {b0.x, b0.y, b0.z, b0.w};
+                const char* brow = st + kTok * kARow + (cb * 32 + row) * 128;
+                const int c0 = 4 * q + 2 * kh;
+                const float4 b0 = *(const float4*)(brow + ((c0) ^ swz128(row)) * 16);
+                const float4 b1 = *(const float4*)(brow + ((c0 + 1) ^ swz128(row)) * 16);
+                const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-                for (int s = 0; s < 4; s++)
-                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s], b[s], acc[i], 0, 0, 0);
-            }
-        }
-        // the normalised rows of this K slice, for the experts
-        if (rp.r_out) {
-            for (int idx = tid; idx < kTok * kKS; idx += kThreads) {
-                const int rr = idx / kKS, kk = idx % kKS;
-                if (rr < ntok) {
-                    const int off = kk * kInB;
-                    const int pc = (kARow == 64) ? ((off >> 4) ^ swz64(rr)) : ((off >> 4) ^ swz32(rr));
-                    const char* src = st + rr * kARow + pc * 16 + (off & 15);
-                    const float hv = kInB == 4 ? *(const float*)src
-                                               : bf16_to_f32(*(const u16*)src);
-                    const float gk = rp.g ? rp.g[kb + kk] : 1.0f;
-                    Elem<Tr>::store((Tr*)rp.r_out, (t0 + rr) * (int64_t)d + kb + kk,
-                                    hv * inv_rms[rr] * gk);
-                }
+                for (int s2 = 0; s2 < 8; s2++)
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s2], b[s2], acc[i], 0, 0, 0);
             }
         }
     }
@@ -331,28 +376,29 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
     }
 }
 
-template <typename Tin, typename Tr, int NB>
-hipError_t launch_nb(const RouteParams& rp, hipStream_t s) {
+template <typename Tin, typename Tr, int NH>
+hipError_t launch_nh(const RouteParams& rp, hipStream_t s) {
     constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
-    constexpr size_t kStage = kTok * kKS * kInB + NB * 16 * kWaves * 64;
-    constexpr size_t kTile = (size_t)kTok * (NB * 16 * kWaves + 1) * 4;
-    const size_t lds = (kStages * kStage + 1024) > kTile ? (kStages * kStage + 1024) : kTile;
-    hipError_t e = hipFuncSetAttribute((const void*)route_kernel<Tin, Tr, NB>,
+    constexpr size_t kStage = (size_t)kTok * kKS * kInB + (size_t)128 * NH * 128;
+    constexpr size_t kTile = (size_t)kTok * (128 * NH + 1) * 4;
+    constexpr size_t kRing = route_stages<NH>() * kStage + 1024;
+    const size_t lds = kRing > kTile ? kRing : kTile;
+    hipError_t e = hipFuncSetAttribute((const void*)route_kernel<Tin, Tr, NH>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t blocks = (rp.T + kTok - 1) / kTok;
-    hipLaunchKernelGGL((route_kernel<Tin, Tr, NB>), dim3((unsigned)blocks), dim3(kThreads), lds, s,
+    hipLaunchKernelGGL((route_kernel<Tin, Tr, NH>), dim3((unsigned)blocks), dim3(kThreads), lds, s,
                        rp);
     return hipGetLastError();
 }
 
 template <typename Tin, typename Tr>
 hipError_t launch_rt(const RouteParams& rp, hipStream_t s) {
-    switch ((rp.E + 16 * kWaves - 1) / (16 * kWaves)) {
-        case 1: return launch_nb<Tin, Tr, 1>(rp, s);
-        case 2: return launch_nb<Tin, Tr, 2>(rp, s);
-        case 3: return launch_nb<Tin, Tr, 3>(rp, s);
-        default: return launch_nb<Tin, Tr, 4>(rp, s);
+    switch ((rp.E + 127) / 128) {
+        case 1: return launch_nh<Tin, Tr, 1>(rp, s);
+        case 2: return launch_nh<Tin, Tr, 2>(rp, s);
+        case 3: return launch_nh<Tin, Tr, 3>(rp, s);
+        default: return launch_nh<Tin, Tr, 4>(rp, s);
     }
 }
 
