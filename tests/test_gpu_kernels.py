@@ -38,6 +38,8 @@ def _rms(a):
 ROUTE_SHAPES = [  # T, d_r, E, k
     (1, 16, 1, 1),
     (33, 64, 16, 2),        # ragged token tile
+    (65, 48, 130, 3),       # K = 1.5 stages (a 16-value tail), E just over a 128 multiple
+    (40, 80, 256, 5),       # K = 2.5 stages
     (1000, 128, 64, 4),
     (8192, 64, 384, 8),     # 535B router width and expert count, full token count
     (300, 32, 512, 16),     # largest E and k
@@ -80,7 +82,8 @@ def test_route_signed_zero_and_ties(M):
 
 @pytest.mark.parametrize("T,d,E,k,hdt,rdt", [(777, 3072, 384, 8, "f32", "bf16"),
                                               (256, 128, 16, 2, "f32", "f32"),
-                                              (500, 2048, 64, 4, "bf16", "f32")])
+                                              (500, 2048, 64, 4, "bf16", "f32"),
+                                              (129, 1040, 96, 6, "bf16", "bf16")])
 def test_route_rmsnorm_router_on_real_distribution(M, T, d, E, k, hdt, rdt):
     """RMSNorm + router on Gaussian inputs: normalised rows within one storage
     rounding, logits within float32 accumulation error, ids equal wherever the
@@ -117,6 +120,19 @@ def test_route_rmsnorm_router_on_real_distribution(M, T, d, E, k, hdt, rdt):
     # the rest is valid: every chosen expert is within the tolerance of the k-th logit
     for t in np.flatnonzero(~clear):
         assert np.all(lg64[t, gi[t]] >= srt[t, k - 1] - 2 * tol_l)
+
+
+@pytest.mark.parametrize("hdt,rdt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16")])
+def test_route_writes_router_input_without_norm(M, hdt, rdt):
+    """Without the norm the router input r is h itself, stored in r's dtype."""
+    g = torch.Generator().manual_seed(11)
+    T, d, E, k = 70, 112, 24, 3
+    h = torch.randn((T, d), generator=g).to(TDT[hdt])
+    W = torch.randn((E, d), generator=g).float()
+    r_out = torch.full((T, d), 7.0, dtype=TDT[rdt], device=DEV)
+    M.moe_route(h.to(DEV), W.to(DEV), k, r_out=r_out)
+    torch.cuda.synchronize()
+    assert torch.equal(r_out.cpu(), h.float().to(TDT[rdt]))
 
 
 # -------------------------------------------------------------- permute ----
@@ -190,6 +206,9 @@ def _group_counts(rng, E, kind, scale):
     ("bf16", 6, 3072, 3072, "sparse", 0),      # 535B expert shape, empty groups
     ("f32", 8, 128, 96, "uniform", 70),
     ("f32", 5, 64, 32, "sparse", 0),
+    ("bf16", 3, 64, 64, "uniform", 300),       # one K step in both GEMMs
+    ("bf16", 4, 128, 192, "skewed", 200),      # two and three K steps
+    ("f32", 3, 32, 64, "uniform", 90),         # one and two K steps in float32
 ])
 def test_grouped_ffn_parity(M, dt, E, d, H, kind, scale):
     rng = np.random.default_rng(E * d + H)
