@@ -10,17 +10,19 @@
 // Determinism: ranks come from the arrival order of assignments, never from
 // the order atomics happen to land, so every integer output is a pure function
 // of the ids (required bit-exact).
-//   pass 1  one wave per segment of kSeg assignments, in order: a lane's rank
-//           among equal ids of its 64-lane step comes from ballots (a match-any
-//           built bit by bit), plus the segment's running count in LDS; writes
-//           per-assignment local ranks and per-segment counts.
-//   pass 2  one workgroup: per expert, exclusive scan of segment counts (the
-//           segment's base), the capacity cut, the exclusive scan of kept rows
+//   pass 1  one wave per segment of 256 or more assignments (at most 4,096
+//           segments): a lane's rank among equal
+//           ids of its 64-lane step comes from ballots (a match-any built bit by
+//           bit), plus the segment's running count in LDS; writes per-assignment
+//           local ranks and per-segment counts.
+//   pass 2  one workgroup per expert: exclusive scan of that expert's segment
+//           counts (each segment's base) and the expert's total.
+//   pass 3  one workgroup: the capacity cut, the exclusive scan of kept rows
 //           (offsets), the drop count and optionally the GEMM's row-tile prefix.
-//   pass 3  one thread per assignment: row = offsets[e] + base + local rank,
-//           dropped if that rank reaches the capacity; writes slot_row/row_src.
-//   pass 4  one wave per destination row: copies the source row (optional) and
-//           clears row_src past the last kept row.
+//   pass 4  one thread per assignment: row = offsets[e] + base + local rank,
+//           dropped if that rank reaches the capacity; writes slot_row/row_src,
+//           and marks the rows past the last kept one empty.
+//   pass 5  (only with a source) one wave per destination row copies the row.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,31 +30,43 @@ namespace moe {
 
 namespace {
 
-constexpr int kSeg = 4096;        // assignments per pass-1 wave
+constexpr int kStepIds = 256;     // ids a pass-1 wave loads at a time
+constexpr int kMaxSeg = 4096;     // segments at most (bounds the workspace)
 constexpr int kMaxE = 1024;
 
-struct PermWs {
-    int32_t* local_rank;          // [n]
-    int32_t* seg_count;           // [nseg][E] (counts, then bases in place)
-};
+// Assignments per pass-1 segment: 256, or more so that there are at most
+// kMaxSeg segments (a multiple of 256).
+inline int64_t seg_len(int64_t n) {
+    const int64_t per = (n + kMaxSeg - 1) / kMaxSeg;
+    return per <= kStepIds ? kStepIds : (per + kStepIds - 1) / kStepIds * kStepIds;
+}
 
-__global__ __launch_bounds__(256) void rank_kernel(const int32_t* ids, int64_t n, int E,
-                                                   int32_t* local_rank, int32_t* seg_count) {
+__global__ __launch_bounds__(256) void rank_kernel(const int32_t* ids, int64_t n, int64_t seg_n,
+                                                   int E, int32_t* local_rank, int32_t* seg_count) {
     __shared__ int32_t hist[4][kMaxE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t seg = (int64_t)blockIdx.x * 4 + wave;
-    const int64_t nseg = (n + kSeg - 1) / kSeg;
+    const int64_t nseg = (n + seg_n - 1) / seg_n;
     int32_t* H = hist[wave];
     for (int e = lane; e < E; e += 64) H[e] = 0;
     __builtin_amdgcn_wave_barrier();
     if (seg < nseg) {
-        const int64_t a0 = seg * kSeg;
-        const int64_t a1 = min(n, a0 + kSeg);
+        const int64_t a0 = seg * seg_n;
+        const int64_t a1 = min(n, a0 + seg_n);
         const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-        for (int64_t base = a0; base < a1; base += 64) {
-            const int64_t a = base + lane;
+        for (int64_t b0 = a0; b0 < a1; b0 += kStepIds) {
+        // the next kStepIds ids, loaded up front
+        int idv[kStepIds / 64];
+#pragma unroll
+        for (int q = 0; q < kStepIds / 64; q++) {
+            const int64_t a = b0 + 64 * q + lane;
+            idv[q] = a < a1 ? ids[a] : -1;
+        }
+#pragma unroll
+        for (int q = 0; q < kStepIds / 64; q++) {
+            const int64_t a = b0 + 64 * q + lane;
             const bool in = a < a1;
-            int id = in ? ids[a] : -1;
+            const int id = idv[q];
             const bool valid = in && id >= 0 && id < E;
             // lanes with the same (valid, id)
             uint64_t match = __ballot(valid);
@@ -74,12 +88,32 @@ __global__ __launch_bounds__(256) void rank_kernel(const int32_t* ids, int64_t n
             __builtin_amdgcn_wave_barrier();
             if (in) local_rank[a] = valid ? prev + before : -1;
         }
+        }
         for (int e = lane; e < E; e += 64) seg_count[seg * E + e] = H[e];
     }
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(int64_t nseg, int E, int64_t capacity,
-                                                    int32_t* seg_count, int32_t* counts,
+// One workgroup per expert e: seg_count[s][e] becomes the number of e's
+// assignments in segments before s; counts[e] the total.
+__global__ __launch_bounds__(256) void colscan_kernel(int64_t nseg, int E, int32_t* seg_count,
+                                                      int32_t* counts) {
+    __shared__ int red[16];
+    const int e = blockIdx.x, tid = threadIdx.x;
+    const int64_t per = (nseg + 255) / 256;           // consecutive segments per thread
+    const int64_t s0 = tid * per;
+    int sum = 0;
+    for (int64_t s = s0; s < min(nseg, s0 + per); s++) sum += seg_count[s * E + e];
+    int total;
+    int run = block_exclusive_scan_1024(sum, red, total);
+    for (int64_t s = s0; s < min(nseg, s0 + per); s++) {
+        const int c = seg_count[s * E + e];
+        seg_count[s * E + e] = run;
+        run += c;
+    }
+    if (tid == 0) counts[e] = total;
+}
+
+__global__ __launch_bounds__(1024) void scan_kernel(int E, int64_t capacity, const int32_t* counts,
                                                     int32_t* offsets, int64_t* n_dropped,
                                                     int32_t* tile_prefix, int tile_bm) {
     __shared__ int red[16];
@@ -88,13 +122,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(int64_t nseg, int E, int64_t
     int kept = 0, tiles = 0;
     long long dropped = 0;
     if (tid < E) {
-        int run = 0;
-        for (int64_t s = 0; s < nseg; s++) {
-            const int c = seg_count[s * E + tid];
-            seg_count[s * E + tid] = run;
-            run += c;
-        }
-        counts[tid] = run;
+        const int run = counts[tid];
         kept = (capacity >= 0 && run > capacity) ? (int)capacity : run;
         dropped = run - kept;
         if (tile_prefix) tiles = (kept + tile_bm - 1) / tile_bm;
@@ -122,11 +150,16 @@ __global__ __launch_bounds__(1024) void scan_kernel(int64_t nseg, int E, int64_t
     }
 }
 
-__global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t n, int E,
-                                                    int64_t capacity, const int32_t* local_rank,
+// One thread per index i < max(n, R_phys): places assignment i (if i < n) and
+// marks row i empty if it lies past the last kept row (if i < R_phys).
+__global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t n, int64_t seg_n,
+                                                    int E, int64_t capacity,
+                                                    const int32_t* local_rank,
                                                     const int32_t* seg_base, const int32_t* offsets,
-                                                    int32_t* slot_row, int32_t* row_src) {
+                                                    int64_t R_phys, int32_t* slot_row,
+                                                    int32_t* row_src) {
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (a < R_phys && a >= offsets[E]) row_src[a] = -1;
     if (a >= n) return;
     const int lr = local_rank[a];
     if (lr < 0) {
@@ -134,7 +167,7 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t 
         return;
     }
     const int e = ids[a];
-    const int rank = seg_base[(a / kSeg) * E + e] + lr;
+    const int rank = seg_base[(a / seg_n) * E + e] + lr;
     if (capacity >= 0 && rank >= capacity) {
         slot_row[a] = -1;
         return;
@@ -144,20 +177,13 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t 
     row_src[row] = (int32_t)a;
 }
 
-// One wave per destination row: copy the source row in 16-byte chunks, or mark
-// the row empty when it lies past the last kept row.
+// One wave per kept destination row: copy the source row in 16-byte chunks.
 __global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E, int64_t R_phys,
-                                                   int32_t* row_src, const char* src, char* dst,
-                                                   int64_t row_bytes, int src_div) {
+                                                   const int32_t* row_src, const char* src,
+                                                   char* dst, int64_t row_bytes, int src_div) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= R_phys) return;
-    const int total = offsets[E];
-    if (r >= total) {
-        if (lane == 0) row_src[r] = -1;
-        return;
-    }
-    if (!src) return;
+    if (r >= R_phys || r >= offsets[E]) return;
     const int64_t a = row_src[r];
     const char* s = src + (a / src_div) * row_bytes;
     char* d = dst + r * row_bytes;
@@ -170,7 +196,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 size_t permute_ws_bytes(int64_t n, int E) {
-    const int64_t nseg = (n + kSeg - 1) / kSeg;
+    const int64_t nseg = (n + seg_len(n) - 1) / seg_len(n);
     return align256((size_t)(n > 0 ? n : 1) * 4) + align256((size_t)(nseg > 0 ? nseg : 1) * E * 4);
 }
 
@@ -179,20 +205,25 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                           int32_t* slot_row, int32_t* row_src, int32_t* counts, int32_t* offsets,
                           int64_t* n_dropped, int32_t* tile_prefix, int tile_bm, void* ws,
                           hipStream_t s) {
-    const int64_t nseg = (n + kSeg - 1) / kSeg;
+    const int64_t seg_n = seg_len(n);
+    const int64_t nseg = (n + seg_n - 1) / seg_n;
     int32_t* local_rank = (int32_t*)ws;
     int32_t* seg_count = (int32_t*)((char*)ws + align256((size_t)(n > 0 ? n : 1) * 4));
-    if (nseg > 0) {
+    if (nseg > 0)
         hipLaunchKernelGGL(rank_kernel, dim3((unsigned)((nseg + 3) / 4)), dim3(256), 0, s, ids, n,
-                           E, local_rank, seg_count);
+                           seg_n, E, local_rank, seg_count);
+    // with no segments this writes zero counts
+    hipLaunchKernelGGL(colscan_kernel, dim3((unsigned)E), dim3(256), 0, s, nseg, E, seg_count,
+                       counts);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, E, capacity, counts, offsets,
+                       n_dropped, tile_prefix, tile_bm);
+    const int64_t m = n > R_phys ? n : R_phys;
+    if (m > 0) {
+        hipLaunchKernelGGL(place_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, ids,
+                           n, seg_n, E, capacity, local_rank, seg_count, offsets, R_phys, slot_row,
+                           row_src);
     }
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, nseg, E, capacity, seg_count,
-                       counts, offsets, n_dropped, tile_prefix, tile_bm);
-    if (n > 0) {
-        hipLaunchKernelGGL(place_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids,
-                           n, E, capacity, local_rank, seg_count, offsets, slot_row, row_src);
-    }
-    if (R_phys > 0) {
+    if (src && R_phys > 0) {
         hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((R_phys + 3) / 4)), dim3(256), 0, s,
                            offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
                            width * elem_bytes, src_div);
