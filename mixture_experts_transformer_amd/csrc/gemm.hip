@@ -62,9 +62,8 @@ constexpr int kBM = 256;          // rows per tile
 constexpr int kBN = 256;          // B rows (LDS columns) per tile
 constexpr int kRowBytes = 128;    // bytes of each row per K step: whole cache lines
 constexpr int kOpBytes = kBM * kRowBytes;              // one operand's K step: 32 KB
-constexpr int kSlotsA = 2;        // LDS ring of A steps
-constexpr int kSlotsB = 3;        // LDS ring of B steps (the streamed weights run further ahead)
-constexpr int kBBase = kSlotsA * kOpBytes;             // B ring offset in LDS
+constexpr int kSlotsFar = 3;      // LDS ring of the operand that runs two steps ahead
+constexpr int kSlotsNear = 2;     // LDS ring of the other operand
 constexpr int kDmaPerOperand = kBM * kRowBytes / 1024 / kWaves;   // 1-KB DMAs per wave
 
 static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
@@ -131,8 +130,13 @@ __device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* C, int64_t off, con
     *(uint4*)(C + off) = u;
 }
 
-template <typename T, typename OutT, int EPI>
+// AA: A's steps run two ahead in the three-slot ring (dense GEMMs, and grouped
+// ones whose weights serve several row tiles); otherwise B's do (grouped GEMMs
+// that stream each expert's weights once).
+template <typename T, typename OutT, int EPI, bool AA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+    constexpr int kSlotsA = AA ? kSlotsFar : kSlotsNear;
+    constexpr int kBBase = kSlotsA * kOpBytes;             // B ring offset in LDS
     constexpr int kElem = Elem<T>::kBytes;
     constexpr int kSteps = kRowBytes / (Mfma<T>::kK * kElem);   // MFMA k-steps per K step
     constexpr int kSub = kSteps / 4;                             // k-steps per quarter step
@@ -255,11 +259,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     };
     char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
     char* const b_lds = lds + kBBase + (wave * kDmaPerOperand) * 1024;
-    auto issue_a = [&](int kt, int slot) __attribute__((always_inline)) {
+    // A DMAs i0, i0+1, ... (n of them) of step kt
+    auto issue_a = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
         const char* const Ak = A_t + (int64_t)kt * kRowBytes;
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++)
-            dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
+            if (i >= i0 && i < i0 + n) dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
     };
     // B DMAs i0, i0+1, ... (n of them) of step kt
     auto issue_b = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
@@ -268,25 +273,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         for (int i = 0; i < kDmaPerOperand; i++)
             if (i >= i0 && i < i0 + n) dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
     };
-    // Issue order, per wave: B0 A0 B1 A1 (this prologue), then during step kt's
-    // quarters 1-2 B(kt+2), and after step kt's barrier A(kt+2).  When step kt+1
-    // is needed, the only younger loads are B(kt+2)'s, so the wait is a constant
-    // kDmaPerOperand while the weights run two steps ahead.  Past the last step,
-    // the same DMAs re-read the last step into slots nothing reads any more,
-    // which keeps the count fixed.
+    // the operand in the three-slot ring ("far") and the other one ("near")
+    auto issue_far = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
+        if constexpr (AA) issue_a(kt, slot, i0, n);
+        else issue_b(kt, slot, i0, n);
+    };
+    auto issue_near = [&](int kt, int slot) __attribute__((always_inline)) {
+        if constexpr (AA) issue_b(kt, slot, 0, kDmaPerOperand);
+        else issue_a(kt, slot, 0, kDmaPerOperand);
+    };
+    // Issue order, per wave: F0 N0 F1 N1 (this prologue; F = the far operand,
+    // N = the near one), then during step kt's quarters 1-2 F(kt+2), and after
+    // step kt's barrier N(kt+2).  When step kt+1 is needed, the only younger
+    // loads are F(kt+2)'s, so the wait is a constant kDmaPerOperand while the far
+    // operand runs two steps ahead.  Past the last step, the same DMAs re-read
+    // the last step into slots nothing reads any more, which keeps the count
+    // fixed.
     auto prologue = [&]() __attribute__((always_inline)) {
-        issue_b(0, 0, 0, kDmaPerOperand);
-        issue_a(0, 0);
+        issue_far(0, 0, 0, kDmaPerOperand);
+        issue_near(0, 0);
         if (nk > 1) {
-            issue_b(1, 1, 0, kDmaPerOperand);
-            issue_a(1, 1);
+            issue_far(1, 1, 0, kDmaPerOperand);
+            issue_near(1, 1);
         }
     };
 
-    // Epilogue staging: each wave owns a 4 KB piece of the third B slot, which
-    // the next tile's first loads (slots A0, A1, B0, B1) leave alone.
-    float* const stage = (float*)(lds + kBBase + 2 * kOpBytes + wave * 4096);
-    static_assert(kSlotsB == 3 && kWaves * 4096 == kOpBytes, "staging layout");
+    // Epilogue staging: each wave owns a 4 KB piece of the far ring's third
+    // slot, which the next tile's first loads (slots 0 and 1 of both rings)
+    // leave alone.
+    float* const stage = (float*)(lds + (AA ? 0 : kBBase) + 2 * kOpBytes + wave * 4096);
+    static_assert(kSlotsFar == 3 && kWaves * 4096 == kOpBytes, "staging layout");
 
     int64_t t = lo + slot;
     if (t >= hi) return;
@@ -385,44 +401,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             // fragments are read while the MFMAs of the previous one run.  After
             // the third quarter's reads the wave waits for step kt+1 to land and
             // meets the others at the barrier; by then every read of step kt's
-            // slots has completed, so A's is refilled at once with step kt+2 and
-            // B's during the next step with step kt+3.
-            int sa = 0, sb = 0;           // slots of step kt
+            // slots has completed, so the near ring's is refilled at once with
+            // step kt+2 and the far ring's during the next step with step kt+3.
+            int sf = 0, sn = 0;           // far and near ring slots of step kt
 #pragma unroll 1
             for (int kt = 0; kt + 1 < nk; kt++) {
-                const int kb2 = min(kt + 2, nk - 1);            // B step issued now
-                const int sb2 = sb == 0 ? kSlotsB - 1 : sb - 1;  // its slot, (kt + 2) % 3
+                const int kf2 = min(kt + 2, nk - 1);              // far step issued now
+                const int sf2 = sf == 0 ? kSlotsFar - 1 : sf - 1;  // its slot, (kt + 2) % 3
+                const int sa = AA ? sf : sn, sb = AA ? sn : sf;
                 if (NACT > 0) {
                     load_sub(sa, sb, 1, f1a, f1b);
                     mma_sub(f0a, f0b);
-                    issue_b(kb2, sb2, 0, kDmaPerOperand / 2);
+                    issue_far(kf2, sf2, 0, kDmaPerOperand / 2);
                     order_sub(V2{});
                     load_sub(sa, sb, 2, f0a, f0b);
                     mma_sub(f1a, f1b);
-                    issue_b(kb2, sb2, kDmaPerOperand / 2, kDmaPerOperand / 2);
+                    issue_far(kf2, sf2, kDmaPerOperand / 2, kDmaPerOperand / 2);
                     order_sub(V2{});
                     load_sub(sa, sb, 3, f1a, f1b);
                     mma_sub(f0a, f0b);
                     order_sub(V0{});
                 } else {
-                    issue_b(kb2, sb2, 0, kDmaPerOperand);
+                    issue_far(kf2, sf2, 0, kDmaPerOperand);
                 }
                 // keep this step's MFMAs ahead of the wait, so they run while the
                 // wave waits at the barrier
                 __builtin_amdgcn_sched_barrier(0);
                 wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
                 bare_barrier();
-                sb = sb == kSlotsB - 1 ? 0 : sb + 1;
+                sf = sf == kSlotsFar - 1 ? 0 : sf + 1;
                 if (NACT > 0) {
-                    load_sub(sa ^ 1, sb, 0, f0a, f0b);
+                    load_sub(AA ? sf : sn ^ 1, AA ? sn ^ 1 : sf, 0, f0a, f0b);
                     mma_sub(f1a, f1b);
-                    issue_a(min(kt + 2, nk - 1), sa);
+                    issue_near(min(kt + 2, nk - 1), sn);
                     order_sub(VA{});
                 } else {
-                    issue_a(min(kt + 2, nk - 1), sa);
+                    issue_near(min(kt + 2, nk - 1), sn);
                 }
-                sa ^= 1;
+                sn ^= 1;
             }
+            const int sa = AA ? sf : sn, sb = AA ? sn : sf;
             // last step (its first quarter is already in registers)
             if (NACT > 0) {
                 load_sub(sa, sb, 1, f1a, f1b);
@@ -534,16 +552,22 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* offset
     if (tid == 0) tp[G] = total;
 }
 
-constexpr size_t kLdsBytes = (size_t)(kSlotsA + kSlotsB) * kOpBytes;   // 163,840 bytes
+constexpr size_t kLdsBytes = (size_t)(kSlotsFar + kSlotsNear) * kOpBytes;   // 163,840 bytes
+
+template <typename T, typename OutT, int EPI, bool AA>
+hipError_t launch_aa(const GemmParams& p, int grid, hipStream_t s) {
+    // opting in to more than 64 KB of dynamic LDS is idempotent and cheap
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI, AA>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI, AA>), dim3(grid), dim3(kThreads), kLdsBytes, s, p);
+    return hipGetLastError();
+}
 
 template <typename T, typename OutT, int EPI>
 hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
-    // opting in to more than 64 KB of dynamic LDS is idempotent and cheap
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI>), dim3(grid), dim3(kThreads), kLdsBytes, s, p);
-    return hipGetLastError();
+    return p.a_ahead ? launch_aa<T, OutT, EPI, true>(p, grid, s)
+                     : launch_aa<T, OutT, EPI, false>(p, grid, s);
 }
 
 }  // namespace

@@ -34,6 +34,7 @@ struct GemmParams {
     int64_t n_per;               // SwiGLU: hidden columns per [gate; up] block of B
     int64_t a_src_rows;          // gather: rows of the A matrix a_rows indexes (host check)
     int32_t group_m;             // row tiles per swizzle group
+    int32_t a_ahead;             // 1: A's K steps run two ahead (else B's)
     GemmSeg seg[kMaxSeg];
     int32_t nseg;
     void* C;                     // output row r: C + r * ldc
