@@ -13,7 +13,13 @@ namespace moe {
 
 namespace {
 
-constexpr int kMaxChunks = 8;     // 16-byte chunks per lane held in registers
+// Rows whose loads one wave keeps in flight together, and 16-byte chunks per
+// lane per pass: 4 x 3 KB per wave in flight with 98 VGPRs (measured against
+// 8 x 2 and 8 x 3 at the 535B shape; all within 4%).
+constexpr int kRowsInFlight = 4;
+constexpr int kChunksPerPass = 3;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ void unpack(const uint4& u, float* v);
@@ -48,7 +54,14 @@ __device__ __forceinline__ uint4 pack<bf16_t>(const float* v) {
     return u;
 }
 
-template <typename T>
+// One wave per output row.  Lane j < k holds assignment j's row and weight, read
+// once; the wave takes them in order with readlane.  The row is done in passes
+// of C 16-byte chunks per lane; in each pass the loads of J assignments' rows
+// are all issued before any is accumulated, so a wave keeps J * C KB of reads
+// in flight.  Accumulation stays in j order.  Every Y row is read once and every
+// output row written once, so both go through non-temporal accesses (14% faster
+// than cached ones at the 535B shape).
+template <typename T, int J, int C>
 __global__ __launch_bounds__(256) void combine_kernel(const char* Y, const int32_t* slot_row,
                                                       const float* w, int64_t n_tok, int k,
                                                       int64_t row_bytes, char* out, int flags) {
@@ -56,45 +69,77 @@ __global__ __launch_bounds__(256) void combine_kernel(const char* Y, const int32
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= n_tok) return;
+    int my_row = -1;
+    float my_w = 0.0f;
+    if (lane < k) {
+        my_row = slot_row[t * k + lane];
+        my_w = w ? w[t * k + lane] : 1.0f;
+    }
+    if (__ballot(my_row >= 0) == 0 && (flags & MOE_COMBINE_KEEP_UNROUTED)) return;
     const int64_t nchunk = row_bytes / 16;
-    bool any = false;
-    for (int j = 0; j < k; j++) any |= slot_row[t * k + j] >= 0;
-    if (!any && (flags & MOE_COMBINE_KEEP_UNROUTED)) return;
-    // chunks handled by this lane: lane, lane + 64, ... (kMaxChunks per pass)
-    for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * kMaxChunks) {
-        float acc[kMaxChunks][kPer];
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * C) {
+        float acc[C][kPer];
 #pragma unroll
-        for (int q = 0; q < kMaxChunks; q++)
+        for (int q = 0; q < C; q++)
 #pragma unroll
             for (int e = 0; e < kPer; e++) acc[q][e] = 0.0f;
-        for (int j = 0; j < k; j++) {
-            const int row = slot_row[t * k + j];
-            if (row < 0) continue;
-            const float wj = w ? w[t * k + j] : 1.0f;
-            const char* src = Y + (int64_t)row * row_bytes;
-            uint4 u[kMaxChunks];
+        for (int j0 = 0; j0 < k; j0 += J) {
+            uint4 u[J][C];
 #pragma unroll
-            for (int q = 0; q < kMaxChunks; q++) {
-                const int64_t c = c0 + lane + 64 * q;
-                if (c < nchunk) u[q] = *(const uint4*)(src + c * 16);
+            for (int jj = 0; jj < J; jj++) {
+                const int j = j0 + jj;
+                const int row = j < k ? __builtin_amdgcn_readlane(my_row, j) : -1;
+                if (row >= 0) {
+                    // lanes past the row's end re-read its last chunk (unused)
+                    const char* src = Y + (int64_t)row * row_bytes;
+#pragma unroll
+                    for (int q = 0; q < C; q++) {
+                        const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
+                        const u32x4 x = __builtin_nontemporal_load((const u32x4*)(src + c * 16));
+                        u[jj][q] = make_uint4(x[0], x[1], x[2], x[3]);
+                    }
+                }
             }
 #pragma unroll
-            for (int q = 0; q < kMaxChunks; q++) {
-                const int64_t c = c0 + lane + 64 * q;
-                if (c < nchunk) {
-                    float v[kPer];
-                    unpack<T>(u[q], v);
+            for (int jj = 0; jj < J; jj++) {
+                const int j = j0 + jj;
+                const int row = j < k ? __builtin_amdgcn_readlane(my_row, j) : -1;
+                if (row >= 0) {
+                    const float wj = __int_as_float(
+                        __builtin_amdgcn_readlane(__float_as_int(my_w), j));
 #pragma unroll
-                    for (int e = 0; e < kPer; e++) acc[q][e] += wj * v[e];
+                    for (int q = 0; q < C; q++) {
+                        float v[kPer];
+                        unpack<T>(u[jj][q], v);
+#pragma unroll
+                        for (int e = 0; e < kPer; e++) acc[q][e] += wj * v[e];
+                    }
                 }
             }
         }
 #pragma unroll
-        for (int q = 0; q < kMaxChunks; q++) {
+        for (int q = 0; q < C; q++) {
             const int64_t c = c0 + lane + 64 * q;
-            if (c < nchunk) *(uint4*)(out + t * row_bytes + c * 16) = pack<T>(acc[q]);
+            if (c < nchunk) {
+                const uint4 pk = pack<T>(acc[q]);
+                const u32x4 x = {pk.x, pk.y, pk.z, pk.w};
+                __builtin_nontemporal_store(x, (u32x4*)(out + t * row_bytes + c * 16));
+            }
         }
     }
+}
+
+template <typename T>
+void launch_t(const void* Y, const int32_t* slot_row, const float* w, int64_t T_, int k,
+              int64_t row_bytes, void* out, int flags, hipStream_t s) {
+    const int64_t blocks = (T_ + 3) / 4;
+    if (k == 1)
+        hipLaunchKernelGGL((combine_kernel<T, 1, 8>), dim3((unsigned)blocks), dim3(256), 0, s,
+                           (const char*)Y, slot_row, w, T_, k, row_bytes, (char*)out, flags);
+    else
+        hipLaunchKernelGGL((combine_kernel<T, kRowsInFlight, kChunksPerPass>),
+                           dim3((unsigned)blocks), dim3(256), 0, s, (const char*)Y, slot_row, w,
+                           T_, k, row_bytes, (char*)out, flags);
 }
 
 }  // namespace
@@ -102,13 +147,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const char* Y, const int32
 hipError_t launch_combine(const void* Y, moe_dtype dt, const int32_t* slot_row, const float* w,
                           int64_t T, int k, int64_t width, void* out, int flags, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const int64_t blocks = (T + 3) / 4;
     if (dt == MOE_BF16)
-        hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s,
-                           (const char*)Y, slot_row, w, T, k, width * 2, (char*)out, flags);
+        launch_t<bf16_t>(Y, slot_row, w, T, k, width * 2, out, flags, s);
     else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, s,
-                           (const char*)Y, slot_row, w, T, k, width * 4, (char*)out, flags);
+        launch_t<float>(Y, slot_row, w, T, k, width * 4, out, flags, s);
     return hipGetLastError();
 }
 
