@@ -87,6 +87,13 @@ int grouped_a_ahead(int64_t R_rows, int E) {
     return R_rows >= (int64_t)2 * gemm_block_m() * E ? 1 : 0;
 }
 
+// The grouped GEMMs' outputs (the expert hidden and output rows, hundreds of MB
+// at the 535B shape) are read back from HBM by the next kernel anyway, so they
+// are written non-temporally (down GEMM 1.72 -> 1.66 ms, gate/up 3.23 -> 3.19 ms
+// there); the dense GEMMs' smaller outputs keep the cached path, which lets the
+// next GEMM find part of them in cache.
+constexpr int kGroupedNtStore = 1;
+
 // Grouped gated MLP over row groups: h = SwiGLU(X W_gu[g]^T), Y = h W_d[g]^T.
 // X rows optionally gathered (a_rows / a_div).
 moe_status grouped_ffn_impl(const void* X, int64_t ldx, const int32_t* a_rows, int a_div,
@@ -97,6 +104,7 @@ moe_status grouped_ffn_impl(const void* X, int64_t ldx, const int32_t* a_rows, i
     GemmParams p = gemm_base();
     p.group_m = kGroupGrouped;
     p.a_ahead = grouped_a_ahead(R_rows, E);
+    p.nt_store = kGroupedNtStore;
     p.a_src_rows = a_src_rows;
     p.offsets = offsets;
     p.tile_prefix = tile_prefix;
@@ -120,6 +128,7 @@ moe_status grouped_down_impl(const void* h, const int32_t* offsets, const int32_
     GemmParams p = gemm_base();
     p.group_m = kGroupGrouped;
     p.a_ahead = grouped_a_ahead(R_rows, E);
+    p.nt_store = kGroupedNtStore;
     p.offsets = offsets;
     p.tile_prefix = tile_prefix;
     p.G = E;

@@ -114,20 +114,30 @@ __device__ __forceinline__ int find_group(const int32_t* tp, int G, int m) {
     return lo;
 }
 
+// 16-byte output store; nt: non-temporal (the output is re-read from HBM anyway)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16(void* dst, u32x4 x, bool nt) {
+    if (nt) __builtin_nontemporal_store(x, (u32x4*)dst);
+    else *(u32x4*)dst = x;
+}
 template <typename OutT, int kVec>
-__device__ __forceinline__ void store_vec(OutT* C, int64_t off, const float* v);
+__device__ __forceinline__ void store_vec(OutT* C, int64_t off, const float* v, bool nt);
 template <>
-__device__ __forceinline__ void store_vec<float, 4>(float* C, int64_t off, const float* v) {
-    *(float4*)(C + off) = make_float4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ void store_vec<float, 4>(float* C, int64_t off, const float* v,
+                                                    bool nt) {
+    const u32x4 x = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                     __float_as_uint(v[3])};
+    store16(C + off, x, nt);
 }
 template <>
-__device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* C, int64_t off, const float* v) {
-    uint4 u;
-    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    u.z = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    u.w = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
-    *(uint4*)(C + off) = u;
+__device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* C, int64_t off, const float* v,
+                                                     bool nt) {
+    u32x4 x;
+    x[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    x[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    x[2] = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
+    x[3] = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    store16(C + off, x, nt);
 }
 
 // AA: A's steps run two ahead in the three-slot ring (dense GEMMs, and grouped
@@ -464,6 +474,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // SwiGLU a wave's two column blocks are the gate and the up rows of the
         // same hidden columns, so h = silu(G) * U is formed in registers first.
         OutT* const C = (OutT*)p.C;
+        const bool nt_out = p.nt_store != 0;
         constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
         // write back R staged rows of W columns starting at tile row rbase
         auto store_rows = [&](auto r_c, auto w_c, int rbase, int64_t cbase)
@@ -486,7 +497,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                         for (int e = 0; e < kVec; e++)
                             vals[e] += Elem<OutT>::load((const OutT*)p.addend, aoff + e);
                     }
-                    store_vec<OutT, kVec>(C, (done.row0 + grow) * p.ldc + col, vals);
+                    store_vec<OutT, kVec>(C, (done.row0 + grow) * p.ldc + col, vals, nt_out);
                 }
             }
         };

@@ -35,6 +35,7 @@ struct GemmParams {
     int64_t a_src_rows;          // gather: rows of the A matrix a_rows indexes (host check)
     int32_t group_m;             // row tiles per swizzle group
     int32_t a_ahead;             // 1: A's K steps run two ahead (else B's)
+    int32_t nt_store;            // 1: non-temporal output stores
     GemmSeg seg[kMaxSeg];
     int32_t nseg;
     void* C;                     // output row r: C + r * ldc
