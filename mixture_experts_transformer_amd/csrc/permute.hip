@@ -178,6 +178,16 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t 
 }
 
 // One wave per kept destination row: copy the source row in 16-byte chunks.
+// One wave per kept row.  Each pass issues the loads of 8 16-byte chunks per
+// lane before any store, so a wave keeps 8 KB in flight; lanes past the row's
+// end re-read its last chunk and store nothing.  Destination rows are written
+// once and stored non-temporally; source rows are read non-temporally only when
+// each is read once (NT_SRC: src_div == 1), since a source row gathered for
+// several assignments should stay in cache between its reads.
+constexpr int kCopyChunks = 8;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT_SRC>
 __global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E, int64_t R_phys,
                                                    const int32_t* row_src, const char* src,
                                                    char* dst, int64_t row_bytes, int src_div) {
@@ -187,8 +197,21 @@ __global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E
     const int64_t a = row_src[r];
     const char* s = src + (a / src_div) * row_bytes;
     char* d = dst + r * row_bytes;
-    for (int64_t c = (int64_t)lane * 16; c < row_bytes; c += 64 * 16)
-        *(uint4*)(d + c) = *(const uint4*)(s + c);
+    const int64_t nchunk = row_bytes / 16;
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * kCopyChunks) {
+        u32x4 v[kCopyChunks];
+#pragma unroll
+        for (int q = 0; q < kCopyChunks; q++) {
+            const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
+            if constexpr (NT_SRC) v[q] = __builtin_nontemporal_load((const u32x4*)(s + c * 16));
+            else v[q] = *(const u32x4*)(s + c * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < kCopyChunks; q++) {
+            const int64_t c = c0 + lane + 64 * q;
+            if (c < nchunk) __builtin_nontemporal_store(v[q], (u32x4*)(d + c * 16));
+        }
+    }
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -224,9 +247,14 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                            row_src);
     }
     if (src && R_phys > 0) {
-        hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((R_phys + 3) / 4)), dim3(256), 0, s,
-                           offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
-                           width * elem_bytes, src_div);
+        if (src_div == 1)
+            hipLaunchKernelGGL(copy_kernel<true>, dim3((unsigned)((R_phys + 3) / 4)), dim3(256),
+                               0, s, offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
+                               width * elem_bytes, src_div);
+        else
+            hipLaunchKernelGGL(copy_kernel<false>, dim3((unsigned)((R_phys + 3) / 4)), dim3(256),
+                               0, s, offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
+                               width * elem_bytes, src_div);
     }
     return hipGetLastError();
 }
