@@ -80,7 +80,8 @@ const char *moe_status_str(moe_status s);
  *   logits_out (device) [T, E] float32, or NULL
  *   topk_ids   (device) [T, k] int32: j-th best expert of token t
  *   topk_w     (device) [T, k] float32 routing weights
- * Limits: 1 <= E <= 512, 1 <= k <= min(E, 16), d_r a multiple of 16, T >= 0. */
+ * Limits: 1 <= E <= 512, 1 <= k <= min(E, 16), d_r a multiple of 16 and at
+ * least 32, T >= 0. */
 moe_status moe_route(const void *h, moe_dtype h_dt, int64_t T, int64_t d_r,
                      const float *norm_g, float eps, int32_t apply_norm,
                      const float *W_r, const float *b_r, int32_t E, int32_t k,

@@ -242,7 +242,7 @@ moe_status moe_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d_r, cons
                      float eps, int32_t apply_norm, const float* W_r, const float* b_r, int32_t E,
                      int32_t k, void* r_out, moe_dtype r_dt, float* logits_out, int32_t* topk_ids,
                      float* topk_w, moe_stream stream) {
-    if (T < 0 || d_r <= 0 || d_r % 16) return MOE_ESHAPE;
+    if (T < 0 || d_r < 32 || d_r % 16) return MOE_ESHAPE;
     if (E < 1 || E > 512 || k < 1 || k > 16 || k > E) return MOE_ESHAPE;
     if (!dt_ok(h_dt) || (r_out && !dt_ok(r_dt))) return MOE_EDTYPE;
     if (T > 0 && (!h || !W_r || !topk_ids || !topk_w)) return MOE_EINVAL;

@@ -54,6 +54,33 @@ __device__ __forceinline__ void dma16(const void* g, void* l) {
                                      (__attribute__((address_space(3))) void*)l, 16, 0, 0);
 }
 
+// a pointer every lane holds the same value of, moved to scalar registers (so a
+// DMA takes it as its scalar base)
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t x = (uint64_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return (const void*)(((uint64_t)hi << 32) | lo);
+}
+
+// One 1-KB DMA (64 lanes x 16 bytes) from a wave-uniform base plus a 32-bit
+// per-lane offset into LDS at byte address lds_addr, written out so that the
+// compiler neither rebuilds 64-bit addresses per stage nor inserts waits of its
+// own for it: every wait for these loads is the explicit vmcnt wait before the
+// stage's barrier.  (M0 needs one wait state before the load reads it.)
+__device__ __forceinline__ void dma16_off(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
 // Chunk swizzles (16-byte chunk c of row r stored at c ^ swz): conflict-free
 // 16-byte reads of 8 (16) consecutive rows for 128-byte rows (float32 W_r,
 // float32 h) and for 64-byte rows (bfloat16 h).
@@ -193,43 +220,46 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
         }
     }
 
-    // ---- 2. DMA sources (per lane, per stage offset kt * kKS elements).  When
-    // d is an odd multiple of 16 the last stage holds 16 K values: lanes of the
-    // missing half re-read the present half (their products are zeroed).
+    // ---- 2. DMA sources (per lane, per stage offset kt * kKS elements)
     const int nk = (d + kKS - 1) / kKS;
     const bool tail16 = (d % kKS) != 0;
-    const char* a_src;
+    // Each DMA source is a wave-uniform base (advanced per stage in scalar
+    // registers) plus a fixed 32-bit per-lane offset, so no address register is
+    // rewritten while its DMA may still be in flight.  When d is an odd multiple
+    // of 16 the last stage takes the row's last 32 values (its base moved back
+    // by 16): its first half was already summed in the previous stage and is
+    // zeroed, its second half is the 16-value tail (d >= 48 then).
+    const char* const a_base = (const char*)rp.h + t0 * (int64_t)d * kInB;
+    uint32_t a_off;
     char* a_dst;
-    int a_tail;                              // byte shift of this lane's chunk in the tail stage
     {
         const int slice = wave < kAInstr ? wave : 0;
         const int r = slice * (1024 / kARow) + lane / kAChunks;
         const int c = lane % kAChunks;
         const int pc = kAChunks == 8 ? (c ^ swz128(r)) : (c ^ swz64(r));
         const int rr = r < ntok ? r : 0;
-        a_src = (const char*)rp.h + ((t0 + rr) * (int64_t)d) * kInB + pc * 16;
+        a_off = (uint32_t)(rr * d * kInB + pc * 16);
         a_dst = wave < kAInstr ? lds + slice * 1024 : dummy;
-        a_tail = pc >= kAChunks / 2 ? -(kAChunks / 2) * 16 : 0;
     }
-    const char* b_src[NB];
-    int b_tail[NB];
+    uint32_t b_off[NB];
 #pragma unroll
     for (int i = 0; i < NB; i++) {
         const int r = (wave * NB + i) * 8 + (lane >> 3);
         const int pc = (lane & 7) ^ swz128(r & 31);
         const int e = r < rp.E ? r : 0;
-        b_src[i] = (const char*)(rp.W_r + (int64_t)e * d) + pc * 16;
-        b_tail[i] = pc >= 4 ? -64 : 0;
+        b_off[i] = (uint32_t)(e * d * 4 + pc * 16);
     }
     auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
         char* st = lds + buf * kStageBytes;
-        const bool tl = tail16 && kt == nk - 1;
-        dma16(a_src + (int64_t)kt * kARow + (tl ? a_tail : 0),
-              a_dst == dummy ? dummy : st + (a_dst - lds));
+        char* const ad = a_dst == dummy ? dummy : st + (a_dst - lds);
+        const int64_t k0 = (int64_t)kt * kKS - (tail16 && kt == nk - 1 ? kKS / 2 : 0);
+        const void* const Ak = uniform_ptr(a_base + k0 * kInB);
+        const void* const Bk = uniform_ptr((const char*)rp.W_r + k0 * 4);
+        const uint32_t st_addr = lds_addr(st);
+        dma16_off(Ak, a_off, lds_addr(ad));
 #pragma unroll
         for (int i = 0; i < NB; i++)
-            dma16(b_src[i] + (int64_t)kt * 128 + (tl ? b_tail[i] : 0),
-                  st + kTok * kARow + (wave * NB + i) * 1024);
+            dma16_off(Bk, b_off[i], st_addr + kTok * kARow + (wave * NB + i) * 1024);
     };
 
     floatx16 acc[kCBW];
@@ -240,7 +270,30 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
 
     const int q = lane >> 5;                // which half of the stage's K this lane takes
     const int row = lane & 31;
+    // This lane's eight MFMA steps of stage kt use K values kt*32 + 16 q + 8 kh
+    // + 0..7 (in the tail stage, values 16 lower; its q = 0 lanes are zeroed).
+    // The gains of both halves are scalar loads issued at the end of the stage
+    // before, after its MFMAs.
+    // (read through the constant address space: the gains are never written
+    // here, and the loads then go through the scalar unit)
+    typedef const __attribute__((address_space(4))) float* cgp;
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    f32x8 g0n, g1n;
+    auto load_g = [&](int kt) __attribute__((always_inline)) {
+        const int kb = kt * kKS;
+        const bool tl = tail16 && kt == nk - 1;
+        if (rp.g) {
+            // in the tail stage the q = 1 lanes take the first 16 gains
+            const cgp g = (cgp)rp.g + kb + 8 * kh;
+            g0n = *(const __attribute__((address_space(4))) f32x8*)g;
+            g1n = *(const __attribute__((address_space(4))) f32x8*)(g + (tl ? 0 : 16));
+        } else {
+            g0n = 1.0f;
+            g1n = 1.0f;
+        }
+    };
     __syncthreads();                        // inv_rms visible
+    load_g(0);
 #pragma unroll
     for (int s0 = 0; s0 < kStages - 1; s0++)
         if (s0 < nk) issue(s0, s0);
@@ -251,25 +304,19 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
         if (kStages == 3 && kt + 1 < nk) wait_vmcnt<kDma>();
         else wait_vmcnt<0>();
         bare_barrier();
+        const bool dead = tail16 && kt == nk - 1 && q == 0;
+        const f32x8 gq = q ? g1n : g0n;
+        float gs[8];
+#pragma unroll
+        for (int s2 = 0; s2 < 8; s2++) gs[s2] = dead ? 0.0f : gq[s2];
         {
-            const int nb = buf == 0 ? kStages - 1 : buf - 1;   // slot of stage kt-1
-            if (kt + kStages - 1 < nk) issue(kt + kStages - 1, nb);
+            // into the slot of stage kt-1; past the last stage the DMAs re-read
+            // it into a slot nothing reads any more
+            const int nb = buf == 0 ? kStages - 1 : buf - 1;
+            issue(min(kt + kStages - 1, nk - 1), nb);
         }
         const char* st = lds + buf * kStageBytes;
         buf = buf + 1 == kStages ? 0 : buf + 1;
-        const int kb = kt * kKS;
-
-        // this wave's eight MFMA steps s = 8 kh .. 8 kh + 7 use K values
-        // kb + 16 q + 8 kh + s; g for them (scalar loads of the stage's values)
-        const bool dead = tail16 && kt == nk - 1 && q == 1;
-        float gs[8];
-#pragma unroll
-        for (int s2 = 0; s2 < 8; s2++) {
-            const float g0 = rp.g ? rp.g[kb + 8 * kh + s2] : 1.0f;
-            const float g1 = (rp.g && !(tail16 && kt == nk - 1)) ? rp.g[kb + 16 + 8 * kh + s2]
-                                                                  : 1.0f;
-            gs[s2] = dead ? 0.0f : (q ? g1 : g0);
-        }
         // this lane's 8 values of its h row
         float a[8];
         if (kInB == 4) {
@@ -303,6 +350,8 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
                     acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s2], b[s2], acc[i], 0, 0, 0);
             }
         }
+        // the next stage's gains, once this stage's MFMAs are issued
+        load_g(min(kt + 1, nk - 1));
     }
     __syncthreads();
 

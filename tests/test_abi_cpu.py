@@ -44,7 +44,7 @@ def test_status_strings(lib):
     assert lib.moe_abi_version() == 1
 
 
-def _route(lib, T=4, d=16, E=8, k=2, h=1, W=1, ids=1, w=1, hdt=0):
+def _route(lib, T=4, d=32, E=8, k=2, h=1, W=1, ids=1, w=1, hdt=0):
     vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
     lib.moe_route.argtypes = [vp, C.c_int, i64, i64, vp, C.c_float, i32, vp, vp, i32, i32, vp,
                               C.c_int, vp, vp, vp, vp]
@@ -58,6 +58,7 @@ def test_route_rejects_bad_arguments(lib):
     assert _route(lib, E=513) == 2        # E above the limit
     assert _route(lib, k=17, E=64) == 2   # k above 16
     assert _route(lib, d=24) == 2         # d_r not a multiple of 16
+    assert _route(lib, d=16) == 2         # d_r below 32
     assert _route(lib, h=0) == 1          # null input
     assert _route(lib, hdt=7) == 3        # bad dtype
     assert _route(lib, T=0, h=0, W=0, ids=0, w=0) == 0   # nothing to do

@@ -36,7 +36,7 @@ def _rms(a):
 # ---------------------------------------------------------------- route ----
 
 ROUTE_SHAPES = [  # T, d_r, E, k
-    (1, 16, 1, 1),
+    (1, 32, 1, 1),          # narrowest router width
     (33, 64, 16, 2),        # ragged token tile
     (65, 48, 130, 3),       # K = 1.5 stages (a 16-value tail), E just over a 128 multiple
     (40, 80, 256, 5),       # K = 2.5 stages
@@ -67,8 +67,8 @@ def test_route_topk_bit_exact_on_exact_logits(M, T, d, E, k, hdt):
 
 
 def test_route_signed_zero_and_ties(M):
-    h = torch.ones((1, 16), dtype=torch.float32)
-    W = torch.zeros((8, 16))
+    h = torch.ones((1, 32), dtype=torch.float32)
+    W = torch.zeros((8, 32))
     W[3, 0] = -0.0
     W[5, 0] = 1.0
     W[6, 0] = 1.0
