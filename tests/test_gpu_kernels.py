@@ -209,6 +209,10 @@ def _group_counts(rng, E, kind, scale):
     ("bf16", 3, 64, 64, "uniform", 300),       # one K step in both GEMMs
     ("bf16", 4, 128, 192, "skewed", 200),      # two and three K steps
     ("f32", 3, 32, 64, "uniform", 90),         # one and two K steps in float32
+    # two or more row tiles per expert on average: the GEMMs run A's K steps ahead
+    ("bf16", 2, 128, 128, "uniform", 700),     # 2.7 tiles per expert, ragged
+    ("bf16", 4, 256, 256, "uniform", 600),     # four K steps
+    ("f32", 3, 64, 96, "skewed", 300),         # one expert five times the others
 ])
 def test_grouped_ffn_parity(M, dt, E, d, H, kind, scale):
     rng = np.random.default_rng(E * d + H)
