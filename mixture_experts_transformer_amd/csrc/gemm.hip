@@ -18,16 +18,19 @@
 // instructions).  A K step is 128 bytes -- one whole cache line -- of each of the
 // 256 A rows and 256 B rows (64 KB): with 64-byte row pieces every DMA
 // instruction would touch half of each of 16 lines and the L2-to-LDS rate
-// halves.  A's steps alternate in two LDS slots and B's (the weights, streamed
-// from HBM in the grouped GEMMs) rotate through three, so B runs two steps
-// ahead: all 160 KB of LDS.  The fragments of a K step are read in four
-// quarters, each while the MFMAs of the previous quarter run, so the barrier at
-// the end of a step finds its slots fully read and they are refilled at once.  Within a row the eight 16-byte chunks are
-// XOR-swizzled by a function of the row, chosen so that the fragment reads of 8
-// (or 16) consecutive rows hit distinct banks; the swizzle is applied on the
-// global side, since each DMA instruction fills 1 KB of LDS contiguously.  Each
-// DMA source is a wave-uniform base plus a 32-bit per-lane offset.  Waits are
-// explicit (vmcnt) followed by a bare s_barrier.
+// halves.  One operand's steps rotate through three LDS slots and run two steps
+// ahead, the other's alternate in two: all 160 KB of LDS.  The host picks the
+// operand per launch -- the one whose slices come from farthest away: B (the
+// weights) where a grouped GEMM streams each expert's weights once, A otherwise.
+// The fragments of a K step are read in four quarters, each while the MFMAs of
+// the previous quarter run, so the barrier at the end of a step finds its slots
+// fully read and they are refilled at once.  Within a row the eight 16-byte
+// chunks are XOR-swizzled by a function of the row, chosen so that the fragment
+// reads of 8 (or 16) consecutive rows hit distinct banks; the swizzle is applied
+// on the global side, since each DMA instruction fills 1 KB of LDS contiguously.
+// Each DMA source is a wave-uniform base plus a 32-bit per-lane offset.  Waits
+// are explicit (vmcnt) followed by a bare s_barrier.  The grouped GEMMs' outputs
+// can be stored non-temporally (they are re-read from HBM by the next kernel).
 //
 // Each wave owns up to 4 x 2 blocks of v_mfma_f32_32x32x16_bf16 (a 128 x 64
 // sub-tile, 128 accumulators).  The wave's 32-row blocks are interleaved (wm,
