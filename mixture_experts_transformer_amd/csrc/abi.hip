@@ -59,14 +59,17 @@ int64_t dense_tiles(int64_t rows, int64_t N, int epi) {
 
 // Row tiles per swizzle group.  An XCD's 32 CUs work on consecutive tiles in
 // near lockstep along K, so with 8 row tiles per group each B slice is shared by
-// 8 concurrent tiles and each A slice by 4 (dense GEMMs).  Grouped GEMMs keep
-// the row tiles of one expert's weight slices together and walk the columns
-// innermost, so the expert's rows stay in L2 across its column tiles while its
-// weights stream past.  Measured faster than grouping by 8 both at the 535B
-// shape, where an expert has one row tile, and on the 6-expert receiver pool,
-// where it has dozens (3.17 vs 3.38 ms for the pool's two grouped GEMMs).
+// 8 concurrent tiles and each A slice by 4 (dense GEMMs).  Grouped GEMMs whose
+// experts have few row tiles keep one row tile and walk the columns innermost,
+// so the expert's rows stay in L2 across its column tiles while its weights
+// stream past: faster than groups of 8 at the 535B shape (one row tile per
+// expert) and at 65,536 tokens (about five; gate/up GEMM 19.7 vs 20.5 ms).
+// Experts with many row tiles (the 6-expert receiver pool, about 43 each) take
+// groups of 8 as the dense GEMMs do (pool FFN 3.00 vs 3.02 ms, three rounds).
 constexpr int kGroupDense = 8;
-constexpr int kGroupGrouped = 1;
+constexpr int kGroupGroupedFew = 1;
+constexpr int kGroupGroupedMany = 8;
+constexpr int kManyTilesPerExpert = 16;
 
 GemmParams gemm_base() {
     GemmParams p;
@@ -87,6 +90,11 @@ int grouped_a_ahead(int64_t R_rows, int E) {
     return R_rows >= (int64_t)2 * gemm_block_m() * E ? 1 : 0;
 }
 
+int grouped_group_m(int64_t R_rows, int E) {
+    return R_rows >= (int64_t)kManyTilesPerExpert * gemm_block_m() * E ? kGroupGroupedMany
+                                                                       : kGroupGroupedFew;
+}
+
 // The grouped GEMMs' outputs (the expert hidden and output rows, hundreds of MB
 // at the 535B shape) are read back from HBM by the next kernel anyway, so they
 // are written non-temporally (down GEMM 1.72 -> 1.66 ms, gate/up 3.23 -> 3.19 ms
@@ -102,7 +110,7 @@ moe_status grouped_ffn_impl(const void* X, int64_t ldx, const int32_t* a_rows, i
                             const void* W_d, int64_t d, int64_t H, moe_dtype dt, void* h,
                             void* Y, hipStream_t s) {
     GemmParams p = gemm_base();
-    p.group_m = kGroupGrouped;
+    p.group_m = grouped_group_m(R_rows, E);
     p.a_ahead = grouped_a_ahead(R_rows, E);
     p.nt_store = kGroupedNtStore;
     p.a_src_rows = a_src_rows;
@@ -126,7 +134,7 @@ moe_status grouped_down_impl(const void* h, const int32_t* offsets, const int32_
                              int E, int64_t R_rows, const void* W_d, int64_t d, int64_t H,
                              moe_dtype dt, void* Y, hipStream_t s) {
     GemmParams p = gemm_base();
-    p.group_m = kGroupGrouped;
+    p.group_m = grouped_group_m(R_rows, E);
     p.a_ahead = grouped_a_ahead(R_rows, E);
     p.nt_store = kGroupedNtStore;
     p.offsets = offsets;

@@ -213,6 +213,8 @@ def _group_counts(rng, E, kind, scale):
     ("bf16", 2, 128, 128, "uniform", 700),     # 2.7 tiles per expert, ragged
     ("bf16", 4, 256, 256, "uniform", 600),     # four K steps
     ("f32", 3, 64, 96, "skewed", 300),         # one expert five times the others
+    # 16 or more row tiles per expert: tiles swizzled in groups of 8 row tiles
+    ("bf16", 2, 64, 64, "uniform", 4200),
 ])
 def test_grouped_ffn_parity(M, dt, E, d, H, kind, scale):
     rng = np.random.default_rng(E * d + H)
