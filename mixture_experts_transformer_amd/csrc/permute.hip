@@ -177,25 +177,21 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t 
     row_src[row] = (int32_t)a;
 }
 
-// One wave per kept destination row: copy the source row in 16-byte chunks.
-// One wave per kept row.  Each pass issues the loads of 8 16-byte chunks per
+// Row copy when each source row feeds one assignment (src_div == 1): one wave
+// per kept destination row.  Each pass issues the loads of 8 16-byte chunks per
 // lane before any store, so a wave keeps 8 KB in flight; lanes past the row's
-// end re-read its last chunk and store nothing.  Destination rows are written
-// once and stored non-temporally; source rows are read non-temporally only when
-// each is read once (NT_SRC: src_div == 1), since a source row gathered for
-// several assignments should stay in cache between its reads.
+// end re-read its last chunk and store nothing.  Every row is read once and
+// written once, so loads and stores are both non-temporal.
 constexpr int kCopyChunks = 8;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <bool NT_SRC>
 __global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E, int64_t R_phys,
                                                    const int32_t* row_src, const char* src,
-                                                   char* dst, int64_t row_bytes, int src_div) {
+                                                   char* dst, int64_t row_bytes) {
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (r >= R_phys || r >= offsets[E]) return;
-    const int64_t a = row_src[r];
-    const char* s = src + (a / src_div) * row_bytes;
+    const char* s = src + (int64_t)row_src[r] * row_bytes;
     char* d = dst + r * row_bytes;
     const int64_t nchunk = row_bytes / 16;
     for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * kCopyChunks) {
@@ -203,13 +199,55 @@ __global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E
 #pragma unroll
         for (int q = 0; q < kCopyChunks; q++) {
             const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
-            if constexpr (NT_SRC) v[q] = __builtin_nontemporal_load((const u32x4*)(s + c * 16));
-            else v[q] = *(const u32x4*)(s + c * 16);
+            v[q] = __builtin_nontemporal_load((const u32x4*)(s + c * 16));
         }
 #pragma unroll
         for (int q = 0; q < kCopyChunks; q++) {
             const int64_t c = c0 + lane + 64 * q;
             if (c < nchunk) __builtin_nontemporal_store(v[q], (u32x4*)(d + c * 16));
+        }
+    }
+}
+
+// One wave per source row, for source rows shared by several assignments
+// (src_div > 1): the row is loaded once and stored to the destination row of
+// each of its kept assignments, so each source byte crosses HBM once rather
+// than once per assignment.  Lane j of a block of 64 assignments holds the
+// row of assignment a0 + jb + j; a source row none of whose assignments was
+// kept is not read.  Each kept row has exactly one assignment, so this writes
+// the same rows as the gather above.
+__global__ __launch_bounds__(256) void scatter_copy_kernel(const int32_t* slot_row, int64_t n,
+                                                           int64_t n_src, const char* src,
+                                                           char* dst, int64_t row_bytes,
+                                                           int src_div) {
+    const int lane = threadIdx.x & 63;
+    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (s >= n_src) return;
+    const int64_t a0 = s * src_div;
+    const int64_t na = min((int64_t)src_div, n - a0);
+    const char* sp = src + s * row_bytes;
+    const int64_t nchunk = row_bytes / 16;
+    for (int64_t jb = 0; jb < na; jb += 64) {
+        const int32_t my = jb + lane < na ? slot_row[a0 + jb + lane] : -1;
+        const uint64_t kept = __ballot(my >= 0);
+        if (!kept) continue;
+        for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * kCopyChunks) {
+            u32x4 v[kCopyChunks];
+#pragma unroll
+            for (int q = 0; q < kCopyChunks; q++) {
+                const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
+                v[q] = __builtin_nontemporal_load((const u32x4*)(sp + c * 16));
+            }
+            for (uint64_t m = kept; m; m &= m - 1) {
+                const int j = __builtin_ctzll(m);
+                const int64_t r = __builtin_amdgcn_readlane(my, j);
+                char* d = dst + r * row_bytes;
+#pragma unroll
+                for (int q = 0; q < kCopyChunks; q++) {
+                    const int64_t c = c0 + lane + 64 * q;
+                    if (c < nchunk) __builtin_nontemporal_store(v[q], (u32x4*)(d + c * 16));
+                }
+            }
         }
     }
 }
@@ -247,14 +285,16 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                            row_src);
     }
     if (src && R_phys > 0) {
-        if (src_div == 1)
-            hipLaunchKernelGGL(copy_kernel<true>, dim3((unsigned)((R_phys + 3) / 4)), dim3(256),
+        if (src_div == 1) {
+            hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((R_phys + 3) / 4)), dim3(256),
                                0, s, offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
+                               width * elem_bytes);
+        } else if (n > 0) {
+            const int64_t n_src = (n + src_div - 1) / src_div;
+            hipLaunchKernelGGL(scatter_copy_kernel, dim3((unsigned)((n_src + 3) / 4)), dim3(256),
+                               0, s, slot_row, n, n_src, (const char*)src, (char*)dst,
                                width * elem_bytes, src_div);
-        else
-            hipLaunchKernelGGL(copy_kernel<false>, dim3((unsigned)((R_phys + 3) / 4)), dim3(256),
-                               0, s, offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
-                               width * elem_bytes, src_div);
+        }
     }
     return hipGetLastError();
 }

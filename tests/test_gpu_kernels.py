@@ -171,17 +171,30 @@ def test_permute_bit_exact(M, case):
     assert int(out["n_dropped"].item()) == ref["n_dropped"]
 
 
-@pytest.mark.parametrize("dt,width,div", [("bf16", 3072, 8), ("f32", 128, 2), ("bf16", 64, 1)])
-def test_permute_row_copy(M, dt, width, div):
-    rng = np.random.default_rng(width)
-    n, E = 4000, 24
+@pytest.mark.parametrize("dt,width,div,n,E,cap,pad", [
+    ("bf16", 3072, 8, 4000, 24, -1, 0.0),      # one source row per token, k = 8
+    ("f32", 128, 2, 4000, 24, -1, 0.0),
+    ("bf16", 64, 1, 4000, 24, -1, 0.0),        # one source row per assignment
+    ("bf16", 3072, 8, 4003, 24, -1, 0.0),      # last source row has 3 assignments
+    ("bf16", 256, 3, 6000, 16, 200, 0.1),      # capacity drops and padding ids
+    ("f32", 64, 70, 7000, 5, -1, 0.3),         # more than 64 assignments per source row
+    ("bf16", 128, 4, 4096, 8, 0, 0.0),         # capacity 0: nothing kept, nothing copied
+])
+def test_permute_row_copy(M, dt, width, div, n, E, cap, pad):
+    rng = np.random.default_rng(width + n)
     ids = rng.integers(0, E, n).astype(np.int32)
-    src = torch.randn((n // div, width), generator=torch.Generator().manual_seed(1)).to(TDT[dt])
+    ids[rng.random(n) < pad] = -1
+    n_src = -(-n // div)
+    src = torch.randn((n_src, width), generator=torch.Generator().manual_seed(1)).to(TDT[dt])
     dst = torch.full((n, width), -7.0, dtype=TDT[dt], device=DEV)
-    M.moe_permute(torch.from_numpy(ids).to(DEV), E, src=src.to(DEV), src_div=div, dst=dst)
+    M.moe_permute(torch.from_numpy(ids).to(DEV), E, capacity=cap, src=src.to(DEV), src_div=div,
+                  dst=dst)
     torch.cuda.synchronize()
-    ref = O.permute(ids, E)
-    assert torch.equal(dst.cpu(), src[torch.from_numpy(ref["row_src"] // div).long()])
+    ref = O.permute(ids, E, capacity=cap, R_phys=n)
+    kept = int(ref["offsets"][-1])
+    got = dst.cpu()
+    assert torch.equal(got[:kept], src[torch.from_numpy(ref["row_src"][:kept] // div).long()])
+    assert bool((got[kept:] == -7.0).all()), "rows past the kept total were written"
 
 
 # ----------------------------------------------------------- grouped FFN ----
