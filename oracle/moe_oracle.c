@@ -1,6 +1,7 @@
 /*
  * moe_oracle.c -- plain, slow, obviously-correct CPU oracle for the forward pass
- * of one routed mixture-of-experts layer.
+ * of one routed mixture-of-experts layer, and for the backward of its grouped
+ * expert matmuls and gated expert MLP.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  The GPU library never
@@ -32,6 +33,10 @@
  *     is an ordered gather, summed in a fixed order, not an atomic scatter-add.
  *   - same summary (hero-run engineering): capacity is an integer computation
  *     so that it can never exceed the buffer by a row.
+ *   - Marin: Week of April 26th summary, the paragraph on moving the backward
+ *     pass onto Triton: the grouped matmul's backward is an input-gradient
+ *     grouped GEMM against the transposed weights plus a ragged-contracting
+ *     weight-gradient GEMM.
  * Readings where the pages are silent (router input, tie rule, capacity rounding,
  * gate/up halves, eps) are stated next to the function that takes them.
  *
@@ -316,6 +321,132 @@ void moe_ref_expert_rows(const void *X, int dt, int64_t n, int64_t d, int64_t H,
         free(x);
         free(h);
     }
+}
+
+/* ------------------------------------------------- backward of the experts --- */
+
+/* The backward of a grouped matmul, as the pages split it (Marin: Week of April
+ * 26th summary, the paragraph on moving the backward pass onto Triton with a
+ * custom VJP: one kernel for the input gradient with the grouped right-hand side
+ * transposed, a separate ragged-contracting kernel for the weight gradient).  The forward is Z[r] = W[e(r)] X[r] for the rows r of
+ * group e = [offsets[e], offsets[e+1]), W [E, N, K], X [R, K], Z [R, N]; for a
+ * scalar loss with dZ = dLoss/dZ:
+ *   dX[r, k]    = sum over n = 0..N-1 (ascending) of dZ[r, n] * W[e(r)][n, k]
+ *   dW[e][n, k] = sum over rows r of group e (ascending) of dZ[r, n] * X[r, k]
+ * Inputs in dt, sums in double, results unrounded.  Rows r >= offsets[E] of dX
+ * are not written; an empty group's dW is zero. */
+void moe_ref_ragged_dlhs(const void *dZ, const void *W, int dt, const int32_t *offsets,
+                         int32_t E, int64_t N, int64_t K, double *dX)
+{
+    for (int32_t e = 0; e < E; e++) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; r++) {
+            for (int64_t k = 0; k < K; k++) {
+                double s = 0.0;
+                for (int64_t n = 0; n < N; n++)
+                    s += ld(dZ, dt, r * N + n) * ld(W, dt, ((int64_t)e * N + n) * K + k);
+                dX[r * K + k] = s;
+            }
+        }
+    }
+}
+
+void moe_ref_ragged_drhs(const void *X, const void *dZ, int dt, const int32_t *offsets,
+                         int32_t E, int64_t N, int64_t K, double *dW)
+{
+    for (int32_t e = 0; e < E; e++) {
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < N; n++) {
+            for (int64_t k = 0; k < K; k++) {
+                double s = 0.0;
+                for (int64_t r = offsets[e]; r < offsets[e + 1]; r++)
+                    s += ld(dZ, dt, r * N + n) * ld(X, dt, r * K + k);
+                dW[((int64_t)e * N + n) * K + k] = s;
+            }
+        }
+    }
+}
+
+/* Backward of the gated expert MLP of expert_row for the rows of each group
+ * (rows r of group e use expert e; rows >= offsets[E] take no part), given the
+ * gradient dY [R, d] of its output.  The forward is recomputed row by row:
+ *   g = W_gate x, u = W_up x (rows [0, H) and [H, 2H) of W_gu), h = silu(g) u
+ *   stored in dt as the forward stores it, y = W_d h.
+ * Chain rule, with silu'(v) = s (1 + v (1 - s)), s = 1 / (1 + exp(-v)), and the
+ * storage rounding of h taken as the identity (it has no derivative):
+ *   dh = W_d^T dy;  dg = dh * u * silu'(g);  du = dh * silu(g)
+ *   dx = W_gate^T dg + W_up^T du
+ *   dW_d[e]  = sum over the group's rows (ascending) of dy h^T      [d, H]
+ *   dW_gu[e] = sum over the group's rows (ascending) of [dg; du] x^T [2H, d]
+ * All in double; dX [R, d], dW_gu [E, 2H, d], dW_d [E, d, H] unrounded. */
+static void expert_row_grad(const double *x, const double *dy, int64_t d, int64_t H,
+                            const void *W_gu, const void *W_d, int dt, double *h,
+                            double *dgu, double *dx)
+{
+    for (int64_t i = 0; i < H; i++) {
+        double g = 0.0, u = 0.0, dh = 0.0;
+        for (int64_t c = 0; c < d; c++) {
+            g += ld(W_gu, dt, i * d + c) * x[c];
+            u += ld(W_gu, dt, (H + i) * d + c) * x[c];
+        }
+        for (int64_t o = 0; o < d; o++)
+            dh += ld(W_d, dt, o * H + i) * dy[o];
+        double s = 1.0 / (1.0 + exp(-g));
+        double silu = g / (1.0 + exp(-g));
+        h[i] = store_as(silu * u, dt);
+        dgu[i] = dh * u * (s * (1.0 + g * (1.0 - s)));
+        dgu[H + i] = dh * silu;
+    }
+    for (int64_t c = 0; c < d; c++) {
+        double s = 0.0;
+        for (int64_t i = 0; i < 2 * H; i++)
+            s += ld(W_gu, dt, i * d + c) * dgu[i];
+        dx[c] = s;
+    }
+}
+
+void moe_ref_expert_rows_bwd(const void *X, const void *dY, int dt, const int32_t *offsets,
+                             int32_t E, int64_t d, int64_t H, const void *W_gu,
+                             const void *W_d, double *dX, double *dW_gu, double *dW_d)
+{
+    const int64_t R = offsets[E];
+    double *hh = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1) * (size_t)H);
+    double *gg = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1) * (size_t)(2 * H));
+    for (int32_t e = 0; e < E; e++) {
+        const void *Wg = (const char *)W_gu + (size_t)e * (size_t)(2 * H * d) * (dt == DT_BF16 ? 2 : 4);
+        const void *Wd = (const char *)W_d + (size_t)e * (size_t)(d * H) * (dt == DT_BF16 ? 2 : 4);
+#pragma omp parallel for schedule(dynamic, 1)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; r++) {
+            double *x = (double *)malloc(sizeof(double) * (size_t)d);
+            double *dy = (double *)malloc(sizeof(double) * (size_t)d);
+            for (int64_t c = 0; c < d; c++) {
+                x[c] = ld(X, dt, r * d + c);
+                dy[c] = ld(dY, dt, r * d + c);
+            }
+            expert_row_grad(x, dy, d, H, Wg, Wd, dt, hh + r * H, gg + r * 2 * H, dX + r * d);
+            free(x);
+            free(dy);
+        }
+        /* weight gradients: each element sums its group's rows in ascending order */
+#pragma omp parallel for schedule(static)
+        for (int64_t o = 0; o < d; o++)
+            for (int64_t i = 0; i < H; i++) {
+                double s = 0.0;
+                for (int64_t r = offsets[e]; r < offsets[e + 1]; r++)
+                    s += ld(dY, dt, r * d + o) * hh[r * H + i];
+                dW_d[((int64_t)e * d + o) * H + i] = s;
+            }
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < 2 * H; i++)
+            for (int64_t c = 0; c < d; c++) {
+                double s = 0.0;
+                for (int64_t r = offsets[e]; r < offsets[e + 1]; r++)
+                    s += gg[r * 2 * H + i] * ld(X, dt, r * d + c);
+                dW_gu[((int64_t)e * 2 * H + i) * d + c] = s;
+            }
+    }
+    free(hh);
+    free(gg);
 }
 
 /* Weighted combine, ordered gather: c_t = sum over j = 0..k-1 (ascending) of

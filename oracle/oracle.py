@@ -67,6 +67,10 @@ def lib():
             L.moe_ref_permute.argtypes = [vp, i64, i32, i64, vp, vp, vp, vp, i64, vp]
             L.moe_ref_expert_rows.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, vp, vp]
             L.moe_ref_combine.argtypes = [vp, C.c_int, vp, vp, i64, i32, i64, vp]
+            L.moe_ref_ragged_dlhs.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
+            L.moe_ref_ragged_drhs.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
+            L.moe_ref_expert_rows_bwd.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp, vp,
+                                                  vp, vp, vp]
             L.moe_ref_route_tokens.argtypes = [C.POINTER(Dims), C.POINTER(Weights), vp, vp, i64,
                                                vp, vp, vp, vp, vp]
             L.moe_ref_output_tokens.argtypes = [C.POINTER(Dims), C.POINTER(Weights), vp, vp, i64,
@@ -177,6 +181,55 @@ def expert_rows(X, expert, W_gu_e, W_d_e, H: int, want_h: bool = False):
     lib().moe_ref_expert_rows(_p(X), dt, n, d, H, _p(expert), C.cast(gu_ptrs, C.c_void_p),
                               C.cast(d_ptrs, C.c_void_p), _p(Y), _p(h))
     return (Y, h) if want_h else Y
+
+
+def ragged_dlhs(dZ, W, offsets):
+    """Input gradient of the grouped matmul Z[r] = W[e(r)] X[r]: dZ [R, N], W [E, N, K]
+    (float32 or bf16 bits) -> dX [R, K] float64; rows >= offsets[E] are NaN (unwritten)."""
+    dZ, W = np.ascontiguousarray(dZ), np.ascontiguousarray(W)
+    dt = _dt_of(dZ)
+    assert W.dtype == dZ.dtype
+    E, N, K = W.shape
+    off = _c(offsets, np.int32)
+    assert off.shape == (E + 1,) and dZ.shape[1] == N and off[-1] <= dZ.shape[0]
+    dX = np.full((dZ.shape[0], K), np.nan)
+    lib().moe_ref_ragged_dlhs(_p(dZ), _p(W), dt, _p(off), E, N, K, _p(dX))
+    return dX
+
+
+def ragged_drhs(X, dZ, offsets):
+    """Weight gradient of the grouped matmul: X [R, K], dZ [R, N] -> dW [E, N, K] float64."""
+    X, dZ = np.ascontiguousarray(X), np.ascontiguousarray(dZ)
+    dt = _dt_of(X)
+    assert dZ.dtype == X.dtype
+    off = _c(offsets, np.int32)
+    E = off.size - 1
+    N, K = dZ.shape[1], X.shape[1]
+    assert off[-1] <= min(X.shape[0], dZ.shape[0])
+    dW = np.empty((E, N, K))
+    lib().moe_ref_ragged_drhs(_p(X), _p(dZ), dt, _p(off), E, N, K, _p(dW))
+    return dW
+
+
+def expert_rows_bwd(X, dY, offsets, W_gu, W_d):
+    """Backward of the gated expert MLP over row groups.  X, dY [R, d]; W_gu [E, 2H, d];
+    W_d [E, d, H] (float32 or bf16 bits) -> (dX [R, d], dW_gu [E, 2H, d], dW_d [E, d, H])
+    float64; dX rows >= offsets[E] are NaN (unwritten)."""
+    X, dY = np.ascontiguousarray(X), np.ascontiguousarray(dY)
+    W_gu, W_d = np.ascontiguousarray(W_gu), np.ascontiguousarray(W_d)
+    dt = _dt_of(X)
+    assert dY.dtype == X.dtype == W_gu.dtype == W_d.dtype
+    off = _c(offsets, np.int32)
+    E = off.size - 1
+    d = X.shape[1]
+    H = W_d.shape[2]
+    assert W_gu.shape == (E, 2 * H, d) and W_d.shape == (E, d, H) and dY.shape[1] == d
+    dX = np.full((X.shape[0], d), np.nan)
+    dWgu = np.empty((E, 2 * H, d))
+    dWd = np.empty((E, d, H))
+    lib().moe_ref_expert_rows_bwd(_p(X), _p(dY), dt, _p(off), E, d, H, _p(W_gu), _p(W_d),
+                                  _p(dX), _p(dWgu), _p(dWd))
+    return dX, dWgu, dWd
 
 
 def combine(Y, slot_row, w, T: int, k: int):
