@@ -138,6 +138,55 @@ moe_status moe_grouped_ffn(const void *X, const int32_t *offsets, int32_t E, int
                            moe_dtype dt, void *Y, void *ws, size_t ws_bytes, moe_stream stream);
 size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt);
 
+/* ------------------------------------------------------- ragged dot VJP -- */
+/* Backward of the grouped matmul (the pages' ragged_dot), split as the pages
+ * split their custom VJP (Marin: Week of April 26th summary, the paragraph on
+ * moving the backward pass onto Triton): an input-gradient kernel with the
+ * grouped right-hand side transposed and a separate ragged-contracting kernel
+ * for the weight gradient.  The forward convention is this library's:
+ *   Z[r] = W[e] X[r]  for the rows r of group e = [offsets[e], offsets[e+1]),
+ *   X [R_phys, K], W [E, N, K] (each group's matrix output-major), Z [R_phys, N].
+ * Accumulation is float32.
+ *
+ * moe_ragged_dot_dlhs:  dX[r] = W[e]^T dZ[r], i.e. dX[r, k] = sum_n dZ[r, n] W[e][n, k]
+ *   dZ (device) [R_phys, N] dt;  W (device) [E, N, K] dt;  dX (device) [R_phys, K] dt.
+ *   Rows >= offsets[E] of dX are not touched.
+ *   ws (device) moe_ragged_dot_dlhs_workspace_size(E) bytes (the row-tile prefix).
+ * moe_ragged_dot_drhs:  dW[e] = sum over the rows r of group e of dZ[r] X[r]^T
+ *   X (device) [R_phys, K] dt;  dZ (device) [R_phys, N] dt;  dW (device) [E, N, K]
+ *   in dw_dt (dt or MOE_F32).  An empty group's dW[e] is written as zeros; no
+ *   workspace.
+ * Both: offsets (device) [E+1] int32 ascending, offsets[0] = 0, offsets[E] <=
+ * R_phys.  Limits: N and K multiples of 64 for MOE_BF16 and of 32 for MOE_F32,
+ * 1 <= E <= 1024, R_phys < 2^31; otherwise MOE_ESHAPE.  Pointers 16-byte
+ * aligned (MOE_EALIGN).  Nothing is allocated; work is enqueued on `stream`. */
+moe_status moe_ragged_dot_dlhs(const void *dZ, const int32_t *offsets, int32_t E, int64_t R_phys,
+                               const void *W, int64_t N, int64_t K, moe_dtype dt, void *dX,
+                               void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_ragged_dot_dlhs_workspace_size(int32_t E);
+moe_status moe_ragged_dot_drhs(const void *X, const void *dZ, const int32_t *offsets, int32_t E,
+                               int64_t R_phys, int64_t N, int64_t K, moe_dtype dt, void *dW,
+                               moe_dtype dw_dt, moe_stream stream);
+
+/* Backward of moe_grouped_ffn (the gated expert MLP over row groups; the same
+ * VJP pieces as above, chained through SwiGLU's derivative).  Given the
+ * gradient dY of Y:
+ *   [g | u] = W_gu[e] x  (recomputed),  h = silu(g) u,  dh = W_d[e]^T dy,
+ *   dg = dh u silu'(g),  du = dh silu(g),  silu'(g) = s (1 + g (1 - s)), s = sigmoid(g),
+ *   dx = W_gu[e]^T [dg | du],  dW_d[e] = sum dy h^T,  dW_gu[e] = sum [dg | du] x^T.
+ *   X, dY (device) [R_phys, d] dt;  W_gu [E, 2H, d], W_d [E, d, H] (dt).
+ *   dX (device) [R_phys, d] dt (rows >= offsets[E] not touched);  dW_gu [E, 2H, d]
+ *   and dW_d [E, d, H] in dw_dt (dt or MOE_F32); empty groups get zeros.
+ *   ws (device) moe_grouped_ffn_bwd_workspace_size(E, R_phys, H, dt) bytes: holds
+ *   [g | u] in float32 and [dg | du] and h in dt (both are operands of the
+ *   weight-gradient and input-gradient GEMMs, so they are rounded to dt).
+ * Limits as moe_grouped_ffn. */
+moe_status moe_grouped_ffn_bwd(const void *X, const void *dY, const int32_t *offsets, int32_t E,
+                               int64_t R_phys, const void *W_gu, const void *W_d, int64_t d,
+                               int64_t H, moe_dtype dt, void *dX, void *dW_gu, void *dW_d,
+                               moe_dtype dw_dt, void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_grouped_ffn_bwd_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt);
+
 /* ---------------------------------------------------------------- combine -- */
 /* Ordered weighted gather (Marin weekly summary of September 14: an ordered
  * gather replaced an atomic scatter-add so repeated scoring is bitwise exact):

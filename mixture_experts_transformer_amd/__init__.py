@@ -1,4 +1,5 @@
-"""MI355X-native forward pass of one routed mixture-of-experts layer.
+"""MI355X-native forward pass of one routed mixture-of-experts layer, and the
+backward of its grouped expert matmuls.
 
 The compute lives in libmoe.so (hand-written gfx950 HIP kernels behind the C ABI
 of include/moe.h); this package is its thin Python binding.  Importing it fails
@@ -6,6 +7,7 @@ loudly if the library has not been built.
 """
 from .moe import (  # noqa: F401
     LayerDesc, MoeError, abi_version, layer_desc, moe_combine, moe_grouped_ffn,
-    moe_grouped_ffn_workspace_size, moe_layer_fwd, moe_layer_workspace_size, moe_permute,
-    moe_permute_workspace_size, moe_route, status_str, MOE_COMBINE_KEEP_UNROUTED, EV_NAMES,
-    MOE_EV_COUNT)
+    moe_grouped_ffn_bwd, moe_grouped_ffn_bwd_workspace_size, moe_grouped_ffn_workspace_size,
+    moe_layer_fwd, moe_layer_workspace_size, moe_permute, moe_permute_workspace_size,
+    moe_ragged_dot_dlhs, moe_ragged_dot_drhs, moe_route, status_str, MOE_COMBINE_KEEP_UNROUTED,
+    EV_NAMES, MOE_EV_COUNT)

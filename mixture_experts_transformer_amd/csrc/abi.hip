@@ -151,6 +151,59 @@ moe_status grouped_down_impl(const void* h, const int32_t* offsets, const int32_
     return MOE_OK;
 }
 
+// Input gradient of the grouped matmul Z[r] = X[r] W[g]^T (W [G, N, K]):
+// dX[r] = dZ[r] W[g], a grouped GEMM that reads W[g] along its rows.  With
+// EPI_SWIGLU_BWD the reduction result is dh of the gated MLP (K = H columns) and
+// the epilogue turns it into [dG | dU] (C, 2H wide) and h (h_out) using the
+// forward's pre-activations gu [rows, 2H] (float32).
+moe_status dlhs_impl(const void* dZ, const int32_t* offsets, const int32_t* tile_prefix, int E,
+                     int64_t R_rows, const void* W, int64_t N, int64_t K, moe_dtype dt, int epi,
+                     void* C, int64_t ldc, const void* gu, void* h_out, hipStream_t s) {
+    GemmParams p = gemm_base();
+    p.layout = LAY_BT;
+    p.group_m = grouped_group_m(R_rows, E);
+    p.a_ahead = grouped_a_ahead(R_rows, E);
+    p.offsets = offsets;
+    p.tile_prefix = tile_prefix;
+    p.G = E;
+    p.b_group_rows = N;
+    p.N = K;
+    p.seg[0] = GemmSeg{dZ, N, W, K, (int32_t)N};
+    p.nseg = 1;
+    p.C = C;
+    p.ldc = ldc;
+    if (epi == EPI_SWIGLU_BWD) {
+        p.addend = gu;
+        p.ld_add = 2 * K;
+        p.n_per = K;
+        p.C2 = h_out;
+        p.ldc2 = K;
+    }
+    MOE_TRY(launch_gemm(p, dt, false, epi, grouped_tile_bound(R_rows, E, K, EPI_STORE), s));
+    return MOE_OK;
+}
+
+// Weight gradient of the grouped matmul: dW[g] = dZ[rows of g]^T X[rows of g],
+// [N, K] per group, the reduction running over each group's rows.
+moe_status drhs_impl(const void* X, const void* dZ, const int32_t* offsets, int E, int64_t N,
+                     int64_t K, moe_dtype dt, void* dW, bool out_f32, hipStream_t s) {
+    GemmParams p = gemm_base();
+    p.layout = LAY_DW;
+    p.group_m = 1;
+    p.offsets = offsets;
+    p.G = E;
+    p.M = N;
+    p.N = K;
+    p.seg[0] = GemmSeg{dZ, N, X, K, 0};
+    p.nseg = 1;
+    p.C = dW;
+    p.ldc = K;
+    const int64_t BM = gemm_block_m();
+    MOE_TRY(launch_gemm(p, dt, out_f32, EPI_STORE,
+                        (int64_t)E * ((N + BM - 1) / BM) * ((K + BM - 1) / BM), s));
+    return MOE_OK;
+}
+
 struct LayerBufs {
     float* z_pre;
     void* z_e;
@@ -329,6 +382,118 @@ moe_status moe_grouped_ffn(const void* X, const int32_t* offsets, int32_t E, int
                                      H, dt, h, Y, s);
     if (st != MOE_OK) return st;
     return grouped_down_impl(h, offsets, tp, E, R_phys, W_d, d, H, dt, Y, s);
+}
+
+// ------------------------------------------------- ragged dot backward ----
+size_t moe_ragged_dot_dlhs_workspace_size(int32_t E) {
+    if (E < 1) return 0;
+    return a256((size_t)(E + 1) * 4);
+}
+
+moe_status moe_ragged_dot_dlhs(const void* dZ, const int32_t* offsets, int32_t E, int64_t R_phys,
+                               const void* W, int64_t N, int64_t K, moe_dtype dt, void* dX,
+                               void* ws, size_t ws_bytes, moe_stream stream) {
+    if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (!width_ok(N, dt) || !width_ok(K, dt)) return MOE_ESHAPE;
+    if (!under4g(gemm_block_m() + 1, N, dt) || !under4g(gemm_k_bytes() + 1, K, dt))
+        return MOE_ESHAPE;
+    if (!offsets || !W || (R_phys > 0 && (!dZ || !dX))) return MOE_EINVAL;
+    const void* ptrs[] = {dZ, offsets, W, dX, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if (!ws || ws_bytes < moe_ragged_dot_dlhs_workspace_size(E)) return MOE_EWORKSPACE;
+    int32_t* tp = (int32_t*)ws;
+    hipStream_t s = hs(stream);
+    MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tp, s));
+    return dlhs_impl(dZ, offsets, tp, E, R_phys, W, N, K, dt, EPI_STORE, dX, K, nullptr, nullptr,
+                     s);
+}
+
+moe_status moe_ragged_dot_drhs(const void* X, const void* dZ, const int32_t* offsets, int32_t E,
+                               int64_t R_phys, int64_t N, int64_t K, moe_dtype dt, void* dW,
+                               moe_dtype dw_dt, moe_stream stream) {
+    if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!dt_ok(dt) || (dw_dt != dt && dw_dt != MOE_F32)) return MOE_EDTYPE;
+    if (!width_ok(N, dt) || !width_ok(K, dt)) return MOE_ESHAPE;
+    if (!under4g(gemm_k_bytes() + 1, N, dt) || !under4g(gemm_k_bytes() + 1, K, dt))
+        return MOE_ESHAPE;
+    if (!offsets || !dW || (R_phys > 0 && (!X || !dZ))) return MOE_EINVAL;
+    const void* ptrs[] = {X, dZ, offsets, dW};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    return drhs_impl(X, dZ, offsets, E, N, K, dt, dW, dw_dt == MOE_F32 && dt != MOE_F32,
+                     hs(stream));
+}
+
+// ---------------------------------------------------- grouped FFN backward ----
+size_t moe_grouped_ffn_bwd_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt) {
+    if (E < 1 || R_phys < 0 || H <= 0 || !dt_ok(dt)) return 0;
+    Carver cv(nullptr);
+    cv.take<int32_t>((size_t)(E + 1) * 4);
+    cv.take<char>((size_t)R_phys * 2 * H * 4);             // [g | u], float32
+    cv.take<char>((size_t)R_phys * 2 * H * esize(dt));     // [dg | du]
+    cv.take<char>((size_t)R_phys * H * esize(dt));         // h
+    return cv.off;
+}
+
+moe_status moe_grouped_ffn_bwd(const void* X, const void* dY, const int32_t* offsets, int32_t E,
+                               int64_t R_phys, const void* W_gu, const void* W_d, int64_t d,
+                               int64_t H, moe_dtype dt, void* dX, void* dW_gu, void* dW_d,
+                               moe_dtype dw_dt, void* ws, size_t ws_bytes, moe_stream stream) {
+    if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!dt_ok(dt) || (dw_dt != dt && dw_dt != MOE_F32)) return MOE_EDTYPE;
+    if (!width_ok(d, dt) || !width_ok(H, dt)) return MOE_ESHAPE;
+    if (!under4g(2 * H + 1, d, dt) || !under4g(d + 1, H, dt) ||
+        !under4g(gemm_block_m() + 1, 2 * H, dt))
+        return MOE_ESHAPE;
+    if (!offsets || !W_gu || !W_d || !dW_gu || !dW_d || (R_phys > 0 && (!X || !dY || !dX)))
+        return MOE_EINVAL;
+    const void* ptrs[] = {X, dY, offsets, W_gu, W_d, dX, dW_gu, dW_d, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    const size_t need = moe_grouped_ffn_bwd_workspace_size(E, R_phys, H, dt);
+    if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+    Carver cv(ws);
+    int32_t* tp = cv.take<int32_t>((size_t)(E + 1) * 4);
+    void* gu = cv.take<char>((size_t)R_phys * 2 * H * 4);
+    void* dgu = cv.take<char>((size_t)R_phys * 2 * H * esize(dt));
+    void* h = cv.take<char>((size_t)R_phys * H * esize(dt));
+    hipStream_t s = hs(stream);
+    const bool w32 = dw_dt == MOE_F32 && dt != MOE_F32;
+    MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tp, s));
+    // 1. the forward's pre-activations [g | u] = X W_gu[e]^T, kept in float32:
+    //    rounding them to bfloat16 as well as [dg | du] took the weight
+    //    gradients past the bf16 bound on ordinary inputs
+    {
+        GemmParams p = gemm_base();
+        p.group_m = grouped_group_m(R_phys, E);
+        p.a_ahead = grouped_a_ahead(R_phys, E);
+        p.offsets = offsets;
+        p.tile_prefix = tp;
+        p.G = E;
+        p.b_group_rows = 2 * H;
+        p.N = 2 * H;
+        p.seg[0] = GemmSeg{X, d, W_gu, d, (int32_t)d};
+        p.nseg = 1;
+        p.C = gu;
+        p.ldc = 2 * H;
+        MOE_TRY(launch_gemm(p, dt, true, EPI_STORE,
+                            grouped_tile_bound(R_phys, E, 2 * H, EPI_STORE), s));
+    }
+    // 2. dh = dY W_d[e]; the epilogue writes [dg | du] and h
+    moe_status st = dlhs_impl(dY, offsets, tp, E, R_phys, W_d, d, H, dt, EPI_SWIGLU_BWD, dgu,
+                              2 * H, gu, h, s);
+    if (st != MOE_OK) return st;
+    // 3. dW_d[e] = dY[rows]^T h[rows]
+    st = drhs_impl(h, dY, offsets, E, d, H, dt, dW_d, w32, s);
+    if (st != MOE_OK) return st;
+    // 4. dX = [dg | du] W_gu[e]
+    st = dlhs_impl(dgu, offsets, tp, E, R_phys, W_gu, 2 * H, d, dt, EPI_STORE, dX, d, nullptr,
+                   nullptr, s);
+    if (st != MOE_OK) return st;
+    // 5. dW_gu[e] = [dg | du][rows]^T X[rows]
+    return drhs_impl(X, dgu, offsets, E, 2 * H, d, dt, dW_gu, w32, s);
 }
 
 // -------------------------------------------------------------- combine ----

@@ -76,6 +76,28 @@ static_assert(kBM == kBN, "the DMA split assumes equal operand tiles");
 // distinct banks whether the LDS serves 8 or 16 lanes of a 16-byte read per cycle.
 __device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
+// Operands stored [reduction][column] (LAY_BT's B, both of LAY_DW's): a slot
+// holds 256 / kSubW sub-blocks of kSubW columns (128 bytes), and LDS row kk of
+// sub-block b is columns [b kSubW, (b + 1) kSubW) at reduction index kk of the
+// step.  Chunk c of that row is stored at c ^ swzT(kk): the four rows that one
+// 16-lane transpose read touches then fall on distinct banks.
+__device__ __forceinline__ int swzT(int kk) { return ((kk >> 1) & 1) << 2; }
+
+// bf16 fragment of a [reduction][column] slot: ds_read_b64_tr_b16 gives lane j
+// of each 16-lane group element j % 4 of the 8 bytes that lane 4 i + j / 4 of
+// the group points at (i = 0..3).  With the group's lanes on 4 consecutive rows
+// (4 lanes of 4 columns each per row), every lane receives 4 consecutive
+// reduction indices of one column; two reads 4 rows apart make the 8 the MFMA
+// operand holds.
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef short v8i16 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ bf16x8 tr_frag_bf16(const char* p) {
+    typedef __attribute__((address_space(3))) v4i16* lds_v4;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)p);
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p + 4 * kRowBytes));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
 // expcnt and lgkmcnt left at "no wait").
 template <int N>
@@ -146,8 +168,11 @@ __device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* C, int64_t off, con
 // AA: A's steps run two ahead in the three-slot ring (dense GEMMs, and grouped
 // ones whose weights serve several row tiles); otherwise B's do (grouped GEMMs
 // that stream each expert's weights once).
-template <typename T, typename OutT, int EPI, bool AA>
+template <typename T, typename OutT, int EPI, bool AA, int LAY>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
+    constexpr bool kAT = (LAY & 1) != 0;      // A stored [reduction][row]
+    constexpr bool kBT = (LAY & 2) != 0;      // B stored [reduction][column]
+    constexpr bool kRK = (LAY & 4) != 0;      // reduction over each group's rows
     constexpr int kSlotsA = AA ? kSlotsFar : kSlotsNear;
     constexpr int kBBase = kSlotsA * kOpBytes;             // B ring offset in LDS
     constexpr int kElem = Elem<T>::kBytes;
@@ -155,6 +180,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr int kSub = kSteps / 4;                             // k-steps per quarter step
     static_assert(kSteps % 4 == 0, "a K step splits into four quarters");
     constexpr int kColsOut = (EPI == EPI_SWIGLU) ? kBN / 2 : kBN;
+    constexpr int kKStep = kRowBytes / kElem;          // reduction indices per K step
+    constexpr int kSubW = kRowBytes / kElem;           // columns per [reduction][column] sub-block
+    constexpr int kSubBytes = kKStep * kRowBytes;      // bytes of one such sub-block
+    static_assert(!kRK || (kAT && kBT), "a row-group reduction reads both operands transposed");
 
     extern __shared__ __attribute__((aligned(16))) char lds[];
 
@@ -165,7 +194,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 
     // ---- tile space
     const int64_t n_tiles_n = (p.N + kColsOut - 1) / kColsOut;
-    const int64_t n_tiles_m = p.offsets ? (int64_t)p.tile_prefix[p.G] : (p.M + kBM - 1) / kBM;
+    int64_t n_tiles_m;
+    if constexpr (kRK) n_tiles_m = (int64_t)p.G * ((p.M + kBM - 1) / kBM);
+    else n_tiles_m = p.offsets ? (int64_t)p.tile_prefix[p.G] : (p.M + kBM - 1) / kBM;
     const int64_t total = n_tiles_m * n_tiles_n;
     const int xcd = blockIdx.x % kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
@@ -176,11 +207,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // fragment read offsets (the swizzle depends only on row % 32)
     const int fl = swz(lane & 31);
     const int rd_row = (lane & 31) * kRowBytes;
+    // Fragment offsets in a [reduction][column] slot.  bf16: the lane's offset
+    // for a 32-column block at column 0 (tro0) or 32 (tro1) of its sub-block
+    // (lanes of a 16-lane group on rows kr..kr+3, columns cp..cp+3; see
+    // tr_frag_bf16).  f32: row lane / 32 and column lane % 32 of the MFMA
+    // k-step, whose chunk swizzle alternates with the k-step's parity.
+    int tro0 = 0, tro1 = 0;
+    if constexpr (kAT || kBT) {
+        if constexpr (kElem == 2) {
+            const int j = lane & 15;
+            const int kr = 8 * (lane >> 5) + (j >> 2);
+            const int cp = 16 * ((lane >> 4) & 1) + 4 * (j & 3);
+            const int c1 = 32 + cp;
+            tro0 = kr * kRowBytes + (((cp >> 3) ^ swzT(kr)) << 4) + ((cp & 7) << 1);
+            tro1 = kr * kRowBytes + (((c1 >> 3) ^ swzT(kr)) << 4) + ((c1 & 7) << 1);
+        } else {
+            const int c = lane & 31;
+            tro0 = (lane >> 5) * kRowBytes + ((c >> 2) << 4) + ((c & 3) << 2);
+            tro1 = (lane >> 5) * kRowBytes + (((c >> 2) ^ 4) << 4) + ((c & 3) << 2);
+        }
+    }
+    // fragment of the 32-column block at m_base for MFMA k-step ks, from a
+    // [reduction][column] slot
+    auto t_frag = [&](const char* slot, int m_base, int ks) __attribute__((always_inline)) {
+        const char* q = slot + (m_base / kSubW) * kSubBytes + ks * (Mfma<T>::kK * kRowBytes);
+        if constexpr (kElem == 2) return tr_frag_bf16(q + ((m_base & 32) ? tro1 : tro0));
+        else return *(const float*)(q + ((ks & 1) ? tro1 : tro0));
+    };
 
     // ---- a tile: its rows, columns and expert
     struct Tile {
         int64_t row0, rows_valid, n0;
         int g, nrb;
+        int64_t kbeg, mc0;     // LAY_DW: first row of the group, first A column
+        int klen;              // LAY_DW: rows of the group
     };
     auto tile_at = [&](int64_t t) __attribute__((always_inline)) {
         // grouped swizzle along m
@@ -193,7 +253,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         const int64_t tn = within / gm;
         Tile tl;
         tl.g = 0;
-        if (p.offsets) {
+        tl.kbeg = 0;
+        tl.mc0 = 0;
+        tl.klen = 0;
+        if constexpr (kRK) {
+            // output rows: group g's [M, N] block of C, row tile tm % ntm
+            const int64_t ntm = (p.M + kBM - 1) / kBM;
+            tl.g = (int)(tm / ntm);
+            tl.mc0 = (tm - (int64_t)tl.g * ntm) * kBM;
+            tl.row0 = (int64_t)tl.g * p.M + tl.mc0;
+            tl.rows_valid = min((int64_t)kBM, p.M - tl.mc0);
+            tl.kbeg = p.offsets[tl.g];
+            tl.klen = p.offsets[tl.g + 1] - p.offsets[tl.g];
+        } else if (p.offsets) {
             tl.g = find_group(p.tile_prefix, p.G, (int)tm);
             const int64_t mloc = tm - p.tile_prefix[tl.g];
             tl.row0 = p.offsets[tl.g] + mloc * kBM;
@@ -223,23 +295,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++) {
             const int r = lrow + (64 / kLanesPerRow) * i;
-            // rows past the group's end read the tile's first row; their
-            // results are never stored
-            const int rl = r < tl.rows_valid ? r : 0;
-            // gathered: the source row itself; else the row within the tile
-            a_src[i] = p.a_rows ? p.a_rows[tl.row0 + rl] / p.a_div : rl;
-            int64_t col, brow;
-            if (EPI == EPI_SWIGLU) {
-                // each 64-row slice of B: [gate 32 | up 32] of 32 hidden columns
-                const int up = (r >> 5) & 1;
-                col = tl.n0 + (r >> 6) * 32 + (r & 31);
-                const int64_t zi = col / p.n_per, cc = col - zi * p.n_per;
-                brow = zi * 2 * p.n_per + cc + up * p.n_per;
-            } else {
-                col = tl.n0 + r;
-                brow = col;
+            if constexpr (!kAT) {
+                // rows past the group's end read the tile's first row; their
+                // results are never stored
+                const int rl = r < tl.rows_valid ? r : 0;
+                // gathered: the source row itself; else the row within the tile
+                a_src[i] = p.a_rows ? p.a_rows[tl.row0 + rl] / p.a_div : rl;
             }
-            b_src[i] = (int32_t)(col < p.N ? brow : 0);     // row within the group
+            if constexpr (!kBT) {
+                int64_t col, brow;
+                if (EPI == EPI_SWIGLU) {
+                    // each 64-row slice of B: [gate 32 | up 32] of 32 hidden columns
+                    const int up = (r >> 5) & 1;
+                    col = tl.n0 + (r >> 6) * 32 + (r & 31);
+                    const int64_t zi = col / p.n_per, cc = col - zi * p.n_per;
+                    brow = zi * 2 * p.n_per + cc + up * p.n_per;
+                } else {
+                    col = tl.n0 + r;
+                    brow = col;
+                }
+                b_src[i] = (int32_t)(col < p.N ? brow : 0);     // row within the group
+            }
         }
     };
     // one K segment's bases and offsets for a tile
@@ -247,6 +323,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const char* B_t = nullptr;
     int nk = 0;
     uint32_t a_off[kDmaPerOperand], b_off[kDmaPerOperand];
+    uint32_t a_off_t[kDmaPerOperand], b_off_t[kDmaPerOperand];   // LAY_DW: the last step's
+    int64_t a_step = kRowBytes, b_step = kRowBytes;              // bytes per K step
+    int kvalid = kKStep;          // LAY_DW: reduction rows of the last step
+    // Per-lane byte offset of a [reduction][column] operand's DMA into LDS row
+    // rho of a slot: sub-block rho / kKStep, reduction index rho % kKStep (read
+    // from row min(that, kmax)).  Sub-blocks at or past `ext` columns read
+    // sub-block 0; their results are never stored.
+    auto t_off = [&](int rho, int64_t ld, int64_t ext, int kmax) __attribute__((always_inline)) {
+        const int b = rho / kKStep, kk = rho % kKStep;
+        const int bb = (int64_t)b * kSubW < ext ? b : 0;
+        const int kr = kk < kmax ? kk : kmax;
+        return (uint32_t)((int64_t)kr * ld * kElem) + (uint32_t)(bb * kRowBytes) +
+               (uint32_t)((((lane % kLanesPerRow) ^ swzT(kk))) * 16);
+    };
     auto set_segment = [&](const Tile& tl, int sidx) __attribute__((always_inline)) {
         // The kernel's only argument is p, laid out at the start of the
         // kernel-argument segment; reading the selected segment from there keeps
@@ -258,33 +348,69 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         const char* B = (const char*)uniform64((int64_t)segs[sidx].B);
         const int64_t lda = uniform64(segs[sidx].lda);
         const int64_t ldb = uniform64(segs[sidx].ldb);
-        const int K = __builtin_amdgcn_readfirstlane(segs[sidx].K);
-        nk = __builtin_amdgcn_readfirstlane(K * kElem / kRowBytes);
-        const int64_t a_row_base = p.a_rows ? 0 : tl.row0;
-        const int64_t b_row_base = (int64_t)tl.g * p.b_group_rows;
-        A_t = (const char*)uniform64((int64_t)(A + a_row_base * lda * kElem));
-        B_t = (const char*)uniform64((int64_t)(B + b_row_base * ldb * kElem));
+        if constexpr (kRK) {
+            nk = __builtin_amdgcn_readfirstlane((tl.klen + kKStep - 1) / kKStep);
+            kvalid = __builtin_amdgcn_readfirstlane(tl.klen - (nk - 1) * kKStep);
+        } else {
+            const int K = __builtin_amdgcn_readfirstlane(segs[sidx].K);
+            nk = __builtin_amdgcn_readfirstlane(K * kElem / kRowBytes);
+        }
+        if constexpr (kAT) {
+            A_t = (const char*)uniform64((int64_t)(A + (tl.kbeg * lda + tl.mc0) * kElem));
+            a_step = uniform64((int64_t)kKStep * lda * kElem);
+        } else {
+            const int64_t a_row_base = p.a_rows ? 0 : tl.row0;
+            A_t = (const char*)uniform64((int64_t)(A + a_row_base * lda * kElem));
+        }
+        if constexpr (kBT) {
+            const int64_t k0 = kRK ? tl.kbeg : (int64_t)tl.g * p.b_group_rows;
+            B_t = (const char*)uniform64((int64_t)(B + (k0 * ldb + tl.n0) * kElem));
+            b_step = uniform64((int64_t)kKStep * ldb * kElem);
+        } else {
+            const int64_t b_row_base = (int64_t)tl.g * p.b_group_rows;
+            B_t = (const char*)uniform64((int64_t)(B + b_row_base * ldb * kElem));
+        }
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++) {
-            a_off[i] = (uint32_t)((int64_t)a_src[i] * lda * kElem) + chunk[i];
-            b_off[i] = (uint32_t)((int64_t)b_src[i] * ldb * kElem) + chunk[i];
+            const int rho = lrow + (64 / kLanesPerRow) * i;
+            if constexpr (kAT) {
+                a_off[i] = t_off(rho, lda, tl.rows_valid, kKStep - 1);
+                if constexpr (kRK) a_off_t[i] = t_off(rho, lda, tl.rows_valid, kvalid - 1);
+            } else {
+                a_off[i] = (uint32_t)((int64_t)a_src[i] * lda * kElem) + chunk[i];
+            }
+            if constexpr (kBT) {
+                b_off[i] = t_off(rho, ldb, p.N - tl.n0, kKStep - 1);
+                if constexpr (kRK) b_off_t[i] = t_off(rho, ldb, p.N - tl.n0, kvalid - 1);
+            } else {
+                b_off[i] = (uint32_t)((int64_t)b_src[i] * ldb * kElem) + chunk[i];
+            }
         }
     };
     char* const a_lds = lds + (wave * kDmaPerOperand) * 1024;
     char* const b_lds = lds + kBBase + (wave * kDmaPerOperand) * 1024;
     // A DMAs i0, i0+1, ... (n of them) of step kt
+    // (LAY_DW: the last step's rows past the group's end re-read its last row)
     auto issue_a = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
-        const char* const Ak = A_t + (int64_t)kt * kRowBytes;
+        const char* const Ak = A_t + (int64_t)kt * (kAT ? a_step : (int64_t)kRowBytes);
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++)
-            if (i >= i0 && i < i0 + n) dma16(Ak + a_off[i], a_lds + slot * kOpBytes + i * 1024);
+            if (i >= i0 && i < i0 + n) {
+                uint32_t o = a_off[i];
+                if constexpr (kRK) o = kt == nk - 1 ? a_off_t[i] : o;
+                dma16(Ak + o, a_lds + slot * kOpBytes + i * 1024);
+            }
     };
     // B DMAs i0, i0+1, ... (n of them) of step kt
     auto issue_b = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
-        const char* const Bk = B_t + (int64_t)kt * kRowBytes;
+        const char* const Bk = B_t + (int64_t)kt * (kBT ? b_step : (int64_t)kRowBytes);
 #pragma unroll
         for (int i = 0; i < kDmaPerOperand; i++)
-            if (i >= i0 && i < i0 + n) dma16(Bk + b_off[i], b_lds + slot * kOpBytes + i * 1024);
+            if (i >= i0 && i < i0 + n) {
+                uint32_t o = b_off[i];
+                if constexpr (kRK) o = kt == nk - 1 ? b_off_t[i] : o;
+                dma16(Bk + o, b_lds + slot * kOpBytes + i * 1024);
+            }
     };
     // the operand in the three-slot ring ("far") and the other one ("near")
     auto issue_far = [&](int kt, int slot, int i0, int n) __attribute__((always_inline)) {
@@ -303,6 +429,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     // the last step into slots nothing reads any more, which keeps the count
     // fixed.
     auto prologue = [&]() __attribute__((always_inline)) {
+        if (kRK && nk == 0) return;          // an empty group: nothing to load
         issue_far(0, 0, 0, kDmaPerOperand);
         issue_near(0, 0);
         if (nk > 1) {
@@ -352,11 +479,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 const int kb = ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
                 const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-                    fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
+                for (int j = 0; j < 2; j++) {
+                    if constexpr (kBT)
+                        fb[hs][j] = t_frag(lds + kBBase + sb * kOpBytes, wn * 64 + j * 32, ks);
+                    else
+                        fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
+                }
 #pragma unroll
-                for (int i = 0; i < NACT; i++)
-                    fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+                for (int i = 0; i < NACT; i++) {
+                    if constexpr (kAT)
+                        fa[hs][i] = t_frag(lds + sa * kOpBytes, (wm + 2 * i) * 32, ks);
+                    else
+                        fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+                }
+            }
+        };
+        // LAY_DW, last step: zero the operand elements at reduction indices past
+        // the group's end (their LDS rows hold copies of its last row)
+        auto mask_sub = [&](int q, Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
+            __attribute__((always_inline)) {
+#pragma unroll
+            for (int hs = 0; hs < kSub; hs++) {
+                const int kf = (q * kSub + hs) * Mfma<T>::kK + (lane >> 5) * Mfma<T>::kLaneK;
+                if constexpr (kElem == 2) {
+#pragma unroll
+                    for (int e = 0; e < Mfma<T>::kLaneK; e++) {
+                        if (kf + e >= kvalid) {
+#pragma unroll
+                            for (int i = 0; i < NACT; i++) fa[hs][i][e] = (__bf16)0.0f;
+#pragma unroll
+                            for (int j = 0; j < 2; j++) fb[hs][j][e] = (__bf16)0.0f;
+                        }
+                    }
+                } else {
+                    if (kf >= kvalid) {
+#pragma unroll
+                        for (int i = 0; i < NACT; i++) fa[hs][i] = 0.0f;
+#pragma unroll
+                        for (int j = 0; j < 2; j++) fb[hs][j] = 0.0f;
+                    }
+                }
             }
         };
         auto mma_sub = [&](Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
@@ -402,6 +564,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 set_segment(cur, sidx);
                 prologue();
             }
+            if (kRK && nk == 0) continue;   // an empty group: its block of C is zero
             // step 0 landed once at most step 1's loads are outstanding (the
             // previous tile's stores are older still)
             if (nk > 1) wait_vmcnt<2 * kDmaPerOperand>();
@@ -455,12 +618,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             }
             const int sa = AA ? sf : sn, sb = AA ? sn : sf;
             // last step (its first quarter is already in registers)
+            const bool tail = kRK && kvalid < kKStep;
             if (NACT > 0) {
+                if (tail) mask_sub(0, f0a, f0b);
                 load_sub(sa, sb, 1, f1a, f1b);
+                if (tail) mask_sub(1, f1a, f1b);
                 mma_sub(f0a, f0b);
                 load_sub(sa, sb, 2, f0a, f0b);
+                if (tail) mask_sub(2, f0a, f0b);
                 mma_sub(f1a, f1b);
                 load_sub(sa, sb, 3, f1a, f1b);
+                if (tail) mask_sub(3, f1a, f1b);
                 mma_sub(f0a, f0b);
                 mma_sub(f1a, f1b);
             }
@@ -500,7 +668,29 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                         for (int e = 0; e < kVec; e++)
                             vals[e] += Elem<OutT>::load((const OutT*)p.addend, aoff + e);
                     }
-                    store_vec<OutT, kVec>(C, (done.row0 + grow) * p.ldc + col, vals, nt_out);
+                    if constexpr (EPI == EPI_SWIGLU_BWD) {
+                        // vals = dh.  With the forward's pre-activations g, u
+                        // (float32): dG = dh u silu'(g), dU = dh silu(g), and
+                        // h = silu(g) u, silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g))
+                        const int64_t row = done.row0 + grow;
+                        const float* gu = (const float*)p.addend + row * p.ld_add + col;
+                        float dg[kVec], du[kVec], hv[kVec];
+#pragma unroll
+                        for (int e = 0; e < kVec; e++) {
+                            const float g = gu[e];
+                            const float u = gu[p.n_per + e];
+                            const float sg = 1.0f / (1.0f + expf(-g));
+                            const float si = silu_f(g);
+                            dg[e] = vals[e] * u * (sg * (1.0f + g * (1.0f - sg)));
+                            du[e] = vals[e] * si;
+                            hv[e] = si * u;
+                        }
+                        store_vec<OutT, kVec>(C, row * p.ldc + col, dg, nt_out);
+                        store_vec<OutT, kVec>(C, row * p.ldc + p.n_per + col, du, nt_out);
+                        store_vec<OutT, kVec>((OutT*)p.C2, row * p.ldc2 + col, hv, nt_out);
+                    } else {
+                        store_vec<OutT, kVec>(C, (done.row0 + grow) * p.ldc + col, vals, nt_out);
+                    }
                 }
             }
         };
@@ -568,20 +758,32 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* offset
 
 constexpr size_t kLdsBytes = (size_t)(kSlotsFar + kSlotsNear) * kOpBytes;   // 163,840 bytes
 
-template <typename T, typename OutT, int EPI, bool AA>
+template <typename T, typename OutT, int EPI, bool AA, int LAY>
 hipError_t launch_aa(const GemmParams& p, int grid, hipStream_t s) {
     // opting in to more than 64 KB of dynamic LDS is idempotent and cheap
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI, AA>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI, AA, LAY>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI, AA>), dim3(grid), dim3(kThreads), kLdsBytes, s, p);
+    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI, AA, LAY>), dim3(grid), dim3(kThreads),
+                       kLdsBytes, s, p);
     return hipGetLastError();
 }
 
-template <typename T, typename OutT, int EPI>
+template <typename T, typename OutT, int EPI, int LAY = LAY_NN>
 hipError_t launch_t(const GemmParams& p, int grid, hipStream_t s) {
-    return p.a_ahead ? launch_aa<T, OutT, EPI, true>(p, grid, s)
-                     : launch_aa<T, OutT, EPI, false>(p, grid, s);
+    return p.a_ahead ? launch_aa<T, OutT, EPI, true, LAY>(p, grid, s)
+                     : launch_aa<T, OutT, EPI, false, LAY>(p, grid, s);
+}
+
+// The backward layouts: LAY_BT stores C in the input type (plain, or the SwiGLU
+// derivative); LAY_DW stores C in the input type or float32.
+template <typename T>
+hipError_t launch_bwd(const GemmParams& p, bool out_f32, int epi, int grid, hipStream_t s) {
+    if (p.layout == LAY_DW)
+        return out_f32 ? launch_t<T, float, EPI_STORE, LAY_DW>(p, grid, s)
+                       : launch_t<T, T, EPI_STORE, LAY_DW>(p, grid, s);
+    if (epi == EPI_SWIGLU_BWD) return launch_t<T, T, EPI_SWIGLU_BWD, LAY_BT>(p, grid, s);
+    return launch_t<T, T, EPI_STORE, LAY_BT>(p, grid, s);
 }
 
 }  // namespace
@@ -592,8 +794,22 @@ int gemm_k_bytes() { return kRowBytes; }
 
 bool gemm_offsets_fit(const GemmParams& p, int es) {
     const int64_t lim = (int64_t)1 << 32;
+    const int64_t kstep = kRowBytes / es;
     for (int s = 0; s < p.nseg; s++) {
         const GemmSeg& g = p.seg[s];
+        // [reduction][column] operands: offsets span one K step of rows and a tile
+        if (p.layout == LAY_DW) {
+            if (((kstep - 1) * g.lda + kBM) * es >= lim) return false;
+            if (((kstep - 1) * g.ldb + kBN) * es >= lim) return false;
+            continue;
+        }
+        if (p.layout == LAY_BT) {
+            if (((kstep - 1) * g.ldb + kBN) * es >= lim) return false;
+            const int64_t a_rows = p.a_rows ? p.a_src_rows : kBM;
+            if ((a_rows * g.lda + g.K) * es >= lim) return false;
+            if (((int64_t)g.K * es) % kRowBytes) return false;
+            continue;
+        }
         // A: offsets from the gather base (any source row) or from the tile's row 0
         const int64_t a_rows = p.a_rows ? p.a_src_rows : kBM;
         if ((a_rows * g.lda + g.K) * es >= lim) return false;
@@ -624,6 +840,9 @@ hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int e
     if (max_tiles < grid) grid = max_tiles;
     grid = ((grid + kNumXcd - 1) / kNumXcd) * kNumXcd;
     if (grid < kNumXcd) grid = kNumXcd;
+    if (p.layout != LAY_NN)
+        return in_dt == MOE_BF16 ? launch_bwd<bf16_t>(p, out_f32, epi, (int)grid, s)
+                                 : launch_bwd<float>(p, out_f32, epi, (int)grid, s);
     if (in_dt == MOE_BF16) {
         if (epi == EPI_STORE)
             return out_f32 ? launch_t<bf16_t, float, EPI_STORE>(p, (int)grid, s)

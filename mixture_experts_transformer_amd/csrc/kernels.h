@@ -10,7 +10,13 @@
 namespace moe {
 
 // ------------------------------------------------------------------ GEMM ---
-enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ADD = 2 };
+enum { EPI_STORE = 0, EPI_SWIGLU = 1, EPI_ADD = 2, EPI_SWIGLU_BWD = 3 };
+// Operand layouts.  By default A rows and B rows hold the reduction index
+// contiguously (C = A B^T).  LAY_BT: B is stored [reduction][column] (a weight
+// contracted over its rows: the input gradient of a grouped matmul).  LAY_DW:
+// both operands are stored [reduction][column] and the reduction runs over each
+// group's rows (the weight gradient of a grouped matmul).
+enum { LAY_NN = 0, LAY_BT = 2, LAY_DW = 7 };
 constexpr int kMaxSeg = 4;
 
 struct GemmSeg {
@@ -41,7 +47,10 @@ struct GemmParams {
     void* C;                     // output row r: C + r * ldc
     int64_t ldc;
     const void* addend;          // EPI_ADD: added row r: addend + r * ld_add
-    int64_t ld_add;
+    int64_t ld_add;              //   (EPI_SWIGLU_BWD: the [gate | up] pre-activations)
+    void* C2;                    // EPI_SWIGLU_BWD: h row r: C2 + r * ldc2
+    int64_t ldc2;
+    int32_t layout;              // LAY_*
 };
 
 int gemm_block_m();

@@ -61,6 +61,19 @@ _lib.moe_grouped_ffn.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, C.c
                                  _sz, _vp]
 _lib.moe_grouped_ffn_workspace_size.restype = _sz
 _lib.moe_grouped_ffn_workspace_size.argtypes = [_i32, _i64, _i64, C.c_int]
+_lib.moe_ragged_dot_dlhs.restype = C.c_int
+_lib.moe_ragged_dot_dlhs.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, C.c_int, _vp, _vp, _sz,
+                                     _vp]
+_lib.moe_ragged_dot_dlhs_workspace_size.restype = _sz
+_lib.moe_ragged_dot_dlhs_workspace_size.argtypes = [_i32]
+_lib.moe_ragged_dot_drhs.restype = C.c_int
+_lib.moe_ragged_dot_drhs.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, C.c_int, _vp, C.c_int,
+                                     _vp]
+_lib.moe_grouped_ffn_bwd.restype = C.c_int
+_lib.moe_grouped_ffn_bwd.argtypes = [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, C.c_int, _vp,
+                                     _vp, _vp, C.c_int, _vp, _sz, _vp]
+_lib.moe_grouped_ffn_bwd_workspace_size.restype = _sz
+_lib.moe_grouped_ffn_bwd_workspace_size.argtypes = [_i32, _i64, _i64, C.c_int]
 _lib.moe_combine.restype = C.c_int
 _lib.moe_combine.argtypes = [_vp, C.c_int, _vp, _vp, _i64, _i32, _i64, _vp, _i32, _vp]
 _lib.moe_layer_fwd.restype = C.c_int
@@ -187,6 +200,57 @@ def moe_grouped_ffn(X, offsets, W_gu, W_d, Y=None, ws=None):
     _check(_lib.moe_grouped_ffn(_ptr(X), _ptr(offsets), E, R, _ptr(W_gu), _ptr(W_d), d, H, _dt(X),
                                 _ptr(Y), _ptr(ws), ws.numel(), _stream()), "moe_grouped_ffn")
     return Y
+
+
+# --------------------------------------------------------- ragged dot VJP --
+def moe_ragged_dot_dlhs(dZ, offsets, W, dX=None, ws=None):
+    """dX[r] = W[e]^T dZ[r] for the rows of each group e (W [E, N, K], dZ [R, N])."""
+    R, N = dZ.shape
+    E, N2, K = W.shape
+    if dX is None:
+        dX = torch.empty((R, K), dtype=dZ.dtype, device=dZ.device)
+    ws = _ws(int(_lib.moe_ragged_dot_dlhs_workspace_size(E)), dZ.device, ws)
+    _check(_lib.moe_ragged_dot_dlhs(_ptr(dZ), _ptr(offsets), E, R, _ptr(W), N, K, _dt(dZ),
+                                    _ptr(dX), _ptr(ws), ws.numel(), _stream()),
+           "moe_ragged_dot_dlhs")
+    return dX
+
+
+def moe_ragged_dot_drhs(X, dZ, offsets, dW=None, dw_dtype=None):
+    """dW[e] = sum over the rows r of group e of dZ[r] X[r]^T -> [E, N, K]."""
+    R, K = X.shape
+    N = dZ.shape[1]
+    E = offsets.numel() - 1
+    if dW is None:
+        dW = torch.empty((E, N, K), dtype=dw_dtype or X.dtype, device=X.device)
+    _check(_lib.moe_ragged_dot_drhs(_ptr(X), _ptr(dZ), _ptr(offsets), E, R, N, K, _dt(X), _ptr(dW),
+                                    _dt(dW), _stream()), "moe_ragged_dot_drhs")
+    return dW
+
+
+def moe_grouped_ffn_bwd_workspace_size(E: int, R_phys: int, H: int, dtype: torch.dtype) -> int:
+    return int(_lib.moe_grouped_ffn_bwd_workspace_size(E, R_phys, H,
+                                                        _dt(torch.empty(0, dtype=dtype))))
+
+
+def moe_grouped_ffn_bwd(X, dY, offsets, W_gu, W_d, dX=None, dW_gu=None, dW_d=None,
+                        dw_dtype=None, ws=None):
+    """Backward of moe_grouped_ffn: returns (dX, dW_gu, dW_d)."""
+    R, d = X.shape
+    E, twoH, _ = W_gu.shape
+    H = twoH // 2
+    wdt = dw_dtype or X.dtype
+    if dX is None:
+        dX = torch.empty_like(X)
+    if dW_gu is None:
+        dW_gu = torch.empty(W_gu.shape, dtype=wdt, device=X.device)
+    if dW_d is None:
+        dW_d = torch.empty(W_d.shape, dtype=wdt, device=X.device)
+    ws = _ws(moe_grouped_ffn_bwd_workspace_size(E, R, H, X.dtype), X.device, ws)
+    _check(_lib.moe_grouped_ffn_bwd(_ptr(X), _ptr(dY), _ptr(offsets), E, R, _ptr(W_gu), _ptr(W_d),
+                                    d, H, _dt(X), _ptr(dX), _ptr(dW_gu), _ptr(dW_d), _dt(dW_gu),
+                                    _ptr(ws), ws.numel(), _stream()), "moe_grouped_ffn_bwd")
+    return dX, dW_gu, dW_d
 
 
 # ------------------------------------------------------------------- combine --

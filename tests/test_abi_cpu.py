@@ -110,3 +110,43 @@ def test_layer_rejects_bad_descriptors(lib):
     assert call(d, W=W2) == 1
     need = B.moe_layer_workspace_size(d)
     assert need > 64 * 2 * 64 * 2
+
+
+def test_backward_entry_points_reject_bad_arguments(lib):
+    vp, i64, i32, sz = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
+    lib.moe_ragged_dot_dlhs.argtypes = [vp, vp, i32, i64, vp, i64, i64, C.c_int, vp, vp, sz, vp]
+    lib.moe_ragged_dot_dlhs_workspace_size.restype = sz
+    lib.moe_ragged_dot_dlhs_workspace_size.argtypes = [i32]
+    lib.moe_ragged_dot_drhs.argtypes = [vp, vp, vp, i32, i64, i64, i64, C.c_int, vp, C.c_int, vp]
+    lib.moe_grouped_ffn_bwd.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, C.c_int, vp, vp, vp,
+                                        C.c_int, vp, sz, vp]
+    lib.moe_grouped_ffn_bwd_workspace_size.restype = sz
+    lib.moe_grouped_ffn_bwd_workspace_size.argtypes = [i32, i64, i64, C.c_int]
+    a = 4096
+    need = lib.moe_ragged_dot_dlhs_workspace_size(8)
+    assert need >= 9 * 4
+    dlhs = lambda **kw: lib.moe_ragged_dot_dlhs(
+        a, kw.get("off", a), kw.get("E", 8), 1000, kw.get("W", a), kw.get("N", 128),
+        kw.get("K", 64), kw.get("dt", 1), a, kw.get("ws", a), kw.get("wsb", need), None)
+    assert dlhs(E=0) == 2
+    assert dlhs(N=100) == 2                 # not whole 128-byte steps
+    assert dlhs(dt=7) == 3
+    assert dlhs(W=0) == 1
+    assert dlhs(off=a + 4) == 4             # misaligned
+    assert dlhs(wsb=need - 1) == 5
+    drhs = lambda **kw: lib.moe_ragged_dot_drhs(
+        a, a, a, kw.get("E", 8), 1000, kw.get("N", 128), kw.get("K", 64), kw.get("dt", 1),
+        kw.get("dW", a), kw.get("dw", 0), None)
+    assert drhs(K=96) == 2                  # bf16 rows of 192 bytes
+    assert drhs(dt=0, dw=1) == 3            # float32 inputs, bfloat16 weight gradient
+    assert drhs(dW=0) == 1
+    assert drhs(E=1025) == 2
+    wneed = lib.moe_grouped_ffn_bwd_workspace_size(8, 1000, 64, 1)
+    assert wneed > 1000 * 64 * 2 * 5
+    ffn = lambda **kw: lib.moe_grouped_ffn_bwd(
+        a, a, a, 8, 1000, a, a, kw.get("d", 128), 64, 1, a, kw.get("dWgu", a), a, kw.get("dw", 0),
+        a, kw.get("wsb", wneed), None)
+    assert ffn(d=96) == 2
+    assert ffn(dWgu=0) == 1
+    assert ffn(dw=5) == 3
+    assert ffn(wsb=wneed - 1) == 5

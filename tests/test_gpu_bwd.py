@@ -1,0 +1,150 @@
+"""Parity of the backward entry points (the grouped matmul's VJP and the gated
+expert MLP's backward) against the CPU oracle, through the C ABI.
+
+Tolerance as for the forward: max |err| <= 2e-2 x RMS(ref) for bfloat16
+outputs, 1e-5 x RMS(ref) for float32.  Rows past the groups hold NaN in every
+input, so a read past a group's end shows up as NaN in the results, and output
+rows past the groups hold a sentinel that must survive."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from oracle import torch_bridge as TB
+
+from gpu_util import assert_close
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mixture_experts_transformer_amd as m
+    return m
+
+
+def _offsets(rng, E, kind, scale):
+    if kind == "uniform":
+        c = rng.poisson(scale, E)
+    elif kind == "skewed":
+        c = rng.poisson(scale, E)
+        c[rng.choice(E, max(1, E // 4), replace=False)] *= 5
+    elif kind == "tails":            # reductions of 0, 1, 63, 64, 65, ... rows
+        c = np.array([0, 1, 63, 64, 65, 127, 129, 300][:E])
+    elif kind == "sparse":
+        c = np.zeros(E, np.int64)
+        c[rng.choice(E, 2, replace=False)] = rng.integers(1, 400, 2)
+    else:
+        raise ValueError(kind)
+    return np.concatenate([[0], np.cumsum(c)]).astype(np.int32)
+
+
+def _with_nan_tail(t, R):
+    t = t.clone()
+    t[R:] = float("nan")
+    return t
+
+
+DLHS_CASES = [  # dt, E, N, K, kind, scale
+    ("bf16", 4, 128, 192, "uniform", 150),       # two and three reduction steps
+    ("bf16", 3, 320, 64, "skewed", 200),         # several row tiles in one group
+    ("bf16", 8, 64, 320, "tails", 0),            # partial column tile, empty group
+    ("f32", 3, 96, 64, "uniform", 120),
+    ("f32", 5, 32, 160, "sparse", 0),
+    ("bf16", 2, 256, 256, "uniform", 700),       # A's steps ahead (>= 2 row tiles per group)
+]
+
+
+@pytest.mark.parametrize("dt,E,N,K,kind,scale", DLHS_CASES)
+def test_ragged_dot_dlhs_parity(M, dt, E, N, K, kind, scale):
+    rng = np.random.default_rng(E * N + K)
+    off = _offsets(rng, E, kind, scale)
+    R = int(off[-1])
+    R_phys = R + 29
+    g = torch.Generator().manual_seed(11)
+    dZ = _with_nan_tail(torch.randn((R_phys, N), generator=g), R).to(TDT[dt])
+    W = (torch.randn((E, N, K), generator=g) / math.sqrt(N)).to(TDT[dt])
+    dX = torch.full((R_phys, K), 5.0, dtype=TDT[dt], device=DEV)
+    M.moe_ragged_dot_dlhs(dZ.to(DEV), torch.from_numpy(off).to(DEV), W.to(DEV), dX=dX)
+    torch.cuda.synchronize()
+    ref = O.ragged_dlhs(TB.host(dZ)[:R], TB.host(W), off)
+    got = dX.float().cpu().numpy()
+    assert_close(got[:R], ref[:R], dt, "dX")
+    assert np.all(got[R:] == 5.0), "rows past offsets[E] were written"
+
+
+DRHS_CASES = [  # dt, out, E, N, K, kind, scale
+    ("bf16", "f32", 8, 128, 192, "tails", 0),     # ragged reductions incl. 0 and 1 rows
+    ("bf16", "bf16", 4, 320, 64, "uniform", 200),  # partial row tile of dW
+    ("bf16", "f32", 3, 64, 320, "skewed", 150),    # partial column tile of dW
+    ("f32", "f32", 8, 96, 64, "tails", 0),
+    ("f32", "f32", 3, 32, 160, "uniform", 90),
+    ("bf16", "f32", 2, 256, 256, "uniform", 1500),  # long reductions (about 24 steps)
+]
+
+
+@pytest.mark.parametrize("dt,out,E,N,K,kind,scale", DRHS_CASES)
+def test_ragged_dot_drhs_parity(M, dt, out, E, N, K, kind, scale):
+    rng = np.random.default_rng(E * N + K + 1)
+    off = _offsets(rng, E, kind, scale)
+    R = int(off[-1])
+    R_phys = R + 29
+    g = torch.Generator().manual_seed(12)
+    X = _with_nan_tail(torch.randn((R_phys, K), generator=g), R).to(TDT[dt])
+    dZ = _with_nan_tail(torch.randn((R_phys, N), generator=g), R).to(TDT[dt])
+    dW = torch.full((E, N, K), 7.0, dtype=TDT[out], device=DEV)
+    M.moe_ragged_dot_drhs(X.to(DEV), dZ.to(DEV), torch.from_numpy(off).to(DEV), dW=dW)
+    torch.cuda.synchronize()
+    ref = O.ragged_drhs(TB.host(X)[:R], TB.host(dZ)[:R], off)
+    got = dW.float().cpu().numpy()
+    for e in range(E):
+        if off[e + 1] == off[e]:
+            assert np.all(got[e] == 0.0), f"empty group {e} not zeroed"
+        else:
+            assert_close(got[e], ref[e], out, f"dW[{e}]")
+
+
+FFN_BWD_CASES = [  # dt, dw, E, d, H, kind, scale
+    ("bf16", "f32", 4, 128, 64, "uniform", 150),
+    ("bf16", "bf16", 3, 64, 128, "skewed", 120),
+    ("bf16", "f32", 8, 64, 64, "tails", 0),
+    ("f32", "f32", 3, 64, 96, "uniform", 100),
+    ("f32", "f32", 5, 32, 64, "sparse", 0),
+    ("bf16", "f32", 2, 128, 128, "uniform", 700),
+]
+
+
+@pytest.mark.parametrize("dt,dw,E,d,H,kind,scale", FFN_BWD_CASES)
+def test_grouped_ffn_bwd_parity(M, dt, dw, E, d, H, kind, scale):
+    rng = np.random.default_rng(E * d + H + 2)
+    off = _offsets(rng, E, kind, scale)
+    R = int(off[-1])
+    R_phys = R + 29
+    g = torch.Generator().manual_seed(13)
+    X = _with_nan_tail(torch.randn((R_phys, d), generator=g), R).to(TDT[dt])
+    dY = _with_nan_tail(torch.randn((R_phys, d), generator=g), R).to(TDT[dt])
+    W_gu = (torch.randn((E, 2 * H, d), generator=g) / math.sqrt(d)).to(TDT[dt])
+    W_d = (torch.randn((E, d, H), generator=g) / math.sqrt(H)).to(TDT[dt])
+    dX = torch.full((R_phys, d), 5.0, dtype=TDT[dt], device=DEV)
+    dX, dWgu, dWd = M.moe_grouped_ffn_bwd(X.to(DEV), dY.to(DEV), torch.from_numpy(off).to(DEV),
+                                          W_gu.to(DEV), W_d.to(DEV), dX=dX, dw_dtype=TDT[dw])
+    torch.cuda.synchronize()
+    rX, rWgu, rWd = O.expert_rows_bwd(TB.host(X)[:R], TB.host(dY)[:R], off, TB.host(W_gu),
+                                      TB.host(W_d))
+    gX = dX.float().cpu().numpy()
+    assert_close(gX[:R], rX[:R], dt, "dX")
+    assert np.all(gX[R:] == 5.0), "rows past offsets[E] were written"
+    gWgu, gWd = dWgu.float().cpu().numpy(), dWd.float().cpu().numpy()
+    for e in range(E):
+        if off[e + 1] == off[e]:
+            assert np.all(gWgu[e] == 0.0) and np.all(gWd[e] == 0.0), f"empty group {e}"
+            continue
+        # a bf16 path stores [g | u], [dg | du] and h in bf16 before the weight
+        # gradients reduce them, so those meet the bf16 bound whatever dW's type
+        assert_close(gWgu[e], rWgu[e], dt, f"dW_gu[{e}]")
+        assert_close(gWd[e], rWd[e], dt, f"dW_d[{e}]")
