@@ -46,6 +46,10 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-kernel-extras", action="store_true",
                     help="skip the stand-alone permute-with-copy measurement after the timed steps")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the expert MLP forward + backward (moe_grouped_ffn, "
+                         "moe_grouped_ffn_bwd) on an expert-MLP workload instead of the layer "
+                         "forward; default workload: the pages' custom-VJP microbench shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and report "
@@ -406,6 +410,143 @@ def bench_pool(args, cfg, M, dev):
     return line, pool
 
 
+BWD_METRIC = "expert MLP fwd+bwd TFLOP/s (model FLOPs), % of bf16 MFMA peak (1 MI355X)"
+BWD_DEFAULT = "grug_vjp_bf16_T4096_D1024_H2048_E64_k4"
+
+
+def bench_backward(args, cfg, M, dev):
+    """Forward (moe_grouped_ffn) then backward (moe_grouped_ffn_bwd) of the gated
+    expert MLP over rows grouped by expert; weight gradients in float32."""
+    import numpy as np
+    import torch
+
+    from moe_synth import gen_expert_mlp
+
+    data = gen_expert_mlp(cfg, dev)
+    X, dY, W_gu, W_d, off = data["X"], data["dY"], data["W_gu"], data["W_d"], data["offsets"]
+    R, d, H, E = cfg.R, cfg.d, cfg.H, cfg.E
+    Y = torch.empty_like(X)
+    dX = torch.empty_like(X)
+    dWgu = torch.empty(W_gu.shape, dtype=torch.float32, device=dev)
+    dWd = torch.empty(W_d.shape, dtype=torch.float32, device=dev)
+    fws = torch.empty(M.moe_grouped_ffn_workspace_size(E, R, H, X.dtype), dtype=torch.uint8,
+                      device=dev)
+    bws = torch.empty(M.moe_grouped_ffn_bwd_workspace_size(E, R, H, X.dtype), dtype=torch.uint8,
+                      device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        M.moe_grouped_ffn(X, off, W_gu, W_d, Y=Y, ws=fws)
+        if ev:
+            ev[1].record()
+        M.moe_grouped_ffn_bwd(X, dY, off, W_gu, W_d, dX=dX, dW_gu=dWgu, dW_d=dWd, ws=bws)
+        if ev:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ff, fb = cfg.flops_fwd(), cfg.flops_bwd()
+    tflops = (ff + fb) / (ms * 1e-3) / 1e12
+    es = 2 if cfg.dtype == "bf16" else 4
+    # The two VJP GEMMs of the largest reduction, each timed alone: the input
+    # gradient dX = [dg | du] W_gu[e] and the weight gradient dW_gu[e] = [dg | du]^T X
+    dgu = torch.randn((R, 2 * H), device=dev).to(X.dtype)
+    dlhs_ms = time_ms(lambda: M.moe_ragged_dot_dlhs(dgu, off, W_gu, dX=dX))
+    drhs_ms = time_ms(lambda: M.moe_ragged_dot_drhs(X, dgu, off, dW=dWgu))
+    mm = 2 * R * 2 * H * d
+    dlhs_bytes = E * 2 * H * d * es + R * (2 * H + d) * es
+    drhs_bytes = R * (2 * H + d) * es + E * 2 * H * d * 4
+    del dgu
+    line = {
+        "metric": BWD_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (model FLOPs)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; rows and output gradients ~ N(0,1), weights ~ "
+                "N(0,1/fan_in), uniform top-k routing or Zipf(1) for a pool)",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "top_k": cfg.k, "rows": R, "width": d,
+                   "expert_hidden": H, "experts": E, "weight_grad_dtype": "f32",
+                   "parallelism": "none (1 GPU)"},
+        "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
+        "stage_ms": {"forward": round(fwd_ms, 4), "backward": round(bwd_ms, 4)},
+        "fwd_tflops": round(ff / (fwd_ms * 1e-3) / 1e12, 2),
+        "bwd_tflops": round(fb / (bwd_ms * 1e-3) / 1e12, 2),
+        "roofline": gemm_roofline("ragged-dot weight gradient dW_gu (moe_ragged_dot_drhs)", mm,
+                                  drhs_bytes, drhs_ms, cfg.dtype),
+        "vjp_kernels": {
+            "dlhs_dX": gemm_roofline("ragged-dot input gradient dX (moe_ragged_dot_dlhs)", mm,
+                                     dlhs_bytes, dlhs_ms, cfg.dtype),
+            "drhs_dW_gu": gemm_roofline("ragged-dot weight gradient dW_gu", mm, drhs_bytes,
+                                        drhs_ms, cfg.dtype),
+        },
+        "routed_rows": {"per_expert_min": int(data["counts"].min()),
+                        "per_expert_max": int(data["counts"].max())},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_backward(cfg, data, args.cpu_seconds)
+    return line
+
+
+def cpu_baseline_backward(cfg, data, target_s: float) -> dict:
+    """The oracle's forward and backward of the expert MLP on a bounded random sample:
+    rows of four experts (the weight gradients of those experts over the sampled
+    rows)."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from oracle import torch_bridge as TB
+
+    counts = data["counts"]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    rng = np.random.default_rng(0)
+    experts = np.sort(rng.choice(np.flatnonzero(counts), min(4, int(np.count_nonzero(counts))),
+                                 replace=False))
+    W_gu = TB.host(data["W_gu"][experts.tolist()])
+    W_d = TB.host(data["W_d"][experts.tolist()])
+
+    def run(per_expert):
+        take = [np.sort(rng.choice(counts[e], min(per_expert, counts[e]), replace=False))
+                + off[e] for e in experts]
+        rows = np.concatenate(take).astype(np.int64)
+        sub_counts = np.array([len(t) for t in take])
+        sub_off = np.concatenate([[0], np.cumsum(sub_counts)]).astype(np.int32)
+        X = TB.host(data["X"][rows])
+        dY = TB.host(data["dY"][rows])
+        ex = np.repeat(np.arange(len(experts), dtype=np.int32), sub_counts)
+        t0 = time.perf_counter()
+        O.expert_rows(X, ex, list(W_gu), list(W_d), cfg.H)
+        O.expert_rows_bwd(X, dY, sub_off, W_gu, W_d)
+        return time.perf_counter() - t0, int(len(rows))
+
+    t, n = run(2)
+    per = max(2, int(2 * target_s / max(t, 1e-3)))
+    t, n = run(per)
+    return {"value": round(n / t, 2), "unit": "rows/s (forward + backward)",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+            "kind": "oracle",
+            "sample": f"{n} rows of experts {experts.tolist()} (up to {per} random rows each, "
+                      f"seed 0) of the same workload through the oracle's expert forward and "
+                      f"backward in double precision"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -417,8 +558,12 @@ def main():
     import mixture_experts_transformer_amd as M
     from moe_synth import PoolConfig, by_name
 
-    cfg = by_name(args.workload)
     dev = torch.device("cuda:0")
+    if args.backward:
+        name = args.workload if args.workload != DEFAULT_WORKLOAD else BWD_DEFAULT
+        print(json.dumps(bench_backward(args, by_name(name), M, dev)), flush=True)
+        return
+    cfg = by_name(args.workload)
     if isinstance(cfg, PoolConfig):
         line, data = bench_pool(args, cfg, M, dev)
     else:

@@ -154,8 +154,9 @@ size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_
  *   ws (device) moe_ragged_dot_dlhs_workspace_size(E) bytes (the row-tile prefix).
  * moe_ragged_dot_drhs:  dW[e] = sum over the rows r of group e of dZ[r] X[r]^T
  *   X (device) [R_phys, K] dt;  dZ (device) [R_phys, N] dt;  dW (device) [E, N, K]
- *   in dw_dt (dt or MOE_F32).  An empty group's dW[e] is written as zeros; no
- *   workspace.
+ *   in dw_dt (dt or MOE_F32).  An empty group's dW[e] is written as zeros.
+ *   ws (device) moe_ragged_dot_drhs_workspace_size(E) bytes (the XCD tile ranges,
+ *   balanced by each group's row count).
  * Both: offsets (device) [E+1] int32 ascending, offsets[0] = 0, offsets[E] <=
  * R_phys.  Limits: N and K multiples of 64 for MOE_BF16 and of 32 for MOE_F32,
  * 1 <= E <= 1024, R_phys < 2^31; otherwise MOE_ESHAPE.  Pointers 16-byte
@@ -166,7 +167,8 @@ moe_status moe_ragged_dot_dlhs(const void *dZ, const int32_t *offsets, int32_t E
 size_t moe_ragged_dot_dlhs_workspace_size(int32_t E);
 moe_status moe_ragged_dot_drhs(const void *X, const void *dZ, const int32_t *offsets, int32_t E,
                                int64_t R_phys, int64_t N, int64_t K, moe_dtype dt, void *dW,
-                               moe_dtype dw_dt, moe_stream stream);
+                               moe_dtype dw_dt, void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_ragged_dot_drhs_workspace_size(int32_t E);
 
 /* Backward of moe_grouped_ffn (the gated expert MLP over row groups; the same
  * VJP pieces as above, chained through SwiGLU's derivative).  Given the
@@ -179,7 +181,8 @@ moe_status moe_ragged_dot_drhs(const void *X, const void *dZ, const int32_t *off
  *   and dW_d [E, d, H] in dw_dt (dt or MOE_F32); empty groups get zeros.
  *   ws (device) moe_grouped_ffn_bwd_workspace_size(E, R_phys, H, dt) bytes: holds
  *   [g | u] in float32 and [dg | du] and h in dt (both are operands of the
- *   weight-gradient and input-gradient GEMMs, so they are rounded to dt).
+ *   weight-gradient and input-gradient GEMMs, so they are rounded to dt), and the
+ *   weight-gradient GEMMs' XCD tile ranges.
  * Limits as moe_grouped_ffn. */
 moe_status moe_grouped_ffn_bwd(const void *X, const void *dY, const int32_t *offsets, int32_t E,
                                int64_t R_phys, const void *W_gu, const void *W_d, int64_t d,

@@ -184,10 +184,14 @@ moe_status dlhs_impl(const void* dZ, const int32_t* offsets, const int32_t* tile
 }
 
 // Weight gradient of the grouped matmul: dW[g] = dZ[rows of g]^T X[rows of g],
-// [N, K] per group, the reduction running over each group's rows.
+// [N, K] per group, the reduction running over each group's rows.  `split`
+// ([9] int64, device) receives the XCD tile ranges balanced by group length.
 moe_status drhs_impl(const void* X, const void* dZ, const int32_t* offsets, int E, int64_t N,
-                     int64_t K, moe_dtype dt, void* dW, bool out_f32, hipStream_t s) {
+                     int64_t K, moe_dtype dt, void* dW, bool out_f32, int64_t* split,
+                     hipStream_t s) {
+    MOE_TRY(launch_dw_split(offsets, E, N, K, esize(dt), out_f32 || dt == MOE_F32, split, s));
     GemmParams p = gemm_base();
+    p.xcd_split = split;
     p.layout = LAY_DW;
     p.group_m = 1;
     p.offsets = offsets;
@@ -410,20 +414,26 @@ moe_status moe_ragged_dot_dlhs(const void* dZ, const int32_t* offsets, int32_t E
                      s);
 }
 
+size_t moe_ragged_dot_drhs_workspace_size(int32_t E) {
+    if (E < 1) return 0;
+    return a256(9 * sizeof(int64_t));
+}
+
 moe_status moe_ragged_dot_drhs(const void* X, const void* dZ, const int32_t* offsets, int32_t E,
                                int64_t R_phys, int64_t N, int64_t K, moe_dtype dt, void* dW,
-                               moe_dtype dw_dt, moe_stream stream) {
+                               moe_dtype dw_dt, void* ws, size_t ws_bytes, moe_stream stream) {
     if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
     if (!dt_ok(dt) || (dw_dt != dt && dw_dt != MOE_F32)) return MOE_EDTYPE;
     if (!width_ok(N, dt) || !width_ok(K, dt)) return MOE_ESHAPE;
     if (!under4g(gemm_k_bytes() + 1, N, dt) || !under4g(gemm_k_bytes() + 1, K, dt))
         return MOE_ESHAPE;
     if (!offsets || !dW || (R_phys > 0 && (!X || !dZ))) return MOE_EINVAL;
-    const void* ptrs[] = {X, dZ, offsets, dW};
+    const void* ptrs[] = {X, dZ, offsets, dW, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_EALIGN;
+    if (!ws || ws_bytes < moe_ragged_dot_drhs_workspace_size(E)) return MOE_EWORKSPACE;
     return drhs_impl(X, dZ, offsets, E, N, K, dt, dW, dw_dt == MOE_F32 && dt != MOE_F32,
-                     hs(stream));
+                     (int64_t*)ws, hs(stream));
 }
 
 // ---------------------------------------------------- grouped FFN backward ----
@@ -434,6 +444,7 @@ size_t moe_grouped_ffn_bwd_workspace_size(int32_t E, int64_t R_phys, int64_t H, 
     cv.take<char>((size_t)R_phys * 2 * H * 4);             // [g | u], float32
     cv.take<char>((size_t)R_phys * 2 * H * esize(dt));     // [dg | du]
     cv.take<char>((size_t)R_phys * H * esize(dt));         // h
+    cv.take<int64_t>(2 * 9 * sizeof(int64_t));             // XCD splits of dW_d, dW_gu
     return cv.off;
 }
 
@@ -459,6 +470,7 @@ moe_status moe_grouped_ffn_bwd(const void* X, const void* dY, const int32_t* off
     void* gu = cv.take<char>((size_t)R_phys * 2 * H * 4);
     void* dgu = cv.take<char>((size_t)R_phys * 2 * H * esize(dt));
     void* h = cv.take<char>((size_t)R_phys * H * esize(dt));
+    int64_t* split = cv.take<int64_t>(2 * 9 * sizeof(int64_t));
     hipStream_t s = hs(stream);
     const bool w32 = dw_dt == MOE_F32 && dt != MOE_F32;
     MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tp, s));
@@ -486,14 +498,14 @@ moe_status moe_grouped_ffn_bwd(const void* X, const void* dY, const int32_t* off
                               2 * H, gu, h, s);
     if (st != MOE_OK) return st;
     // 3. dW_d[e] = dY[rows]^T h[rows]
-    st = drhs_impl(h, dY, offsets, E, d, H, dt, dW_d, w32, s);
+    st = drhs_impl(h, dY, offsets, E, d, H, dt, dW_d, w32, split, s);
     if (st != MOE_OK) return st;
     // 4. dX = [dg | du] W_gu[e]
     st = dlhs_impl(dgu, offsets, tp, E, R_phys, W_gu, 2 * H, d, dt, EPI_STORE, dX, d, nullptr,
                    nullptr, s);
     if (st != MOE_OK) return st;
     // 5. dW_gu[e] = [dg | du][rows]^T X[rows]
-    return drhs_impl(X, dgu, offsets, E, 2 * H, d, dt, dW_gu, w32, s);
+    return drhs_impl(X, dgu, offsets, E, 2 * H, d, dt, dW_gu, w32, split + 9, s);
 }
 
 // -------------------------------------------------------------- combine ----

@@ -89,14 +89,46 @@ __device__ __forceinline__ int swzT(int kk) { return ((kk >> 1) & 1) << 2; }
 // (4 lanes of 4 columns each per row), every lane receives 4 consecutive
 // reduction indices of one column; two reads 4 rows apart make the 8 the MFMA
 // operand holds.
+//
+// In the kernels with such operands every fragment read is written out in
+// inline asm: for an LDS transpose read it emits itself, the compiler first
+// waits for every LDS DMA in flight (vmcnt(0)), which would make each K step
+// wait for the loads issued two steps ahead.  A written-out read's result is
+// undefined until lds_fence (s_waitcnt lgkmcnt(0), then an empty asm that
+// "redefines" each fragment register, so no use can move above the wait), and
+// the two halves of a transposed fragment stay apart until then, so nothing
+// copies them early.
 typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef short v8i16 __attribute__((ext_vector_type(8)));
-__device__ __forceinline__ bf16x8 tr_frag_bf16(const char* p) {
-    typedef __attribute__((address_space(3))) v4i16* lds_v4;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)p);
-    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(p + 4 * kRowBytes));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+struct TrPair { v4i16 lo, hi; };
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
+__device__ __forceinline__ void asm_read(TrPair& f, const char* p) {
+    const uint32_t a = lds_u32(p);
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(f.lo) : "v"(a));
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:512" : "=v"(f.hi) : "v"(a));
+    static_assert(4 * kRowBytes == 512, "the second half is four rows down");
+}
+__device__ __forceinline__ void asm_read(bf16x8& f, const char* p) {
+    asm volatile("ds_read_b128 %0, %1" : "=v"(f) : "v"(lds_u32(p)));
+}
+__device__ __forceinline__ void asm_read(float& f, const char* p) {
+    asm volatile("ds_read_b32 %0, %1" : "=v"(f) : "v"(lds_u32(p)));
+}
+__device__ __forceinline__ void tie(TrPair& f) { asm volatile("" : "+v"(f.lo), "+v"(f.hi)); }
+__device__ __forceinline__ void tie(bf16x8& f) { asm volatile("" : "+v"(f)); }
+__device__ __forceinline__ void tie(float& f) { asm volatile("" : "+v"(f)); }
+__device__ __forceinline__ bf16x8 as_frag(const TrPair& f) {
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+__device__ __forceinline__ bf16x8 as_frag(const bf16x8& f) { return f; }
+__device__ __forceinline__ float as_frag(const float& f) { return f; }
+__device__ __forceinline__ void zero_elem(TrPair& f, int e) {
+    if (e < 4) f.lo[e] = 0;
+    else f.hi[e - 4] = 0;
+}
+__device__ __forceinline__ void zero_elem(bf16x8& f, int e) { f[e] = (__bf16)0.0f; }
+__device__ __forceinline__ void zero_elem(float& f, int) { f = 0.0f; }
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
 // expcnt and lgkmcnt left at "no wait").
@@ -201,8 +233,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int xcd = blockIdx.x % kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
     const int nslots = gridDim.x / kNumXcd;
-    const int64_t lo = total * xcd / kNumXcd;
-    const int64_t hi = total * (xcd + 1) / kNumXcd;
+    int64_t lo = total * xcd / kNumXcd;
+    int64_t hi = total * (xcd + 1) / kNumXcd;
+    if constexpr (kRK) {
+        // reduction over each group's rows: the XCD ranges come balanced by cost
+        // (launch_dw_split); without them, equal tile counts
+        if (p.xcd_split) {
+            lo = uniform64(p.xcd_split[xcd]);
+            hi = uniform64(p.xcd_split[xcd + 1]);
+        }
+    }
 
     // fragment read offsets (the swizzle depends only on row % 32)
     const int fl = swz(lane & 31);
@@ -227,12 +267,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             tro1 = (lane >> 5) * kRowBytes + (((c >> 2) ^ 4) << 4) + ((c & 3) << 2);
         }
     }
-    // fragment of the 32-column block at m_base for MFMA k-step ks, from a
-    // [reduction][column] slot
-    auto t_frag = [&](const char* slot, int m_base, int ks) __attribute__((always_inline)) {
+    // LDS address of the lane's fragment of the 32-column block at m_base for
+    // MFMA k-step ks, in a [reduction][column] slot
+    auto t_addr = [&](const char* slot, int m_base, int ks) __attribute__((always_inline)) {
         const char* q = slot + (m_base / kSubW) * kSubBytes + ks * (Mfma<T>::kK * kRowBytes);
-        if constexpr (kElem == 2) return tr_frag_bf16(q + ((m_base & 32) ? tro1 : tro0));
-        else return *(const float*)(q + ((ks & 1) ? tro1 : tro0));
+        if constexpr (kElem == 2) return q + ((m_base & 32) ? tro1 : tro0);
+        else return q + ((ks & 1) ? tro1 : tro0);
     };
 
     // ---- a tile: its rows, columns and expert
@@ -460,6 +500,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         constexpr int NACT = decltype(nact_c)::value;
         constexpr int NA = NACT > 0 ? NACT : 1;
         typedef typename Mfma<T>::frag Frag;
+        // fragments as read: a transposed bf16 fragment is two halves until fenced
+        constexpr bool kTK = kAT || kBT;
+        using FragA = std::conditional_t<kAT && kElem == 2, TrPair, Frag>;
+        using FragB = std::conditional_t<kBT && kElem == 2, TrPair, Frag>;
         floatx16 acc[NA][2];
 #pragma unroll
         for (int i = 0; i < NACT; i++)
@@ -469,7 +513,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 for (int v = 0; v < 16; v++) acc[i][j][v] = 0.0f;
 
         // Fragments of one quarter of a K step (kSub MFMA k-steps).
-        auto load_sub = [&](int sa, int sb, int q, Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
+        auto load_sub = [&](int sa, int sb, int q, FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
             __attribute__((always_inline)) {
             const char* As = lds + sa * kOpBytes + rd_row;
             const char* Bs = lds + kBBase + sb * kOpBytes + rd_row;
@@ -481,14 +525,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
                     if constexpr (kBT)
-                        fb[hs][j] = t_frag(lds + kBBase + sb * kOpBytes, wn * 64 + j * 32, ks);
+                        asm_read(fb[hs][j], t_addr(lds + kBBase + sb * kOpBytes, wn * 64 + j * 32, ks));
+                    else if constexpr (kTK)
+                        asm_read(fb[hs][j], Bs + (wn * 64 + j * 32) * kRowBytes + kbyte);
                     else
                         fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
                 }
 #pragma unroll
                 for (int i = 0; i < NACT; i++) {
                     if constexpr (kAT)
-                        fa[hs][i] = t_frag(lds + sa * kOpBytes, (wm + 2 * i) * 32, ks);
+                        asm_read(fa[hs][i], t_addr(lds + sa * kOpBytes, (wm + 2 * i) * 32, ks));
+                    else if constexpr (kTK)
+                        asm_read(fa[hs][i], As + ((wm + 2 * i) * 32) * kRowBytes + kbyte);
                     else
                         fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
                 }
@@ -496,32 +544,37 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         };
         // LAY_DW, last step: zero the operand elements at reduction indices past
         // the group's end (their LDS rows hold copies of its last row)
-        auto mask_sub = [&](int q, Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
+        auto mask_sub = [&](int q, FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
             __attribute__((always_inline)) {
 #pragma unroll
             for (int hs = 0; hs < kSub; hs++) {
                 const int kf = (q * kSub + hs) * Mfma<T>::kK + (lane >> 5) * Mfma<T>::kLaneK;
-                if constexpr (kElem == 2) {
 #pragma unroll
-                    for (int e = 0; e < Mfma<T>::kLaneK; e++) {
-                        if (kf + e >= kvalid) {
+                for (int e = 0; e < Mfma<T>::kLaneK; e++) {
+                    if (kf + e >= kvalid) {
 #pragma unroll
-                            for (int i = 0; i < NACT; i++) fa[hs][i][e] = (__bf16)0.0f;
+                        for (int i = 0; i < NACT; i++) zero_elem(fa[hs][i], e);
 #pragma unroll
-                            for (int j = 0; j < 2; j++) fb[hs][j][e] = (__bf16)0.0f;
-                        }
-                    }
-                } else {
-                    if (kf >= kvalid) {
-#pragma unroll
-                        for (int i = 0; i < NACT; i++) fa[hs][i] = 0.0f;
-#pragma unroll
-                        for (int j = 0; j < 2; j++) fb[hs][j] = 0.0f;
+                        for (int j = 0; j < 2; j++) zero_elem(fb[hs][j], e);
                     }
                 }
             }
         };
-        auto mma_sub = [&](Frag (&fa)[kSub][NA], Frag (&fb)[kSub][2])
+        // written-out reads: wait for them and make their registers defined
+        auto fence_sub = [&](FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
+            __attribute__((always_inline)) {
+            if constexpr (kTK) {
+                asm volatile("s_waitcnt lgkmcnt(0)");
+#pragma unroll
+                for (int hs = 0; hs < kSub; hs++) {
+#pragma unroll
+                    for (int i = 0; i < NACT; i++) tie(fa[hs][i]);
+#pragma unroll
+                    for (int j = 0; j < 2; j++) tie(fb[hs][j]);
+                }
+            }
+        };
+        auto mma_sub = [&](FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
             __attribute__((always_inline)) {
 #pragma unroll
             for (int hs = 0; hs < kSub; hs++)
@@ -529,7 +582,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 for (int i = 0; i < NACT; i++)
 #pragma unroll
                     for (int j = 0; j < 2; j++)
-                        acc[i][j] = Mfma<T>::mma(fa[hs][i], fb[hs][j], acc[i][j]);
+                        acc[i][j] = Mfma<T>::mma(as_frag(fa[hs][i]), as_frag(fb[hs][j]), acc[i][j]);
         };
         // Instruction order within a quarter step: one MFMA, then the fragment
         // reads of the next quarter, then the remaining MFMAs with NV DMA
@@ -570,7 +623,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             if (nk > 1) wait_vmcnt<2 * kDmaPerOperand>();
             else wait_vmcnt<0>();
             bare_barrier();
-            Frag f0a[kSub][NA], f0b[kSub][2], f1a[kSub][NA], f1b[kSub][2];
+            FragA f0a[kSub][NA], f1a[kSub][NA];
+            FragB f0b[kSub][2], f1b[kSub][2];
             if (NACT > 0) load_sub(0, 0, 0, f0a, f0b);
 
             // Software pipeline over the quarters of the K steps: each quarter's
@@ -585,7 +639,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 const int kf2 = min(kt + 2, nk - 1);              // far step issued now
                 const int sf2 = sf == 0 ? kSlotsFar - 1 : sf - 1;  // its slot, (kt + 2) % 3
                 const int sa = AA ? sf : sn, sb = AA ? sn : sf;
-                if (NACT > 0) {
+                if (NACT > 0 && kTK) {
+                    fence_sub(f0a, f0b);
+                    load_sub(sa, sb, 1, f1a, f1b);
+                    mma_sub(f0a, f0b);
+                    issue_far(kf2, sf2, 0, kDmaPerOperand / 2);
+                    fence_sub(f1a, f1b);
+                    load_sub(sa, sb, 2, f0a, f0b);
+                    mma_sub(f1a, f1b);
+                    issue_far(kf2, sf2, kDmaPerOperand / 2, kDmaPerOperand / 2);
+                    fence_sub(f0a, f0b);
+                    load_sub(sa, sb, 3, f1a, f1b);
+                    mma_sub(f0a, f0b);
+                } else if (NACT > 0) {
                     load_sub(sa, sb, 1, f1a, f1b);
                     mma_sub(f0a, f0b);
                     issue_far(kf2, sf2, 0, kDmaPerOperand / 2);
@@ -606,7 +672,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 wait_vmcnt<kDmaPerOperand>();   // A, B of kt+1 landed
                 bare_barrier();
                 sf = sf == kSlotsFar - 1 ? 0 : sf + 1;
-                if (NACT > 0) {
+                if (NACT > 0 && kTK) {
+                    fence_sub(f1a, f1b);
+                    load_sub(AA ? sf : sn ^ 1, AA ? sn ^ 1 : sf, 0, f0a, f0b);
+                    mma_sub(f1a, f1b);
+                    issue_near(min(kt + 2, nk - 1), sn);
+                } else if (NACT > 0) {
                     load_sub(AA ? sf : sn ^ 1, AA ? sn ^ 1 : sf, 0, f0a, f0b);
                     mma_sub(f1a, f1b);
                     issue_near(min(kt + 2, nk - 1), sn);
@@ -619,16 +690,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             const int sa = AA ? sf : sn, sb = AA ? sn : sf;
             // last step (its first quarter is already in registers)
             const bool tail = kRK && kvalid < kKStep;
-            if (NACT > 0) {
+            if (NACT > 0 && kTK) {
+                fence_sub(f0a, f0b);
                 if (tail) mask_sub(0, f0a, f0b);
                 load_sub(sa, sb, 1, f1a, f1b);
+                mma_sub(f0a, f0b);
+                fence_sub(f1a, f1b);
                 if (tail) mask_sub(1, f1a, f1b);
+                load_sub(sa, sb, 2, f0a, f0b);
+                mma_sub(f1a, f1b);
+                fence_sub(f0a, f0b);
+                if (tail) mask_sub(2, f0a, f0b);
+                load_sub(sa, sb, 3, f1a, f1b);
+                mma_sub(f0a, f0b);
+                fence_sub(f1a, f1b);
+                if (tail) mask_sub(3, f1a, f1b);
+                mma_sub(f1a, f1b);
+            } else if (NACT > 0) {
+                load_sub(sa, sb, 1, f1a, f1b);
                 mma_sub(f0a, f0b);
                 load_sub(sa, sb, 2, f0a, f0b);
-                if (tail) mask_sub(2, f0a, f0b);
                 mma_sub(f1a, f1b);
                 load_sub(sa, sb, 3, f1a, f1b);
-                if (tail) mask_sub(3, f1a, f1b);
                 mma_sub(f0a, f0b);
                 mma_sub(f1a, f1b);
             }
@@ -756,6 +839,77 @@ __global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* offset
     if (tid == 0) tp[G] = total;
 }
 
+// XCD ranges for a GEMM whose reduction runs over each group's rows (LAY_DW).
+// A group's tiles cost in proportion to its reduction steps plus a fixed share
+// for the pipeline fill and the epilogue's 256 x 256 stores (about eight steps'
+// time for float32 output, five for bf16).  An equal split of the tile count
+// is kept when no XCD gets over 5% more than its share of the cost (its ranges
+// hold whole groups whenever the group count divides by 8); otherwise XCD x
+// takes the contiguous tiles where the running cost passes x / 8 of the total,
+// snapped to a group's start when every group is small next to an XCD's share.
+// With skewed groups an equal count leaves one XCD with several times the work
+// of another.  One wave; up to 16 groups per lane (G <= 1024); split[0..8].
+__global__ __launch_bounds__(64) void dw_split_kernel(const int32_t* offsets, int G,
+                                                      int64_t per_g, int k_step, int fixed,
+                                                      int64_t* split) {
+    constexpr int kPer = 16;
+    __shared__ int64_t at_equal[kNumXcd + 1];   // running cost at the equal-count boundaries
+    __shared__ int keep_equal;
+    const int lane = threadIdx.x;
+    const int64_t tiles = (int64_t)G * per_g;
+    int64_t u[kPer];
+    int64_t sum = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; j++) {
+        const int g = lane * kPer + j;
+        u[j] = g < G ? fixed + (offsets[g + 1] - offsets[g] + k_step - 1) / k_step : 0;
+        sum += per_g * u[j];
+    }
+    int64_t incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += y;
+    }
+    const int64_t total = __shfl(incl, 63, 64);
+    const int64_t share = total / kNumXcd;
+    for (int x = 0; x < kNumXcd; x++) {
+        const int64_t t = tiles * x / kNumXcd;
+        int64_t run = incl - sum;
+        for (int j = 0; j < kPer; j++) {
+            const int64_t g0 = (int64_t)(lane * kPer + j) * per_g;
+            if (u[j] > 0 && g0 <= t && t < g0 + per_g) at_equal[x] = run + (t - g0) * u[j];
+            run += per_g * u[j];
+        }
+    }
+    if (lane == 0) at_equal[kNumXcd] = total;
+    __syncthreads();
+    if (lane == 0) {
+        int64_t worst = 0;
+        for (int x = 0; x < kNumXcd; x++) worst = max(worst, at_equal[x + 1] - at_equal[x]);
+        keep_equal = worst * kNumXcd * 100 <= total * 105;
+    }
+    __syncthreads();
+    if (keep_equal) {
+        if (lane <= kNumXcd) split[lane] = tiles * lane / kNumXcd;
+        return;
+    }
+    for (int x = 0; x < kNumXcd; x++) {
+        const int64_t target = total * x / kNumXcd;
+        int64_t run = incl - sum;
+        for (int j = 0; j < kPer; j++) {
+            const int64_t c = per_g * u[j];
+            if (c > 0 && run <= target && target < run + c) {
+                const int64_t g0 = (int64_t)(lane * kPer + j) * per_g;
+                split[x] = 16 * c <= share ? g0 + (2 * (target - run) >= c ? per_g : 0)
+                                           : g0 + (target - run + u[j] - 1) / u[j];
+            }
+            run += c;
+        }
+    }
+    if (lane == 0) split[kNumXcd] = tiles;
+}
+
 constexpr size_t kLdsBytes = (size_t)(kSlotsFar + kSlotsNear) * kOpBytes;   // 163,840 bytes
 
 template <typename T, typename OutT, int EPI, bool AA, int LAY>
@@ -822,6 +976,14 @@ bool gemm_offsets_fit(const GemmParams& p, int es) {
 }
 
 int gemm_cols_per_tile(int epi) { return epi == EPI_SWIGLU ? kBN / 2 : kBN; }
+
+hipError_t launch_dw_split(const int32_t* offsets, int G, int64_t M, int64_t N, int elem_bytes,
+                           bool out_f32, int64_t* split, hipStream_t s) {
+    const int64_t per_g = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    hipLaunchKernelGGL(dw_split_kernel, dim3(1), dim3(64), 0, s, offsets, G, per_g,
+                       kRowBytes / elem_bytes, out_f32 ? 8 : 5, split);
+    return hipGetLastError();
+}
 
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp, hipStream_t s) {
     hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, offsets, G, BM, tp);

@@ -51,6 +51,7 @@ struct GemmParams {
     void* C2;                    // EPI_SWIGLU_BWD: h row r: C2 + r * ldc2
     int64_t ldc2;
     int32_t layout;              // LAY_*
+    const int64_t* xcd_split;    // LAY_DW: [9] tile range of each XCD (device), or nullptr
 };
 
 int gemm_block_m();
@@ -61,6 +62,9 @@ int gemm_k_bytes();
 bool gemm_offsets_fit(const GemmParams& p, int elem_bytes);
 int gemm_cols_per_tile(int epi);
 hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp, hipStream_t s);
+// LAY_DW: XCD tile ranges balanced by each group's reduction length (device, [9]).
+hipError_t launch_dw_split(const int32_t* offsets, int G, int64_t M, int64_t N, int elem_bytes,
+                           bool out_f32, int64_t* split, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,
                        int64_t max_tiles, hipStream_t s);
 

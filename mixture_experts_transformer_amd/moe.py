@@ -68,7 +68,9 @@ _lib.moe_ragged_dot_dlhs_workspace_size.restype = _sz
 _lib.moe_ragged_dot_dlhs_workspace_size.argtypes = [_i32]
 _lib.moe_ragged_dot_drhs.restype = C.c_int
 _lib.moe_ragged_dot_drhs.argtypes = [_vp, _vp, _vp, _i32, _i64, _i64, _i64, C.c_int, _vp, C.c_int,
-                                     _vp]
+                                     _vp, _sz, _vp]
+_lib.moe_ragged_dot_drhs_workspace_size.restype = _sz
+_lib.moe_ragged_dot_drhs_workspace_size.argtypes = [_i32]
 _lib.moe_grouped_ffn_bwd.restype = C.c_int
 _lib.moe_grouped_ffn_bwd.argtypes = [_vp, _vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, C.c_int, _vp,
                                      _vp, _vp, C.c_int, _vp, _sz, _vp]
@@ -216,15 +218,17 @@ def moe_ragged_dot_dlhs(dZ, offsets, W, dX=None, ws=None):
     return dX
 
 
-def moe_ragged_dot_drhs(X, dZ, offsets, dW=None, dw_dtype=None):
+def moe_ragged_dot_drhs(X, dZ, offsets, dW=None, dw_dtype=None, ws=None):
     """dW[e] = sum over the rows r of group e of dZ[r] X[r]^T -> [E, N, K]."""
     R, K = X.shape
     N = dZ.shape[1]
     E = offsets.numel() - 1
     if dW is None:
         dW = torch.empty((E, N, K), dtype=dw_dtype or X.dtype, device=X.device)
+    ws = _ws(int(_lib.moe_ragged_dot_drhs_workspace_size(E)), X.device, ws)
     _check(_lib.moe_ragged_dot_drhs(_ptr(X), _ptr(dZ), _ptr(offsets), E, R, N, K, _dt(X), _ptr(dW),
-                                    _dt(dW), _stream()), "moe_ragged_dot_drhs")
+                                    _dt(dW), _ptr(ws), ws.numel(), _stream()),
+           "moe_ragged_dot_drhs")
     return dW
 
 

@@ -5,5 +5,6 @@ draws random numbers and lays them out in the library's input layout; it holds
 none of the layer's arithmetic, and it imports neither the GPU library nor the
 CPU oracle.
 """
-from .configs import CONFIGS, LayerConfig, PoolConfig, by_name  # noqa: F401
-from .gen import gen_layer, gen_pool, layer_shapes  # noqa: F401
+from .configs import (CONFIGS, MLP_CONFIGS, ExpertMlpConfig, LayerConfig, PoolConfig,  # noqa: F401
+                      by_name)
+from .gen import gen_expert_mlp, gen_layer, gen_pool, layer_shapes  # noqa: F401

@@ -78,6 +78,33 @@ class PoolConfig:
         return 2 * valid_rows * self.L * self.H * 3
 
 
+@dataclass(frozen=True)
+class ExpertMlpConfig:
+    """Routed rows through the gated expert MLP, forward and backward: T tokens
+    each routed to k distinct experts (uniformly at random, or Zipf(zipf_s) over
+    the experts when k = 1), rows grouped by expert."""
+    name: str
+    T: int
+    d: int          # width the experts act on
+    H: int          # expert hidden width
+    E: int
+    k: int
+    seed: int
+    zipf_s: float = 0.0
+    dtype: str = "bf16"
+
+    @property
+    def R(self) -> int:
+        return self.T * self.k
+
+    def flops_fwd(self) -> int:
+        return 2 * self.R * self.d * self.H * 3          # gate, up, down
+
+    def flops_bwd(self) -> int:
+        # dh, dW_d, dX, dW_gu (the last two over 2H): six matmuls of the forward's size
+        return 2 * self.R * self.d * self.H * 6
+
+
 TINY = LayerConfig("tiny_f32_T256_D256_L128_E16_k2", T=256, D=256, L=128, E=16, k=2, H=128,
                    n_shared=1, Hs=128, dtype="f32", seed=0)
 GRUG67B = LayerConfig("grug67b_bf16_T8192_D2048_E64_k4", T=8192, D=2048, L=0, E=64, k=4,
@@ -90,11 +117,24 @@ LONGCTX = LayerConfig("marin535b_longctx_bf16_T65536_D6144_L3072_E384_k8", T=655
                       L=3072, E=384, k=8, H=3072, n_shared=2, Hs=3072, dtype="bf16", seed=4,
                       hot_frac=0.10, hot_load=5.0)
 
+# The pages' custom-VJP microbench of the Grug MoE expert MLP (Marin: Week of
+# April 26th summary, the paragraph on moving the backward pass onto Triton):
+# 4,096 tokens, hidden 1,024, intermediate 2,048, 64 experts, top-4, bf16.
+GRUG_VJP = ExpertMlpConfig("grug_vjp_bf16_T4096_D1024_H2048_E64_k4", T=4096, d=1024, H=2048,
+                           E=64, k=4, seed=6)
+# The 535B layer's routed rows (8,192 tokens x top-8 of 384 experts on the latent)
+# and one GPU's receiver pool of six local experts.
+MARIN535B_EXPERTS = ExpertMlpConfig("marin535b_experts_bf16_T8192_L3072_H3072_E384_k8", T=8192,
+                                    d=3072, H=3072, E=384, k=8, seed=7)
+EP_SHARE_EXPERTS = ExpertMlpConfig("marin535b_ep_share_experts_bf16_R61440_E6", T=61440, d=3072,
+                                   H=3072, E=6, k=1, seed=8, zipf_s=1.0)
+
 CONFIGS = [TINY, GRUG67B, MARIN535B, EP_SHARE, LONGCTX]
+MLP_CONFIGS = [GRUG_VJP, MARIN535B_EXPERTS, EP_SHARE_EXPERTS]
 
 
 def by_name(name: str):
-    for c in CONFIGS:
+    for c in CONFIGS + MLP_CONFIGS:
         if c.name == name:
             return c
     raise KeyError(name)

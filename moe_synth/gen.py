@@ -26,7 +26,7 @@ import math
 import numpy as np
 import torch
 
-from .configs import LayerConfig, PoolConfig
+from .configs import ExpertMlpConfig, LayerConfig, PoolConfig
 
 # Router bias for the hot experts of the long-context workload.  With the
 # latent RMS-normalised and W_r ~ N(0, 1/L), a token's logits are iid N(0, 1)
@@ -154,3 +154,32 @@ def gen_pool(cfg: PoolConfig, device="cpu", seed: int | None = None) -> dict:
                   dt, chunk_rows=1)
     return dict(X=X, ids=torch.as_tensor(ids, device=device), W_gu=W_gu, W_d=W_d,
                 sender_rows=n_s, sender_dropped=int((n_raw - n_s).sum()))
+
+
+def gen_expert_mlp(cfg: ExpertMlpConfig, device="cpu") -> dict:
+    """Rows grouped by expert for the expert MLP forward and backward.
+
+    Routing: each token draws k distinct experts uniformly at random (k > 1), or
+    one expert with P(e) proportional to 1 / (e + 1)^zipf_s (k = 1); the rows are
+    laid out grouped by expert, so `offsets` [E+1] is the exclusive prefix of the
+    per-expert counts.  X, dY ~ N(0, 1) [R, d]; W_gu ~ N(0, 1/d) [E, 2H, d];
+    W_d ~ N(0, 1/H) [E, d, H]; all stored in cfg.dtype.  Sub-seeds seed*1000 + 0..4
+    in the order routing, X, dY, W_gu, W_d."""
+    dt = _TORCH_DT[cfg.dtype]
+    rng = np.random.default_rng(cfg.seed * 1000)
+    if cfg.k == 1 and cfg.zipf_s > 0:
+        p = 1.0 / np.arange(1, cfg.E + 1) ** cfg.zipf_s
+        ids = rng.choice(cfg.E, size=cfg.T, p=p / p.sum())
+    else:
+        ids = np.argsort(rng.random((cfg.T, cfg.E)), axis=1)[:, :cfg.k].ravel()
+    counts = np.bincount(ids, minlength=cfg.E)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    out = {"counts": counts, "offsets": torch.from_numpy(offsets).to(device)}
+    for i, (name, shape, std) in enumerate([("X", (cfg.R, cfg.d), 1.0),
+                                            ("dY", (cfg.R, cfg.d), 1.0),
+                                            ("W_gu", (cfg.E, 2 * cfg.H, cfg.d), cfg.d ** -0.5),
+                                            ("W_d", (cfg.E, cfg.d, cfg.H), cfg.H ** -0.5)]):
+        g = torch.Generator(device=device)
+        g.manual_seed(cfg.seed * 1000 + 1 + i)
+        out[name] = _normal(shape, std, g, device, dt, chunk_rows=16)
+    return out

@@ -117,7 +117,10 @@ def test_backward_entry_points_reject_bad_arguments(lib):
     lib.moe_ragged_dot_dlhs.argtypes = [vp, vp, i32, i64, vp, i64, i64, C.c_int, vp, vp, sz, vp]
     lib.moe_ragged_dot_dlhs_workspace_size.restype = sz
     lib.moe_ragged_dot_dlhs_workspace_size.argtypes = [i32]
-    lib.moe_ragged_dot_drhs.argtypes = [vp, vp, vp, i32, i64, i64, i64, C.c_int, vp, C.c_int, vp]
+    lib.moe_ragged_dot_drhs.argtypes = [vp, vp, vp, i32, i64, i64, i64, C.c_int, vp, C.c_int, vp, sz,
+                                        vp]
+    lib.moe_ragged_dot_drhs_workspace_size.restype = sz
+    lib.moe_ragged_dot_drhs_workspace_size.argtypes = [i32]
     lib.moe_grouped_ffn_bwd.argtypes = [vp, vp, vp, i32, i64, vp, vp, i64, i64, C.c_int, vp, vp, vp,
                                         C.c_int, vp, sz, vp]
     lib.moe_grouped_ffn_bwd_workspace_size.restype = sz
@@ -134,9 +137,12 @@ def test_backward_entry_points_reject_bad_arguments(lib):
     assert dlhs(W=0) == 1
     assert dlhs(off=a + 4) == 4             # misaligned
     assert dlhs(wsb=need - 1) == 5
+    dneed = lib.moe_ragged_dot_drhs_workspace_size(8)
+    assert dneed >= 9 * 8
     drhs = lambda **kw: lib.moe_ragged_dot_drhs(
         a, a, a, kw.get("E", 8), 1000, kw.get("N", 128), kw.get("K", 64), kw.get("dt", 1),
-        kw.get("dW", a), kw.get("dw", 0), None)
+        kw.get("dW", a), kw.get("dw", 0), a, kw.get("wsb", dneed), None)
+    assert drhs(wsb=dneed - 1) == 5
     assert drhs(K=96) == 2                  # bf16 rows of 192 bytes
     assert drhs(dt=0, dw=1) == 3            # float32 inputs, bfloat16 weight gradient
     assert drhs(dW=0) == 1
