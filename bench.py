@@ -559,15 +559,16 @@ def main():
     from moe_synth import PoolConfig, by_name
 
     dev = torch.device("cuda:0")
+    cfg = data = None
     if args.backward:
         name = args.workload if args.workload != DEFAULT_WORKLOAD else BWD_DEFAULT
-        print(json.dumps(bench_backward(args, by_name(name), M, dev)), flush=True)
-        return
-    cfg = by_name(args.workload)
-    if isinstance(cfg, PoolConfig):
-        line, data = bench_pool(args, cfg, M, dev)
+        line = bench_backward(args, by_name(name), M, dev)
     else:
-        line, data = bench_layer(args, cfg, M, dev)
+        cfg = by_name(args.workload)
+        if isinstance(cfg, PoolConfig):
+            line, data = bench_pool(args, cfg, M, dev)
+        else:
+            line, data = bench_layer(args, cfg, M, dev)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -575,7 +576,7 @@ def main():
         line["copy_1GiB"] = {"ms": round(cms, 4),
                              "GB_per_s": round(2 * (1 << 30) / (cms * 1e-3) / 1e9, 1)}
         del src, dst
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and cfg is not None:
         if isinstance(cfg, PoolConfig):
             line["cpu_baseline"] = cpu_baseline_pool(cfg, data, args.cpu_seconds)
         else:

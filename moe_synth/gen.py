@@ -181,5 +181,7 @@ def gen_expert_mlp(cfg: ExpertMlpConfig, device="cpu") -> dict:
                                             ("W_d", (cfg.E, cfg.d, cfg.H), cfg.H ** -0.5)]):
         g = torch.Generator(device=device)
         g.manual_seed(cfg.seed * 1000 + 1 + i)
-        out[name] = _normal(shape, std, g, device, dt, chunk_rows=16)
+        row_elems = int(np.prod(shape[1:]))
+        out[name] = _normal(shape, std, g, device, dt,
+                            chunk_rows=max(1, (64 << 20) // (4 * row_elems)))
     return out
