@@ -148,3 +148,35 @@ def test_grouped_ffn_bwd_parity(M, dt, dw, E, d, H, kind, scale):
         # gradients reduce them, so those meet the bf16 bound whatever dW's type
         assert_close(gWgu[e], rWgu[e], dt, f"dW_gu[{e}]")
         assert_close(gWd[e], rWd[e], dt, f"dW_d[{e}]")
+
+
+def test_grouped_ffn_bwd_full_size_sampled(M):
+    """The 535B expert shape in the benchmark's launch configuration (65,536 rows, 384
+    experts, d = H = 3,072, bf16, fp32 weight gradients): dX on sampled rows of every part
+    of the row range, and the whole dW_gu and dW_d of one expert, against the oracle."""
+    from moe_synth import by_name, gen_expert_mlp
+
+    cfg = by_name("marin535b_experts_bf16_T8192_L3072_H3072_E384_k8")
+    data = gen_expert_mlp(cfg, DEV)
+    off_d = data["offsets"]
+    dX, dWgu, dWd = M.moe_grouped_ffn_bwd(data["X"], data["dY"], off_d, data["W_gu"],
+                                          data["W_d"], dw_dtype=torch.float32)
+    torch.cuda.synchronize()
+    off = off_d.cpu().numpy()
+    rng = np.random.default_rng(9)
+    e_full = 201                                    # every row of this expert
+    others = rng.choice([e for e in range(cfg.E) if e != e_full], 12, replace=False)
+    experts = np.sort(np.concatenate([[e_full], others]))
+    take = [np.arange(off[e], off[e + 1]) if e == e_full
+            else np.sort(rng.choice(np.arange(off[e], off[e + 1]), 2, replace=False))
+            for e in experts]
+    rows = np.concatenate(take)
+    sub_off = np.concatenate([[0], np.cumsum([len(t) for t in take])]).astype(np.int32)
+    idx = torch.from_numpy(rows).to(DEV)
+    sel = torch.from_numpy(experts).to(DEV)
+    rX, rWgu, rWd = O.expert_rows_bwd(TB.host(data["X"][idx]), TB.host(data["dY"][idx]), sub_off,
+                                      TB.host(data["W_gu"][sel]), TB.host(data["W_d"][sel]))
+    assert_close(dX[idx].float().cpu().numpy(), rX, "bf16", "dX (sampled rows)")
+    j = int(np.flatnonzero(experts == e_full)[0])
+    assert_close(dWgu[e_full].cpu().numpy(), rWgu[j], "bf16", "dW_gu (one whole expert)")
+    assert_close(dWd[e_full].cpu().numpy(), rWd[j], "bf16", "dW_d (one whole expert)")
