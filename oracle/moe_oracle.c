@@ -33,6 +33,9 @@
  *     is an ordered gather, summed in a fixed order, not an atomic scatter-add.
  *   - same summary (hero-run engineering): capacity is an integer computation
  *     so that it can never exceed the buffer by a row.
+ *   - Marin: Week of July 6th summary, the fp8 compute-lane paragraph: fp8 ragged
+ *     dots with E4M3 in the forward and delayed (per-tensor, history-based)
+ *     scaling.
  *   - Marin: Week of April 26th summary, the paragraph on moving the backward
  *     pass onto Triton: the grouped matmul's backward is an input-gradient
  *     grouped GEMM against the transposed weights plus a ragged-contracting
@@ -447,6 +450,100 @@ void moe_ref_expert_rows_bwd(const void *X, const void *dY, int dt, const int32_
     }
     free(hh);
     free(gg);
+}
+
+/* ------------------------------------------------------------------- fp8 --- */
+
+/* OCP 8-bit floating point E4M3 (the format the pages name for the fp8 expert
+ * GEMMs' forward: Marin: Week of July 6th summary, the fp8 compute-lane
+ * paragraph).  Sign bit, 4 exponent bits with bias 7, 3 mantissa bits; exponent
+ * field 0 holds subnormals m/8 * 2^-6; S.1111.111 is NaN and there is no
+ * infinity, so the largest finite magnitude is 1.75 * 2^8 = 448. */
+double moe_ref_e4m3_value(uint8_t code)
+{
+    int s = code >> 7, e = (code >> 3) & 15, m = code & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    double v = e == 0 ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* Nearest E4M3 code to x, ties to the code with an even mantissa, magnitudes
+ * beyond 448 (and infinities) saturated to +-448 (the saturating conversion
+ * used for training tensors), NaN to NaN.  Found by comparing x with every
+ * finite positive code's value, so it follows from the definition alone. */
+uint8_t moe_ref_to_e4m3(double x)
+{
+    if (isnan(x))
+        return 0x7F;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; c++) {
+        double d = fabs(moe_ref_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (uint8_t)(sign | best);
+}
+
+/* Quantisation with a per-tensor scale, decided in float32 as a kernel does:
+ *   q[i] = E4M3( (float)(x[i] * inv_scale) ),  x in dt, the product rounded to
+ * float32 first.  amax (nullable) receives max |x[i]| over the tensor (the value
+ * a delayed-scaling history records), NaN ignored. */
+void moe_ref_quantize_e4m3(const void *x, int dt, int64_t n, float inv_scale, uint8_t *q,
+                           float *amax)
+{
+    float m = 0.0f;
+    for (int64_t i = 0; i < n; i++) {
+        float v = (float)ld(x, dt, i);
+        float p = v * inv_scale;          /* one float32 rounding */
+        q[i] = moe_ref_to_e4m3((double)p);
+        if (fabsf(v) > m)
+            m = fabsf(v);
+    }
+    if (amax)
+        *amax = m;
+}
+
+/* The grouped matmul on E4M3 operands: Z[r] = scale * W[e] X[r] for the rows r of
+ * group e, X [R, K] and W [E, N, K] as E4M3 codes, the products of the decoded
+ * values summed in double (ascending k), Z [R, N] unrounded; rows >= offsets[E]
+ * are not written. */
+void moe_ref_ragged_dot_e4m3(const uint8_t *X, const uint8_t *W, const int32_t *offsets,
+                             int32_t E, int64_t N, int64_t K, double scale, double *Z)
+{
+    for (int32_t e = 0; e < E; e++) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; r++)
+            for (int64_t n = 0; n < N; n++) {
+                double s = 0.0;
+                for (int64_t k = 0; k < K; k++)
+                    s += moe_ref_e4m3_value(X[r * K + k]) *
+                         moe_ref_e4m3_value(W[((int64_t)e * N + n) * K + k]);
+                Z[r * N + n] = scale * s;
+            }
+    }
+}
+
+/* The grouped matmul itself in dt (the forward of the pages' ragged_dot in this
+ * library's convention): Z[r] = W[e] X[r], summed in double, unrounded. */
+void moe_ref_ragged_dot(const void *X, const void *W, int dt, const int32_t *offsets, int32_t E,
+                        int64_t N, int64_t K, double *Z)
+{
+    for (int32_t e = 0; e < E; e++) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = offsets[e]; r < offsets[e + 1]; r++)
+            for (int64_t n = 0; n < N; n++) {
+                double s = 0.0;
+                for (int64_t k = 0; k < K; k++)
+                    s += ld(X, dt, r * K + k) * ld(W, dt, ((int64_t)e * N + n) * K + k);
+                Z[r * N + n] = s;
+            }
+    }
 }
 
 /* Weighted combine, ordered gather: c_t = sum over j = 0..k-1 (ascending) of

@@ -67,6 +67,13 @@ def lib():
             L.moe_ref_permute.argtypes = [vp, i64, i32, i64, vp, vp, vp, vp, i64, vp]
             L.moe_ref_expert_rows.argtypes = [vp, C.c_int, i64, i64, i64, vp, vp, vp, vp, vp]
             L.moe_ref_combine.argtypes = [vp, C.c_int, vp, vp, i64, i32, i64, vp]
+            L.moe_ref_e4m3_value.restype = f64
+            L.moe_ref_e4m3_value.argtypes = [C.c_uint8]
+            L.moe_ref_to_e4m3.restype = C.c_uint8
+            L.moe_ref_to_e4m3.argtypes = [f64]
+            L.moe_ref_quantize_e4m3.argtypes = [vp, C.c_int, i64, C.c_float, vp, vp]
+            L.moe_ref_ragged_dot_e4m3.argtypes = [vp, vp, vp, i32, i64, i64, f64, vp]
+            L.moe_ref_ragged_dot.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
             L.moe_ref_ragged_dlhs.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
             L.moe_ref_ragged_drhs.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
             L.moe_ref_expert_rows_bwd.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp, vp,
@@ -181,6 +188,48 @@ def expert_rows(X, expert, W_gu_e, W_d_e, H: int, want_h: bool = False):
     lib().moe_ref_expert_rows(_p(X), dt, n, d, H, _p(expert), C.cast(gu_ptrs, C.c_void_p),
                               C.cast(d_ptrs, C.c_void_p), _p(Y), _p(h))
     return (Y, h) if want_h else Y
+
+
+def e4m3_value(code: int) -> float:
+    """Value of an OCP E4M3 code (NaN for S.1111.111)."""
+    return lib().moe_ref_e4m3_value(int(code))
+
+
+def to_e4m3(x: float) -> int:
+    """Nearest E4M3 code, ties to even mantissa, saturating at +-448."""
+    return int(lib().moe_ref_to_e4m3(float(x)))
+
+
+def quantize_e4m3(x, inv_scale: float):
+    """x (float32 or bf16 bits) -> (E4M3 codes uint8 of x's shape, amax float)."""
+    x = np.ascontiguousarray(x)
+    q = np.empty(x.shape, np.uint8)
+    amax = C.c_float()
+    lib().moe_ref_quantize_e4m3(_p(x), _dt_of(x), x.size, inv_scale, _p(q), C.byref(amax))
+    return q, amax.value
+
+
+def ragged_dot_e4m3(X, W, offsets, scale: float):
+    """Z[r] = scale * W[e] X[r] on E4M3 codes: X [R, K] uint8, W [E, N, K] uint8 -> Z [R, N]
+    float64 (rows >= offsets[E] NaN)."""
+    X, W = np.ascontiguousarray(X, np.uint8), np.ascontiguousarray(W, np.uint8)
+    E, N, K = W.shape
+    off = _c(offsets, np.int32)
+    assert X.shape[1] == K and off.shape == (E + 1,) and off[-1] <= X.shape[0]
+    Z = np.full((X.shape[0], N), np.nan)
+    lib().moe_ref_ragged_dot_e4m3(_p(X), _p(W), _p(off), E, N, K, float(scale), _p(Z))
+    return Z
+
+
+def ragged_dot(X, W, offsets):
+    """Z[r] = W[e] X[r] in double: X [R, K], W [E, N, K] (float32 or bf16 bits) -> [R, N]."""
+    X, W = np.ascontiguousarray(X), np.ascontiguousarray(W)
+    assert X.dtype == W.dtype
+    E, N, K = W.shape
+    off = _c(offsets, np.int32)
+    Z = np.full((X.shape[0], N), np.nan)
+    lib().moe_ref_ragged_dot(_p(X), _p(W), _dt_of(X), _p(off), E, N, K, _p(Z))
+    return Z
 
 
 def ragged_dlhs(dZ, W, offsets):
