@@ -50,7 +50,8 @@ typedef enum {
     MOE_ELAUNCH = 6     /* a kernel launch failed */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_E4M3 (OCP 8-bit E4M3) is taken only by the fp8 entry points below. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
 
 /* A hipStream_t, passed as an opaque pointer so that this header needs no HIP
  * headers.  NULL is the null stream. */
@@ -137,6 +138,46 @@ moe_status moe_grouped_ffn(const void *X, const int32_t *offsets, int32_t E, int
                            const void *W_gu, const void *W_d, int64_t d, int64_t H,
                            moe_dtype dt, void *Y, void *ws, size_t ws_bytes, moe_stream stream);
 size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt);
+
+/* --------------------------------------------------- ragged dot forward -- */
+/* The grouped matmul on its own (the pages' ragged_dot with group sizes: Marin:
+ * Week of April 26th summary), in this library's output-major convention:
+ *   Z[r] = W[e] X[r]  for the rows r of group e = [offsets[e], offsets[e+1]),
+ *   X (device) [R_phys, K] dt;  W (device) [E, N, K] dt;  Z (device) [R_phys, N] in
+ *   z_dt (dt or MOE_F32).  Rows >= offsets[E] of Z are not touched.
+ *   ws (device) moe_ragged_dot_workspace_size(E) bytes (the row-tile prefix).
+ * Accumulation is float32.  Limits: K a multiple of 64 for MOE_BF16 and of 32 for
+ * MOE_F32, N a multiple of 64, 1 <= E <= 1024, each expert's matrix under 4 GiB. */
+moe_status moe_ragged_dot(const void *X, const int32_t *offsets, int32_t E, int64_t R_phys,
+                          const void *W, int64_t N, int64_t K, moe_dtype dt, void *Z,
+                          moe_dtype z_dt, void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_ragged_dot_workspace_size(int32_t E);
+
+/* -------------------------------------------------------------------- fp8 -- */
+/* OCP E4M3 operands for the expert GEMMs (Marin: Week of July 6th summary, the fp8
+ * compute-lane paragraph: fp8 ragged dots, E4M3 in the forward, delayed scaling).
+ * E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinity,
+ * S.1111.111 = NaN, largest finite magnitude 448.
+ *
+ * moe_quantize_e4m3:  q[i] = E4M3(x[i] * inv_scale), the product rounded to float32
+ *   first, then the nearest code with ties to the even mantissa; magnitudes of 464
+ *   and up (and infinities) saturate to 448, NaN becomes 0x7F.  amax (device, nullable)
+ *   receives max |x[i]| (NaN ignored), the value a delayed-scaling history records.
+ *   x (device) [n] in dt (MOE_F32 or MOE_BF16); q (device) [n] bytes.  No workspace.
+ * moe_ragged_dot_e4m3:  Z[r] = scale * W[e] X[r] with X [R_phys, K] and W [E, N, K] as
+ *   E4M3 codes (scale = the product of the two tensors' dequantisation scales);
+ *   the fp8 matrix instruction sums each run of 64 products below float32 precision
+ *   (measured: within 2^-14 of the sum of their magnitudes), the runs accumulate in
+ *   float32, then scale is applied; Z in z_dt (MOE_BF16 or MOE_F32),
+ *   rows >= offsets[E] untouched.  ws as moe_ragged_dot.  Limits: K a multiple of
+ *   128, N a multiple of 64, 1 <= E <= 1024.
+ * Pointers 16-byte aligned (amax 4-byte); nothing is allocated. */
+moe_status moe_quantize_e4m3(const void *x, moe_dtype dt, int64_t n, float inv_scale, uint8_t *q,
+                             float *amax, moe_stream stream);
+moe_status moe_ragged_dot_e4m3(const uint8_t *Xq, const int32_t *offsets, int32_t E,
+                               int64_t R_phys, const uint8_t *Wq, int64_t N, int64_t K,
+                               float scale, void *Z, moe_dtype z_dt, void *ws, size_t ws_bytes,
+                               moe_stream stream);
 
 /* ------------------------------------------------------- ragged dot VJP -- */
 /* Backward of the grouped matmul (the pages' ragged_dot), split as the pages

@@ -15,7 +15,7 @@ constexpr int kAbiVersion = 1;
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-inline int esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : 4; }
+inline int esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : dt == MOE_E4M3 ? 1 : 4; }
 inline bool dt_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 inline hipStream_t hs(moe_stream s) { return (hipStream_t)s; }
 // A GEMM reduction or output width: whole 128-byte K steps and 32-column blocks.
@@ -208,6 +208,46 @@ moe_status drhs_impl(const void* X, const void* dZ, const int32_t* offsets, int 
     return MOE_OK;
 }
 
+// The grouped matmul Z[r] = scale * W[g] X[r] over row groups (the pages'
+// ragged_dot forward in this library's output-major convention), in bf16, fp32
+// or E4M3 operands; Z in bf16 or fp32.
+moe_status ragged_dot_impl(const void* X, const int32_t* offsets, int E, int64_t R_phys,
+                           const void* W, int64_t N, int64_t K, moe_dtype dt, float scale,
+                           void* Z, bool out_f32, int32_t* tile_prefix, hipStream_t s) {
+    MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tile_prefix, s));
+    GemmParams p = gemm_base();
+    p.group_m = grouped_group_m(R_phys, E);
+    p.a_ahead = grouped_a_ahead(R_phys, E);
+    p.nt_store = kGroupedNtStore;
+    p.offsets = offsets;
+    p.tile_prefix = tile_prefix;
+    p.G = E;
+    p.b_group_rows = N;
+    p.N = N;
+    p.seg[0] = GemmSeg{X, K, W, K, (int32_t)K};
+    p.nseg = 1;
+    p.C = Z;
+    p.ldc = N;
+    p.acc_scale = scale;
+    MOE_TRY(launch_gemm(p, dt, out_f32, EPI_STORE, grouped_tile_bound(R_phys, E, N, EPI_STORE), s));
+    return MOE_OK;
+}
+
+moe_status check_ragged_dot(const void* X, const int32_t* offsets, int32_t E, int64_t R_phys,
+                            const void* W, int64_t N, int64_t K, moe_dtype dt, void* Z,
+                            moe_dtype z_dt, void* ws, size_t ws_bytes) {
+    if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!dt_ok(z_dt)) return MOE_EDTYPE;
+    if (!width_ok(K, dt) || !width_ok(N, z_dt) || N % 64) return MOE_ESHAPE;
+    if (!under4g(gemm_block_m() + 1, K, dt) || !under4g(N + 1, K, dt)) return MOE_ESHAPE;
+    if (!offsets || !W || (R_phys > 0 && (!X || !Z))) return MOE_EINVAL;
+    const void* ptrs[] = {X, offsets, W, Z, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if (!ws || ws_bytes < a256((size_t)(E + 1) * 4)) return MOE_EWORKSPACE;
+    return MOE_OK;
+}
+
 struct LayerBufs {
     float* z_pre;
     void* z_e;
@@ -386,6 +426,47 @@ moe_status moe_grouped_ffn(const void* X, const int32_t* offsets, int32_t E, int
                                      H, dt, h, Y, s);
     if (st != MOE_OK) return st;
     return grouped_down_impl(h, offsets, tp, E, R_phys, W_d, d, H, dt, Y, s);
+}
+
+// ---------------------------------------------------- ragged dot forward ----
+size_t moe_ragged_dot_workspace_size(int32_t E) {
+    if (E < 1) return 0;
+    return a256((size_t)(E + 1) * 4);
+}
+
+moe_status moe_ragged_dot(const void* X, const int32_t* offsets, int32_t E, int64_t R_phys,
+                          const void* W, int64_t N, int64_t K, moe_dtype dt, void* Z,
+                          moe_dtype z_dt, void* ws, size_t ws_bytes, moe_stream stream) {
+    if (!dt_ok(dt) || (z_dt != dt && z_dt != MOE_F32)) return MOE_EDTYPE;
+    moe_status st = check_ragged_dot(X, offsets, E, R_phys, W, N, K, dt, Z, z_dt, ws, ws_bytes);
+    if (st != MOE_OK) return st;
+    return ragged_dot_impl(X, offsets, E, R_phys, W, N, K, dt, 1.0f, Z, z_dt == MOE_F32,
+                           (int32_t*)ws, hs(stream));
+}
+
+moe_status moe_ragged_dot_e4m3(const uint8_t* Xq, const int32_t* offsets, int32_t E,
+                               int64_t R_phys, const uint8_t* Wq, int64_t N, int64_t K,
+                               float scale, void* Z, moe_dtype z_dt, void* ws, size_t ws_bytes,
+                               moe_stream stream) {
+    if (z_dt != MOE_BF16 && z_dt != MOE_F32) return MOE_EDTYPE;
+    if (!(scale == scale)) return MOE_EINVAL;
+    moe_status st = check_ragged_dot(Xq, offsets, E, R_phys, Wq, N, K, MOE_E4M3, Z, z_dt, ws,
+                                     ws_bytes);
+    if (st != MOE_OK) return st;
+    return ragged_dot_impl(Xq, offsets, E, R_phys, Wq, N, K, MOE_E4M3, scale, Z,
+                           z_dt == MOE_F32, (int32_t*)ws, hs(stream));
+}
+
+moe_status moe_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale, uint8_t* q,
+                             float* amax, moe_stream stream) {
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (n < 0) return MOE_ESHAPE;
+    if (!(inv_scale == inv_scale)) return MOE_EINVAL;
+    if (n > 0 && (!x || !q)) return MOE_EINVAL;
+    if ((x && !aligned16(x)) || (q && !aligned16(q)) || ((uintptr_t)amax & 3u))
+        return MOE_EALIGN;
+    MOE_TRY(launch_quantize_e4m3(x, dt, n, inv_scale, q, amax, hs(stream)));
+    return MOE_OK;
 }
 
 // ------------------------------------------------- ragged dot backward ----

@@ -15,6 +15,9 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16;
 
 struct bf16_t { u16 bits; };   // storage tag for bfloat16 arrays
+struct fp8_t { uint8_t bits; }; // storage tag for OCP E4M3 arrays
+typedef int intx8 __attribute__((ext_vector_type(8)));
+typedef int intx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;     // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -37,6 +40,10 @@ template <> struct Elem<float> {
     static constexpr int kBytes = 4;
     __device__ static float load(const float* p, int64_t i) { return p[i]; }
     __device__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<fp8_t> {
+    typedef uint8_t store_t;
+    static constexpr int kBytes = 1;
 };
 template <> struct Elem<bf16_t> {
     typedef u16 store_t;
@@ -72,6 +79,18 @@ template <> struct Mfma<float> {
     }
     __device__ static floatx16 mma(frag a, frag b, floatx16 c) {
         return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+    }
+};
+
+// fp8 (OCP E4M3 operands): v_mfma_f32_32x32x64_f8f6f4 with format 0 for both
+// operands and no block scales, K = 64, each lane holds 32 consecutive k of row
+// lane%32 starting at 32*(lane/32) (checked on the hardware); output as above.
+template <> struct Mfma<fp8_t> {
+    static constexpr int kK = 64;
+    static constexpr int kLaneK = 32;
+    typedef intx8 frag;
+    __device__ static floatx16 mma(frag a, frag b, floatx16 c) {
+        return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
     }
 };
 

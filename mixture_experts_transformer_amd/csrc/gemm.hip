@@ -115,6 +115,17 @@ __device__ __forceinline__ void asm_read(bf16x8& f, const char* p) {
 __device__ __forceinline__ void asm_read(float& f, const char* p) {
     asm volatile("ds_read_b32 %0, %1" : "=v"(f) : "v"(lds_u32(p)));
 }
+// an fp8 fragment: two 16-byte chunks of a row, placed apart by the swizzle (the
+// compiler likewise waits for every LDS DMA before its own reads of them)
+struct I4Pair { intx4 lo, hi; };
+__device__ __forceinline__ void asm_read2(I4Pair& f, const char* p0, const char* p1) {
+    asm volatile("ds_read_b128 %0, %1" : "=v"(f.lo) : "v"(lds_u32(p0)));
+    asm volatile("ds_read_b128 %0, %1" : "=v"(f.hi) : "v"(lds_u32(p1)));
+}
+__device__ __forceinline__ void tie(I4Pair& f) { asm volatile("" : "+v"(f.lo), "+v"(f.hi)); }
+__device__ __forceinline__ intx8 as_frag(const I4Pair& f) {
+    return __builtin_shufflevector(f.lo, f.hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
 __device__ __forceinline__ void tie(TrPair& f) { asm volatile("" : "+v"(f.lo), "+v"(f.hi)); }
 __device__ __forceinline__ void tie(bf16x8& f) { asm volatile("" : "+v"(f)); }
 __device__ __forceinline__ void tie(float& f) { asm volatile("" : "+v"(f)); }
@@ -127,7 +138,6 @@ __device__ __forceinline__ void zero_elem(TrPair& f, int e) {
     if (e < 4) f.lo[e] = 0;
     else f.hi[e - 4] = 0;
 }
-__device__ __forceinline__ void zero_elem(bf16x8& f, int e) { f[e] = (__bf16)0.0f; }
 __device__ __forceinline__ void zero_elem(float& f, int) { f = 0.0f; }
 
 // s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt split over bits 3:0 and 15:14;
@@ -208,9 +218,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr int kSlotsA = AA ? kSlotsFar : kSlotsNear;
     constexpr int kBBase = kSlotsA * kOpBytes;             // B ring offset in LDS
     constexpr int kElem = Elem<T>::kBytes;
+    constexpr bool kFp8 = std::is_same<T, fp8_t>::value;
     constexpr int kSteps = kRowBytes / (Mfma<T>::kK * kElem);   // MFMA k-steps per K step
-    constexpr int kSub = kSteps / 4;                             // k-steps per quarter step
-    static_assert(kSteps % 4 == 0, "a K step splits into four quarters");
+    // k-steps per quarter step.  fp8 has two 64-wide k-steps per K step, so its
+    // quarter q is k-step q / 2 against column block q % 2 (A's fragments are read
+    // in both quarters of a k-step).
+    constexpr int kSub = kFp8 ? 1 : kSteps / 4;
+    static_assert(kFp8 ? kSteps == 2 : kSteps % 4 == 0, "a K step splits into four quarters");
+    static_assert(!kFp8 || LAY == LAY_NN, "fp8 operands are row-major");
     constexpr int kColsOut = (EPI == EPI_SWIGLU) ? kBN / 2 : kBN;
     constexpr int kKStep = kRowBytes / kElem;          // reduction indices per K step
     constexpr int kSubW = kRowBytes / kElem;           // columns per [reduction][column] sub-block
@@ -500,10 +515,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         constexpr int NACT = decltype(nact_c)::value;
         constexpr int NA = NACT > 0 ? NACT : 1;
         typedef typename Mfma<T>::frag Frag;
-        // fragments as read: a transposed bf16 fragment is two halves until fenced
-        constexpr bool kTK = kAT || kBT;
-        using FragA = std::conditional_t<kAT && kElem == 2, TrPair, Frag>;
-        using FragB = std::conditional_t<kBT && kElem == 2, TrPair, Frag>;
+        // fragments as read: a transposed bf16 fragment and an fp8 fragment are two
+        // halves until fenced; these kernels write every fragment read out
+        constexpr bool kTK = kAT || kBT || kFp8;
+        using FragA = std::conditional_t<kFp8, I4Pair,
+                                         std::conditional_t<kAT && kElem == 2, TrPair, Frag>>;
+        using FragB = std::conditional_t<kFp8, I4Pair,
+                                         std::conditional_t<kBT && kElem == 2, TrPair, Frag>>;
         floatx16 acc[NA][2];
 #pragma unroll
         for (int i = 0; i < NACT; i++)
@@ -517,28 +535,42 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             __attribute__((always_inline)) {
             const char* As = lds + sa * kOpBytes + rd_row;
             const char* Bs = lds + kBBase + sb * kOpBytes + rd_row;
-#pragma unroll
-            for (int hs = 0; hs < kSub; hs++) {
-                const int ks = q * kSub + hs;
-                const int kb = ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
-                const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    if constexpr (kBT)
-                        asm_read(fb[hs][j], t_addr(lds + kBBase + sb * kOpBytes, wn * 64 + j * 32, ks));
-                    else if constexpr (kTK)
-                        asm_read(fb[hs][j], Bs + (wn * 64 + j * 32) * kRowBytes + kbyte);
-                    else
-                        fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
-                }
+            if constexpr (kFp8) {
+                // a lane's 32 bytes of k are two chunks of its row, which the
+                // swizzle places apart
+                const int c0 = (q >> 1) * 4 + (lane >> 5) * 2;
+                const int o0 = (c0 ^ fl) << 4, o1 = ((c0 + 1) ^ fl) << 4;
+                const char* rb = Bs + (wn * 64 + (q & 1) * 32) * kRowBytes;
+                asm_read2(fb[0][0], rb + o0, rb + o1);
 #pragma unroll
                 for (int i = 0; i < NACT; i++) {
-                    if constexpr (kAT)
-                        asm_read(fa[hs][i], t_addr(lds + sa * kOpBytes, (wm + 2 * i) * 32, ks));
-                    else if constexpr (kTK)
-                        asm_read(fa[hs][i], As + ((wm + 2 * i) * 32) * kRowBytes + kbyte);
-                    else
-                        fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+                    const char* ra = As + ((wm + 2 * i) * 32) * kRowBytes;
+                    asm_read2(fa[0][i], ra + o0, ra + o1);
+                }
+            } else {
+#pragma unroll
+                for (int hs = 0; hs < kSub; hs++) {
+                    const int ks = q * kSub + hs;
+                    const int kb = ks * Mfma<T>::kK * kElem + (lane >> 5) * Mfma<T>::kLaneK * kElem;
+                    const int kbyte = (((kb >> 4) ^ fl) << 4) | (kb & 15);
+#pragma unroll
+                    for (int j = 0; j < 2; j++) {
+                        if constexpr (kBT)
+                            asm_read(fb[hs][j], t_addr(lds + kBBase + sb * kOpBytes, wn * 64 + j * 32, ks));
+                        else if constexpr (kTK)
+                            asm_read(fb[hs][j], Bs + (wn * 64 + j * 32) * kRowBytes + kbyte);
+                        else
+                            fb[hs][j] = Mfma<T>::lds_frag(Bs + (wn * 64 + j * 32) * kRowBytes, kbyte);
+                    }
+#pragma unroll
+                    for (int i = 0; i < NACT; i++) {
+                        if constexpr (kAT)
+                            asm_read(fa[hs][i], t_addr(lds + sa * kOpBytes, (wm + 2 * i) * 32, ks));
+                        else if constexpr (kTK)
+                            asm_read(fa[hs][i], As + ((wm + 2 * i) * 32) * kRowBytes + kbyte);
+                        else
+                            fa[hs][i] = Mfma<T>::lds_frag(As + ((wm + 2 * i) * 32) * kRowBytes, kbyte);
+                    }
                 }
             }
         };
@@ -546,6 +578,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // the group's end (their LDS rows hold copies of its last row)
         auto mask_sub = [&](int q, FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
             __attribute__((always_inline)) {
+            if constexpr (kRK)
 #pragma unroll
             for (int hs = 0; hs < kSub; hs++) {
                 const int kf = (q * kSub + hs) * Mfma<T>::kK + (lane >> 5) * Mfma<T>::kLaneK;
@@ -574,15 +607,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 }
             }
         };
-        auto mma_sub = [&](FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
+        // the MFMAs of quarter q (fp8: one column block, q % 2)
+        auto mma_sub = [&](int q, FragA (&fa)[kSub][NA], FragB (&fb)[kSub][2])
             __attribute__((always_inline)) {
+            if constexpr (kFp8) {
+                if (q & 1) {
 #pragma unroll
-            for (int hs = 0; hs < kSub; hs++)
+                    for (int i = 0; i < NACT; i++)
+                        acc[i][1] = Mfma<T>::mma(as_frag(fa[0][i]), as_frag(fb[0][0]), acc[i][1]);
+                } else {
 #pragma unroll
-                for (int i = 0; i < NACT; i++)
+                    for (int i = 0; i < NACT; i++)
+                        acc[i][0] = Mfma<T>::mma(as_frag(fa[0][i]), as_frag(fb[0][0]), acc[i][0]);
+                }
+            } else {
 #pragma unroll
-                    for (int j = 0; j < 2; j++)
-                        acc[i][j] = Mfma<T>::mma(as_frag(fa[hs][i]), as_frag(fb[hs][j]), acc[i][j]);
+                for (int hs = 0; hs < kSub; hs++)
+#pragma unroll
+                    for (int i = 0; i < NACT; i++)
+#pragma unroll
+                        for (int j = 0; j < 2; j++)
+                            acc[i][j] = Mfma<T>::mma(as_frag(fa[hs][i]), as_frag(fb[hs][j]), acc[i][j]);
+            }
         };
         // Instruction order within a quarter step: one MFMA, then the fragment
         // reads of the next quarter, then the remaining MFMAs with NV DMA
@@ -590,8 +636,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // complete and the DMA issue never holds up the matrix cores for long.
         auto order_sub = [&](auto nv_c) __attribute__((always_inline)) {
             constexpr int NV = decltype(nv_c)::value;
-            constexpr int kReads = kSub * (NACT + 2);
-            constexpr int kMfmas = kSub * NACT * 2;
+            constexpr int kReads = kFp8 ? 2 * (NACT + 1) : kSub * (NACT + 2);
+            constexpr int kMfmas = kFp8 ? NACT : kSub * NACT * 2;
             constexpr int kPair = NV < kMfmas - 1 ? NV : kMfmas - 1;
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, kReads, 0);
@@ -642,26 +688,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 if (NACT > 0 && kTK) {
                     fence_sub(f0a, f0b);
                     load_sub(sa, sb, 1, f1a, f1b);
-                    mma_sub(f0a, f0b);
+                    mma_sub(0, f0a, f0b);
                     issue_far(kf2, sf2, 0, kDmaPerOperand / 2);
                     fence_sub(f1a, f1b);
                     load_sub(sa, sb, 2, f0a, f0b);
-                    mma_sub(f1a, f1b);
+                    mma_sub(1, f1a, f1b);
                     issue_far(kf2, sf2, kDmaPerOperand / 2, kDmaPerOperand / 2);
                     fence_sub(f0a, f0b);
                     load_sub(sa, sb, 3, f1a, f1b);
-                    mma_sub(f0a, f0b);
+                    mma_sub(2, f0a, f0b);
                 } else if (NACT > 0) {
                     load_sub(sa, sb, 1, f1a, f1b);
-                    mma_sub(f0a, f0b);
+                    mma_sub(0, f0a, f0b);
                     issue_far(kf2, sf2, 0, kDmaPerOperand / 2);
                     order_sub(V2{});
                     load_sub(sa, sb, 2, f0a, f0b);
-                    mma_sub(f1a, f1b);
+                    mma_sub(1, f1a, f1b);
                     issue_far(kf2, sf2, kDmaPerOperand / 2, kDmaPerOperand / 2);
                     order_sub(V2{});
                     load_sub(sa, sb, 3, f1a, f1b);
-                    mma_sub(f0a, f0b);
+                    mma_sub(2, f0a, f0b);
                     order_sub(V0{});
                 } else {
                     issue_far(kf2, sf2, 0, kDmaPerOperand);
@@ -675,11 +721,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 if (NACT > 0 && kTK) {
                     fence_sub(f1a, f1b);
                     load_sub(AA ? sf : sn ^ 1, AA ? sn ^ 1 : sf, 0, f0a, f0b);
-                    mma_sub(f1a, f1b);
+                    mma_sub(3, f1a, f1b);
                     issue_near(min(kt + 2, nk - 1), sn);
                 } else if (NACT > 0) {
                     load_sub(AA ? sf : sn ^ 1, AA ? sn ^ 1 : sf, 0, f0a, f0b);
-                    mma_sub(f1a, f1b);
+                    mma_sub(3, f1a, f1b);
                     issue_near(min(kt + 2, nk - 1), sn);
                     order_sub(VA{});
                 } else {
@@ -694,26 +740,26 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 fence_sub(f0a, f0b);
                 if (tail) mask_sub(0, f0a, f0b);
                 load_sub(sa, sb, 1, f1a, f1b);
-                mma_sub(f0a, f0b);
+                mma_sub(0, f0a, f0b);
                 fence_sub(f1a, f1b);
                 if (tail) mask_sub(1, f1a, f1b);
                 load_sub(sa, sb, 2, f0a, f0b);
-                mma_sub(f1a, f1b);
+                mma_sub(1, f1a, f1b);
                 fence_sub(f0a, f0b);
                 if (tail) mask_sub(2, f0a, f0b);
                 load_sub(sa, sb, 3, f1a, f1b);
-                mma_sub(f0a, f0b);
+                mma_sub(2, f0a, f0b);
                 fence_sub(f1a, f1b);
                 if (tail) mask_sub(3, f1a, f1b);
-                mma_sub(f1a, f1b);
+                mma_sub(3, f1a, f1b);
             } else if (NACT > 0) {
                 load_sub(sa, sb, 1, f1a, f1b);
-                mma_sub(f0a, f0b);
+                mma_sub(0, f0a, f0b);
                 load_sub(sa, sb, 2, f0a, f0b);
-                mma_sub(f1a, f1b);
+                mma_sub(1, f1a, f1b);
                 load_sub(sa, sb, 3, f1a, f1b);
-                mma_sub(f0a, f0b);
-                mma_sub(f1a, f1b);
+                mma_sub(2, f0a, f0b);
+                mma_sub(3, f1a, f1b);
             }
         }
         // every wave is done reading the slots and every DMA has landed
@@ -729,6 +775,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // same hidden columns, so h = silu(G) * U is formed in registers first.
         OutT* const C = (OutT*)p.C;
         const bool nt_out = p.nt_store != 0;
+        if constexpr (kFp8) {
+            const float sc = p.acc_scale;
+#pragma unroll
+            for (int i = 0; i < NACT; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int v = 0; v < 16; v++) acc[i][j][v] *= sc;
+        }
         constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
         // write back R staged rows of W columns starting at tile row rbase
         auto store_rows = [&](auto r_c, auto w_c, int rbase, int64_t cbase)
@@ -993,7 +1048,8 @@ hipError_t launch_tile_prefix(const int32_t* offsets, int G, int BM, int32_t* tp
 hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,
                        int64_t max_tiles, hipStream_t s) {
     // the C ABI has checked these already; a violation here is a library bug
-    if (!gemm_offsets_fit(p, in_dt == MOE_BF16 ? 2 : 4)) return hipErrorInvalidValue;
+    if (!gemm_offsets_fit(p, in_dt == MOE_BF16 ? 2 : in_dt == MOE_E4M3 ? 1 : 4))
+        return hipErrorInvalidValue;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
@@ -1005,6 +1061,11 @@ hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int e
     if (p.layout != LAY_NN)
         return in_dt == MOE_BF16 ? launch_bwd<bf16_t>(p, out_f32, epi, (int)grid, s)
                                  : launch_bwd<float>(p, out_f32, epi, (int)grid, s);
+    if (in_dt == MOE_E4M3) {
+        if (epi != EPI_STORE) return hipErrorInvalidValue;    // E4M3 operands: plain stores
+        return out_f32 ? launch_t<fp8_t, float, EPI_STORE>(p, (int)grid, s)
+                       : launch_t<fp8_t, bf16_t, EPI_STORE>(p, (int)grid, s);
+    }
     if (in_dt == MOE_BF16) {
         if (epi == EPI_STORE)
             return out_f32 ? launch_t<bf16_t, float, EPI_STORE>(p, (int)grid, s)

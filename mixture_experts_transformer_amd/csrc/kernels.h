@@ -52,6 +52,7 @@ struct GemmParams {
     int64_t ldc2;
     int32_t layout;              // LAY_*
     const int64_t* xcd_split;    // LAY_DW: [9] tile range of each XCD (device), or nullptr
+    float acc_scale;             // fp8 operands: accumulators times this before the epilogue
 };
 
 int gemm_block_m();
@@ -67,6 +68,10 @@ hipError_t launch_dw_split(const int32_t* offsets, int G, int64_t M, int64_t N, 
                            bool out_f32, int64_t* split, hipStream_t s);
 hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int epi,
                        int64_t max_tiles, hipStream_t s);
+
+// ------------------------------------------------------------------- fp8 ---
+hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale,
+                                uint8_t* q, float* amax, hipStream_t s);
 
 // ----------------------------------------------------------------- route ---
 hipError_t launch_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d, const float* g,

@@ -61,6 +61,16 @@ _lib.moe_grouped_ffn.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, C.c
                                  _sz, _vp]
 _lib.moe_grouped_ffn_workspace_size.restype = _sz
 _lib.moe_grouped_ffn_workspace_size.argtypes = [_i32, _i64, _i64, C.c_int]
+_lib.moe_ragged_dot.restype = C.c_int
+_lib.moe_ragged_dot.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, C.c_int, _vp, C.c_int, _vp,
+                                _sz, _vp]
+_lib.moe_ragged_dot_workspace_size.restype = _sz
+_lib.moe_ragged_dot_workspace_size.argtypes = [_i32]
+_lib.moe_ragged_dot_e4m3.restype = C.c_int
+_lib.moe_ragged_dot_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, _f32, _vp, C.c_int,
+                                     _vp, _sz, _vp]
+_lib.moe_quantize_e4m3.restype = C.c_int
+_lib.moe_quantize_e4m3.argtypes = [_vp, C.c_int, _i64, _f32, _vp, _vp, _vp]
 _lib.moe_ragged_dot_dlhs.restype = C.c_int
 _lib.moe_ragged_dot_dlhs.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, C.c_int, _vp, _vp, _sz,
                                      _vp]
@@ -202,6 +212,44 @@ def moe_grouped_ffn(X, offsets, W_gu, W_d, Y=None, ws=None):
     _check(_lib.moe_grouped_ffn(_ptr(X), _ptr(offsets), E, R, _ptr(W_gu), _ptr(W_d), d, H, _dt(X),
                                 _ptr(Y), _ptr(ws), ws.numel(), _stream()), "moe_grouped_ffn")
     return Y
+
+
+# ----------------------------------------------------- ragged dot forward --
+MOE_E4M3 = 2
+
+
+def moe_ragged_dot(X, offsets, W, Z=None, z_dtype=None, ws=None):
+    """Z[r] = W[e] X[r] for the rows of each group e (W [E, N, K], X [R, K])."""
+    R, K = X.shape
+    E, N, _ = W.shape
+    if Z is None:
+        Z = torch.empty((R, N), dtype=z_dtype or X.dtype, device=X.device)
+    ws = _ws(int(_lib.moe_ragged_dot_workspace_size(E)), X.device, ws)
+    _check(_lib.moe_ragged_dot(_ptr(X), _ptr(offsets), E, R, _ptr(W), N, K, _dt(X), _ptr(Z),
+                               _dt(Z), _ptr(ws), ws.numel(), _stream()), "moe_ragged_dot")
+    return Z
+
+
+def moe_quantize_e4m3(x, inv_scale: float, q=None, amax=None):
+    """E4M3 codes (uint8 tensor of x's shape) of x * inv_scale; amax (float32 [1]) optional."""
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(_lib.moe_quantize_e4m3(_ptr(x), _dt(x), x.numel(), float(inv_scale), _ptr(q),
+                                  _ptr(amax), _stream()), "moe_quantize_e4m3")
+    return q
+
+
+def moe_ragged_dot_e4m3(Xq, offsets, Wq, scale: float, Z=None, z_dtype=torch.bfloat16, ws=None):
+    """Z[r] = scale * W[e] X[r] on E4M3 codes (uint8 tensors Xq [R, K], Wq [E, N, K])."""
+    R, K = Xq.shape
+    E, N, _ = Wq.shape
+    if Z is None:
+        Z = torch.empty((R, N), dtype=z_dtype, device=Xq.device)
+    ws = _ws(int(_lib.moe_ragged_dot_workspace_size(E)), Xq.device, ws)
+    _check(_lib.moe_ragged_dot_e4m3(_ptr(Xq), _ptr(offsets), E, R, _ptr(Wq), N, K, float(scale),
+                                    _ptr(Z), _dt(Z), _ptr(ws), ws.numel(), _stream()),
+           "moe_ragged_dot_e4m3")
+    return Z
 
 
 # --------------------------------------------------------- ragged dot VJP --

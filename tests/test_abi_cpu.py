@@ -156,3 +156,45 @@ def test_backward_entry_points_reject_bad_arguments(lib):
     assert ffn(dWgu=0) == 1
     assert ffn(dw=5) == 3
     assert ffn(wsb=wneed - 1) == 5
+
+
+def test_forward_ragged_dot_and_fp8_entry_points_reject_bad_arguments(lib):
+    vp, i64, i32, sz, f32 = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t, C.c_float
+    lib.moe_ragged_dot_workspace_size.restype = sz
+    lib.moe_ragged_dot_workspace_size.argtypes = [i32]
+    lib.moe_ragged_dot.argtypes = [vp, vp, i32, i64, vp, i64, i64, C.c_int, vp, C.c_int, vp, sz,
+                                   vp]
+    lib.moe_ragged_dot_e4m3.argtypes = [vp, vp, i32, i64, vp, i64, i64, f32, vp, C.c_int, vp, sz,
+                                        vp]
+    lib.moe_quantize_e4m3.argtypes = [vp, C.c_int, i64, f32, vp, vp, vp]
+    a = 4096
+    need = lib.moe_ragged_dot_workspace_size(8)
+    assert need >= 9 * 4 and lib.moe_ragged_dot_workspace_size(0) == 0
+    rd = lambda **kw: lib.moe_ragged_dot(
+        a, a, kw.get("E", 8), 1000, kw.get("W", a), kw.get("N", 128), kw.get("K", 64),
+        kw.get("dt", 1), a, kw.get("zdt", 1), a, kw.get("wsb", need), None)
+    assert rd(E=0) == 2 and rd(E=1025) == 2
+    assert rd(K=96) == 2                    # bf16 rows of 192 bytes
+    assert rd(N=96) == 2                    # not whole 64-column blocks
+    assert rd(dt=0, zdt=1) == 3             # float32 inputs, bfloat16 output
+    assert rd(dt=2) == 3                    # E4M3 goes through its own entry point
+    assert rd(W=0) == 1
+    assert rd(wsb=need - 1) == 5
+    f8 = lambda **kw: lib.moe_ragged_dot_e4m3(
+        kw.get("X", a), a, 8, 1000, a, kw.get("N", 128), kw.get("K", 128), kw.get("s", 1.0), a,
+        kw.get("zdt", 1), a, kw.get("wsb", need), None)
+    assert f8(K=64) == 2                    # E4M3 rows of 64 bytes
+    assert f8(N=32) == 2
+    assert f8(zdt=2) == 3                   # no E4M3 output
+    assert f8(s=float("nan")) == 1
+    assert f8(X=a + 8) == 4
+    assert f8(wsb=need - 1) == 5
+    qz = lambda **kw: lib.moe_quantize_e4m3(
+        kw.get("x", a), kw.get("dt", 1), kw.get("n", 100), kw.get("inv", 1.0), kw.get("q", a),
+        kw.get("amax", a), None)
+    assert qz(dt=2) == 3
+    assert qz(n=-1) == 2
+    assert qz(inv=float("nan")) == 1
+    assert qz(q=0) == 1
+    assert qz(q=a + 1) == 4
+    assert qz(amax=a + 2) == 4
