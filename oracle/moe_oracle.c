@@ -529,6 +529,34 @@ void moe_ref_ragged_dot_e4m3(const uint8_t *X, const uint8_t *W, const int32_t *
     }
 }
 
+/* The gated activation quantised for an E4M3 down projection (the expert MLP of
+ * the fp8 lane; SwiGLU with the exact activation as in the JaxPP paragraph of the
+ * same summary): for each of n rows of gu = [g | u] (2H wide, in dt, gate first),
+ *   h = silu(g) * u in double, rounded once to float32 (hf, the activation a
+ *   float32 kernel holds), q = E4M3( (float)(hf * inv_scale) ) as
+ *   moe_ref_quantize_e4m3 decides it, amax = max |hf|.
+ * h (nullable) receives the double values before the rounding. */
+void moe_ref_swiglu_quantize_e4m3(const void *gu, int dt, int64_t n, int64_t H, float inv_scale,
+                                  uint8_t *q, float *amax, double *h)
+{
+    float m = 0.0f;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t i = 0; i < H; i++) {
+            double g = ld(gu, dt, r * 2 * H + i);
+            double u = ld(gu, dt, r * 2 * H + H + i);
+            double v = g / (1.0 + exp(-g)) * u;
+            float hf = (float)v;
+            float p = hf * inv_scale;     /* one float32 rounding */
+            q[r * H + i] = moe_ref_to_e4m3((double)p);
+            if (fabsf(hf) > m)
+                m = fabsf(hf);
+            if (h)
+                h[r * H + i] = v;
+        }
+    if (amax)
+        *amax = m;
+}
+
 /* The grouped matmul itself in dt (the forward of the pages' ragged_dot in this
  * library's convention): Z[r] = W[e] X[r], summed in double, unrounded. */
 void moe_ref_ragged_dot(const void *X, const void *W, int dt, const int32_t *offsets, int32_t E,

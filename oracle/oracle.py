@@ -72,6 +72,8 @@ def lib():
             L.moe_ref_to_e4m3.restype = C.c_uint8
             L.moe_ref_to_e4m3.argtypes = [f64]
             L.moe_ref_quantize_e4m3.argtypes = [vp, C.c_int, i64, C.c_float, vp, vp]
+            L.moe_ref_swiglu_quantize_e4m3.argtypes = [vp, C.c_int, i64, i64, C.c_float, vp, vp,
+                                                       vp]
             L.moe_ref_ragged_dot_e4m3.argtypes = [vp, vp, vp, i32, i64, i64, f64, vp]
             L.moe_ref_ragged_dot.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
             L.moe_ref_ragged_dlhs.argtypes = [vp, vp, C.c_int, vp, i32, i64, i64, vp]
@@ -219,6 +221,33 @@ def ragged_dot_e4m3(X, W, offsets, scale: float):
     Z = np.full((X.shape[0], N), np.nan)
     lib().moe_ref_ragged_dot_e4m3(_p(X), _p(W), _p(off), E, N, K, float(scale), _p(Z))
     return Z
+
+
+def swiglu_quantize_e4m3(gu, inv_scale: float, want_h: bool = False):
+    """gu [n, 2H] (float32 or bf16 bits, gate half first) -> (q [n, H] E4M3 codes of
+    float32(silu(g) u) * inv_scale, amax = max |float32(silu(g) u)| [, h in double])."""
+    gu = np.ascontiguousarray(gu)
+    n, twoH = gu.shape
+    H = twoH // 2
+    q = np.empty((n, H), np.uint8)
+    h = np.empty((n, H), np.float64) if want_h else None
+    amax = C.c_float()
+    lib().moe_ref_swiglu_quantize_e4m3(_p(gu), _dt_of(gu), n, H, float(inv_scale), _p(q),
+                                       C.byref(amax), _p(h))
+    return (q, amax.value, h) if want_h else (q, amax.value)
+
+
+def expert_mlp_e4m3(Xq, W_gu_q, W_d_q, offsets, scale_gu: float, inv_scale_h: float,
+                    scale_d: float) -> dict:
+    """The gated expert MLP on E4M3 codes, as moe_grouped_ffn_e4m3 defines it: [g | u]
+    = scale_gu W_gu_q[e] Xq[r] stored in bf16, h's codes from swiglu_quantize_e4m3, Y =
+    scale_d W_d_q[e] hq[r] in double.  Rows are those below offsets[E]."""
+    off = _c(offsets, np.int32)
+    R = int(off[-1])
+    gu = to_bf16(ragged_dot_e4m3(Xq[:R], W_gu_q, off, scale_gu)[:R])
+    hq, amax, h = swiglu_quantize_e4m3(gu, inv_scale_h, want_h=True)
+    Y = ragged_dot_e4m3(hq, W_d_q, off, scale_d)
+    return {"gu": gu, "h": h, "hq": hq, "amax_h": amax, "Y": Y}
 
 
 def ragged_dot(X, W, offsets):

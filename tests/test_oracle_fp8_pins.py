@@ -102,3 +102,74 @@ def test_ragged_dot_is_a_block_matmul():
         np.testing.assert_allclose(Z[rows], X[rows].astype(np.float64) @ W[e].T.astype(np.float64),
                                    rtol=1e-13, atol=1e-13)
     assert np.all(np.isnan(Z[11:]))
+
+
+def _torch_h_codes(gu_bf16_bits, inv):
+    """Codes of float32(silu(g) u) * inv by torch's silu and float8_e4m3fn cast, with
+    the saturation the oracle reads (torch gives NaN past 464)."""
+    t = torch.from_numpy(gu_bf16_bits.view(np.int16)).view(torch.bfloat16).double()
+    H = t.shape[1] // 2
+    h32 = (torch.nn.functional.silu(t[:, :H]) * t[:, H:]).float()
+    p = h32 * torch.tensor(inv, dtype=torch.float32)
+    codes = p.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy().copy()
+    big = p.abs().numpy() >= 464
+    codes[big] = np.where(p.numpy()[big] < 0, 0xFE, 0x7E)
+    return codes, float(h32.abs().max()) if h32.numel() else 0.0, h32.numpy()
+
+
+@pytest.mark.parametrize("inv", [1.0, 23.5, 0.01])
+def test_swiglu_quantize_matches_torch_silu_and_cast(inv):
+    g = torch.Generator().manual_seed(7)
+    gu = (torch.randn(37, 2 * 48, generator=g) * 3).to(torch.bfloat16)
+    bits = gu.view(torch.int16).numpy().view(np.uint16)
+    q, amax, h = O.swiglu_quantize_e4m3(bits, inv, want_h=True)
+    ref, ref_amax, h32 = _torch_h_codes(bits, inv)
+    # torch's and the oracle's float32(h) are both the double rounded once, except where
+    # the two silu evaluations differ in the last double bits across a float32 midpoint
+    same = h.astype(np.float32) == h32
+    assert same.mean() > 0.999
+    assert np.array_equal(q[same], ref[same])
+    assert amax == pytest.approx(ref_amax, rel=2 ** -23)
+
+
+def test_swiglu_quantize_gate_first_and_special_values():
+    H = 4
+    g = np.array([[0.0, 10.0, -40.0, 2.0]])
+    u = np.array([[3.0, 1.0, 5.0, 0.0]])
+    bits = O.to_bf16(np.concatenate([g, u], axis=1))
+    q, amax = O.swiglu_quantize_e4m3(bits, 1.0)
+    vals = np.array([O.e4m3_value(c) for c in q.ravel()])
+    # silu(0) = 0; silu(10) u = 10/(1+e^-10) -> 10 in E4M3; silu(-40) ~ -1.7e-16 -> -0;
+    # u = 0 -> 0.  Swapping the halves would give silu(3)*0, silu(1)*10, ... instead.
+    assert vals.tolist() == [0.0, 10.0, 0.0, 0.0]
+    assert q[0, 2] == 0x80
+    assert amax == np.float32(10 / (1 + np.exp(-10.0)))
+
+
+def test_expert_mlp_e4m3_stages_are_block_matmuls():
+    rng = np.random.default_rng(8)
+    sizes = [3, 0, 5]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    E, d, H = 3, 16, 8
+    R = int(off[-1])
+
+    def codes(shape):
+        c = rng.integers(0x20, 0x48, shape).astype(np.uint8)
+        return c | (rng.integers(0, 2, shape) << 7).astype(np.uint8)
+
+    Xq, Wgu, Wd = codes((R, d)), codes((E, 2 * H, d)), codes((E, d, H))
+    sgu, inv_h, sd = 0.03125, 4.0, 0.5
+    out = O.expert_mlp_e4m3(Xq, Wgu, Wd, off, sgu, inv_h, sd)
+    Xd, Wgud, Wdd = torch_decode(Xq), torch_decode(Wgu), torch_decode(Wd)
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        gu = sgu * Xd[rows] @ Wgud[e].T
+        gu_bits = torch.from_numpy(gu).float().to(torch.bfloat16).view(torch.int16).numpy()
+        # float32 then bfloat16 rounds twice; the values here are exact in float32
+        assert np.array_equal(gu.astype(np.float32).astype(np.float64), gu)
+        assert np.array_equal(out["gu"][rows].view(np.int16), gu_bits)
+        ref, _, _ = _torch_h_codes(gu_bits.view(np.uint16), inv_h)
+        assert np.array_equal(out["hq"][rows], ref)
+        np.testing.assert_allclose(out["Y"][rows], sd * torch_decode(ref) @ Wdd[e].T, rtol=1e-13,
+                                   atol=1e-300)
+    assert np.all(np.isnan(out["Y"][R:]))
