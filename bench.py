@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "marin535b_bf16_T8192_D6144_L3072_E384_k8"
 METRIC = "MoE layer fwd TFLOP/s + tokens/s, % of bf16 MFMA peak (1 MI355X)"
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                          # MI355X HBM3E
 GEMM_TILE_M = 256                              # rows per grouped-GEMM tile
 GEMM_SOURCES = ["gemm.hip", "common.h", "kernels.h"]
@@ -50,6 +50,10 @@ def parse():
                     help="time the expert MLP forward + backward (moe_grouped_ffn, "
                          "moe_grouped_ffn_bwd) on an expert-MLP workload instead of the layer "
                          "forward; default workload: the pages' custom-VJP microbench shape")
+    ap.add_argument("--fp8", action="store_true",
+                    help="time the expert MLP forward with E4M3 ragged dots (moe_quantize_e4m3 "
+                         "of the rows, moe_grouped_ffn_e4m3) beside the bf16 one on an expert-MLP "
+                         "workload; default workload: the 535B expert shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (a kernel of known "
                          "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and report "
@@ -547,6 +551,178 @@ def cpu_baseline_backward(cfg, data, target_s: float) -> dict:
                       f"backward in double precision"}
 
 
+FP8_METRIC = ("expert MLP fwd TFLOP/s with E4M3 ragged dots (model FLOPs), % of fp8 MFMA peak "
+              "(1 MI355X)")
+FP8_DEFAULT = "marin535b_experts_bf16_T8192_L3072_H3072_E384_k8"
+
+
+def bench_fp8(args, cfg, M, dev):
+    """The expert MLP forward on E4M3 operands: per step, the rows are quantised
+    (moe_quantize_e4m3, recording their amax) and moe_grouped_ffn_e4m3 runs the gate/up
+    ragged dot, the activation quantised to E4M3 and the down ragged dot.  Delayed
+    scaling: the rows' and h's scales come from the amax history of the warmup steps.
+    The weights are quantised once per optimizer step (timed separately, not part of
+    the step).  The bf16 expert MLP (moe_grouped_ffn) is timed on the same data."""
+    import numpy as np
+    import torch
+
+    from moe_synth import gen_expert_mlp
+
+    data = gen_expert_mlp(cfg, dev)
+    del data["dY"]
+    X, W_gu, W_d, off = data["X"], data["W_gu"], data["W_d"], data["offsets"]
+    R, d, H, E = cfg.R, cfg.d, cfg.H, cfg.E
+    u8 = dict(dtype=torch.uint8, device=dev)
+    Xq, Wguq, Wdq = torch.empty(X.shape, **u8), torch.empty(W_gu.shape, **u8), \
+        torch.empty(W_d.shape, **u8)
+    a_x, a_h, a_gu, a_d = (torch.zeros(1, device=dev) for _ in range(4))
+
+    def quantize_weights():
+        M.moe_quantize_e4m3(W_gu, 1.0, q=Wguq, amax=a_gu)
+        M.moe_quantize_e4m3(W_d, 1.0, q=Wdq, amax=a_d)
+        torch.cuda.synchronize()
+        s_gu, s_d = float(a_gu.item()) / 448.0, float(a_d.item()) / 448.0
+        M.moe_quantize_e4m3(W_gu, 1.0 / s_gu, q=Wguq)
+        M.moe_quantize_e4m3(W_d, 1.0 / s_d, q=Wdq)
+        return s_gu, s_d
+
+    s_gu, s_d = quantize_weights()
+    wq_ms = time_ms(lambda: (M.moe_quantize_e4m3(W_gu, 1.0 / s_gu, q=Wguq, amax=a_gu),
+                             M.moe_quantize_e4m3(W_d, 1.0 / s_d, q=Wdq, amax=a_d)), reps=2)
+    Y = torch.empty_like(X)
+    ws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, R, H), **u8)
+    scale = {"x": 1.0, "h": 1.0}
+    hist = {"x": [], "h": []}
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        M.moe_quantize_e4m3(X, 1.0 / scale["x"], q=Xq, amax=a_x)
+        if ev:
+            ev[1].record()
+        M.moe_grouped_ffn_e4m3(Xq, off, Wguq, Wdq, scale["x"] * s_gu, 1.0 / scale["h"],
+                               scale["h"] * s_d, Y=Y, amax_h=a_h, ws=ws)
+        if ev:
+            ev[2].record()
+
+    # warmup: record the amax history and derive the delayed scales from it
+    for _ in range(max(2, args.warmup)):
+        step()
+        torch.cuda.synchronize()
+        hist["x"].append(float(a_x.item()))
+        hist["h"].append(float(a_h.item()))
+        scale["x"] = max(hist["x"]) / 448.0
+        scale["h"] = max(hist["h"]) / 448.0
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / args.steps
+    q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    mlp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    ff = cfg.flops_fwd()
+    tflops = ff / (ms * 1e-3) / 1e12
+    # saturation of h under the delayed scale (the last step's amax against the history)
+    h_over = float(a_h.item()) / max(hist["h"])
+    # the gate/up ragged dot alone in E4M3 and in bf16, and the bf16 expert MLP
+    gu8 = torch.empty((R, 2 * H), dtype=torch.bfloat16, device=dev)
+    g8_ms = time_ms(lambda: M.moe_ragged_dot_e4m3(Xq, off, Wguq, scale["x"] * s_gu, Z=gu8))
+    g16_ms = time_ms(lambda: M.moe_ragged_dot(X, off, W_gu, Z=gu8))
+    del gu8
+    fws = torch.empty(M.moe_grouped_ffn_workspace_size(E, R, H, X.dtype), **u8)
+    Y16 = torch.empty_like(X)
+    bf16_ms = time_ms(lambda: M.moe_grouped_ffn(X, off, W_gu, W_d, Y=Y16, ws=fws))
+    rel = float((Y.float() - Y16.float()).pow(2).mean().sqrt() / Y16.float().pow(2).mean().sqrt())
+    del fws, Y16
+    mm = 2 * R * 2 * H * d
+    g8_bytes = E * 2 * H * d + R * d + R * 2 * H * 2
+    g16_bytes = E * 2 * H * d * 2 + R * d * 2 + R * 2 * H * 2
+    line = {
+        "metric": FP8_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (model FLOPs)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded; rows ~ N(0,1), weights ~ N(0,1/fan_in) in bf16, uniform "
+                "top-k routing), quantised to E4M3 with per-tensor scales",
+        "config": {"workload": cfg.name, "tokens": cfg.T, "top_k": cfg.k, "rows": R, "width": d,
+                   "expert_hidden": H, "experts": E, "operands": "E4M3",
+                   "intermediate": "[g | u] bf16", "output": "bf16",
+                   "scaling": "per tensor, delayed (warmup amax history)",
+                   "parallelism": "none (1 GPU)"},
+        "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS["fp8"], 2),
+        "stage_ms": {"quantize_rows": round(q_ms, 4), "expert_mlp_e4m3": round(mlp_ms, 4)},
+        "weight_quantization_ms": round(wq_ms, 4),
+        "bf16_expert_mlp_ms": round(bf16_ms, 4),
+        "speedup_vs_bf16": round(bf16_ms / ms, 3),
+        "rel_rms_diff_vs_bf16": round(rel, 5),
+        "h_amax_vs_history": round(h_over, 4),
+        "roofline": gemm_roofline("E4M3 gate/up ragged dot (moe_ragged_dot_e4m3)", mm, g8_bytes,
+                                  g8_ms, "fp8"),
+        "gate_up_ragged_dot": {
+            "e4m3": gemm_roofline("E4M3 gate/up ragged dot", mm, g8_bytes, g8_ms, "fp8"),
+            "bf16": gemm_roofline("bf16 gate/up ragged dot (moe_ragged_dot)", mm, g16_bytes,
+                                  g16_ms, "bf16"),
+            "speedup": round(g16_ms / g8_ms, 3),
+        },
+        "routed_rows": {"per_expert_min": int(data["counts"].min()),
+                        "per_expert_max": int(data["counts"].max())},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_fp8(cfg, data, scale, s_gu, s_d, args.cpu_seconds)
+    return line
+
+
+def cpu_baseline_fp8(cfg, data, scale, s_gu, s_d, target_s: float) -> dict:
+    """The oracle's quantisation of sampled rows and its E4M3 expert MLP over them, for
+    the rows of two experts (whose weights the oracle quantises first, untimed, as the
+    GPU path quantises weights once per optimizer step)."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from oracle import torch_bridge as TB
+
+    counts = data["counts"]
+    off = np.concatenate([[0], np.cumsum(counts)])
+    rng = np.random.default_rng(0)
+    experts = np.sort(rng.choice(np.flatnonzero(counts), min(2, int(np.count_nonzero(counts))),
+                                 replace=False))
+    wgu, _ = O.quantize_e4m3(TB.host(data["W_gu"][experts.tolist()]), 1.0 / s_gu)
+    wd, _ = O.quantize_e4m3(TB.host(data["W_d"][experts.tolist()]), 1.0 / s_d)
+
+    def run(per_expert):
+        take = [np.sort(rng.choice(counts[e], min(per_expert, counts[e]), replace=False))
+                + off[e] for e in experts]
+        rows = np.concatenate(take).astype(np.int64)
+        sub_off = np.concatenate([[0], np.cumsum([len(t) for t in take])]).astype(np.int32)
+        X = TB.host(data["X"][rows])
+        t0 = time.perf_counter()
+        xq, _ = O.quantize_e4m3(X, 1.0 / scale["x"])
+        O.expert_mlp_e4m3(xq, wgu, wd, sub_off, scale["x"] * s_gu, 1.0 / scale["h"],
+                          scale["h"] * s_d)
+        return time.perf_counter() - t0, int(len(rows))
+
+    t, n = run(2)
+    per = max(2, int(2 * target_s / max(t, 1e-3)))
+    t, n = run(per)
+    return {"value": round(n / t, 2), "unit": "rows/s (E4M3 expert MLP forward)",
+            "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)),
+            "kind": "oracle",
+            "sample": f"{n} rows of experts {experts.tolist()} (up to {per} random rows each, "
+                      f"seed 0) of the same workload: the oracle's E4M3 quantisation of the rows "
+                      f"and its E4M3 expert MLP (products of decoded codes summed in double); "
+                      f"the two experts' weights quantised beforehand, untimed"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -563,6 +739,9 @@ def main():
     if args.backward:
         name = args.workload if args.workload != DEFAULT_WORKLOAD else BWD_DEFAULT
         line = bench_backward(args, by_name(name), M, dev)
+    elif args.fp8:
+        name = args.workload if args.workload != DEFAULT_WORKLOAD else FP8_DEFAULT
+        line = bench_fp8(args, by_name(name), M, dev)
     else:
         cfg = by_name(args.workload)
         if isinstance(cfg, PoolConfig):

@@ -179,6 +179,36 @@ moe_status moe_ragged_dot_e4m3(const uint8_t *Xq, const int32_t *offsets, int32_
                                float scale, void *Z, moe_dtype z_dt, void *ws, size_t ws_bytes,
                                moe_stream stream);
 
+/* moe_swiglu_quantize_e4m3:  the expert MLP's gated activation (Marin: Week of July
+ *   6th summary, the JaxPP paragraph: SwiGLU with the exact activation) quantised
+ *   for an E4M3 down projection.  For the rows r < offsets[E] (at most R_phys) of
+ *   gu = [g | u] (device, [R_phys, 2H] in dt, gate columns first):
+ *     h = silu(g) u in float32,  hq[r, c] = E4M3(h * inv_scale) (product rounded to
+ *     float32, then as moe_quantize_e4m3),  amax (device, nullable) = max |h|.
+ *   hq (device) [R_phys, H]; its rows past offsets[E] are not touched.
+ *   Limits: H a multiple of 16, R_phys * H / 16 < 2^31.  No workspace.
+ * moe_grouped_ffn_e4m3:  the gated expert MLP with E4M3 operands in both ragged
+ *   dots (the same paragraph as above: the fp8 ragged dots threaded through the
+ *   expert MLP), for the rows of group e = [offsets[e], offsets[e+1]):
+ *     [g | u] = scale_gu * W_gu_q[e] Xq[r], stored in bf16 (workspace);
+ *     hq = moe_swiglu_quantize_e4m3([g | u], inv_scale_h), amax_h = max |h|;
+ *     Y[r] = scale_d * W_d_q[e] hq[r]  in y_dt (MOE_BF16 or MOE_F32).
+ *   Xq [R_phys, d], W_gu_q [E, 2H, d], W_d_q [E, d, H] E4M3 codes (device).  With
+ *   per-tensor dequantisation scales s: scale_gu = s_X s_Wgu, scale_d = s_h s_Wd,
+ *   inv_scale_h = 1 / s_h, where s_h comes from earlier steps' amax_h (delayed
+ *   scaling).  Rows >= offsets[E] of Y are not touched.  ws (device)
+ *   moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H) bytes.  Limits: d and H
+ *   multiples of 128, 1 <= E <= 1024.  Accumulation as moe_ragged_dot_e4m3. */
+moe_status moe_swiglu_quantize_e4m3(const void *gu, moe_dtype dt, const int32_t *offsets,
+                                    int32_t E, int64_t R_phys, int64_t H, float inv_scale,
+                                    uint8_t *hq, float *amax, moe_stream stream);
+moe_status moe_grouped_ffn_e4m3(const uint8_t *Xq, const int32_t *offsets, int32_t E,
+                                int64_t R_phys, const uint8_t *W_gu_q, const uint8_t *W_d_q,
+                                int64_t d, int64_t H, float scale_gu, float inv_scale_h,
+                                float scale_d, void *Y, moe_dtype y_dt, float *amax_h, void *ws,
+                                size_t ws_bytes, moe_stream stream);
+size_t moe_grouped_ffn_e4m3_workspace_size(int32_t E, int64_t R_phys, int64_t H);
+
 /* ------------------------------------------------------- ragged dot VJP -- */
 /* Backward of the grouped matmul (the pages' ragged_dot), split as the pages
  * split their custom VJP (Marin: Week of April 26th summary, the paragraph on

@@ -469,6 +469,67 @@ moe_status moe_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_s
     return MOE_OK;
 }
 
+moe_status moe_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
+                                    int32_t E, int64_t R_phys, int64_t H, float inv_scale,
+                                    uint8_t* hq, float* amax, moe_stream stream) {
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (E < 1 || E > 1024 || R_phys < 0 || H <= 0 || H % 16) return MOE_ESHAPE;
+    if (R_phys * (H / 16) >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!(inv_scale == inv_scale)) return MOE_EINVAL;
+    if (!offsets || (R_phys > 0 && (!gu || !hq))) return MOE_EINVAL;
+    const void* ptrs[] = {gu, offsets, hq};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if ((uintptr_t)amax & 3u) return MOE_EALIGN;
+    MOE_TRY(launch_swiglu_quantize_e4m3(gu, dt, offsets, E, R_phys, H, inv_scale, hq, amax,
+                                        hs(stream)));
+    return MOE_OK;
+}
+
+size_t moe_grouped_ffn_e4m3_workspace_size(int32_t E, int64_t R_phys, int64_t H) {
+    if (E < 1 || R_phys < 0 || H <= 0) return 0;
+    Carver cv(nullptr);
+    cv.take<int32_t>((size_t)(E + 1) * 4);
+    cv.take<char>((size_t)R_phys * 2 * H * 2);      // [g | u] in bf16
+    cv.take<char>((size_t)R_phys * H);              // h in E4M3
+    return cv.off;
+}
+
+// The gated expert MLP on E4M3 operands: gate/up ragged dot (bf16 out), the
+// activation fused with h's quantisation, down ragged dot.
+moe_status moe_grouped_ffn_e4m3(const uint8_t* Xq, const int32_t* offsets, int32_t E,
+                                int64_t R_phys, const uint8_t* W_gu_q, const uint8_t* W_d_q,
+                                int64_t d, int64_t H, float scale_gu, float inv_scale_h,
+                                float scale_d, void* Y, moe_dtype y_dt, float* amax_h, void* ws,
+                                size_t ws_bytes, moe_stream stream) {
+    if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (y_dt != MOE_BF16 && y_dt != MOE_F32) return MOE_EDTYPE;
+    if (!width_ok(d, MOE_E4M3) || !width_ok(H, MOE_E4M3)) return MOE_ESHAPE;
+    if (!under4g(2 * H + 1, d, MOE_E4M3) || !under4g(d + 1, H, MOE_E4M3)) return MOE_ESHAPE;
+    if (R_phys * (H / 16) >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!(scale_gu == scale_gu) || !(inv_scale_h == inv_scale_h) || !(scale_d == scale_d))
+        return MOE_EINVAL;
+    if (!offsets || !W_gu_q || !W_d_q || (R_phys > 0 && (!Xq || !Y))) return MOE_EINVAL;
+    const void* ptrs[] = {Xq, offsets, W_gu_q, W_d_q, Y, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if ((uintptr_t)amax_h & 3u) return MOE_EALIGN;
+    if (!ws || ws_bytes < moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H))
+        return MOE_EWORKSPACE;
+    Carver cv(ws);
+    int32_t* tp = cv.take<int32_t>((size_t)(E + 1) * 4);
+    void* gu = cv.take<char>((size_t)R_phys * 2 * H * 2);
+    uint8_t* hq = cv.take<uint8_t>((size_t)R_phys * H);
+    hipStream_t s = hs(stream);
+    moe_status st = ragged_dot_impl(Xq, offsets, E, R_phys, W_gu_q, 2 * H, d, MOE_E4M3, scale_gu,
+                                    gu, false, tp, s);
+    if (st != MOE_OK) return st;
+    MOE_TRY(launch_swiglu_quantize_e4m3(gu, MOE_BF16, offsets, E, R_phys, H, inv_scale_h, hq,
+                                        amax_h, s));
+    return ragged_dot_impl(hq, offsets, E, R_phys, W_d_q, d, H, MOE_E4M3, scale_d, Y,
+                           y_dt == MOE_F32, tp, s);
+}
+
 // ------------------------------------------------- ragged dot backward ----
 size_t moe_ragged_dot_dlhs_workspace_size(int32_t E) {
     if (E < 1) return 0;

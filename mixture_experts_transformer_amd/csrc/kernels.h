@@ -72,6 +72,9 @@ hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int e
 // ------------------------------------------------------------------- fp8 ---
 hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale,
                                 uint8_t* q, float* amax, hipStream_t s);
+hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
+                                       int E, int64_t R_phys, int64_t H, float inv_scale,
+                                       uint8_t* hq, float* amax, hipStream_t s);
 
 // ----------------------------------------------------------------- route ---
 hipError_t launch_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d, const float* g,

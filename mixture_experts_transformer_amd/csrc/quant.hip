@@ -5,6 +5,9 @@
 //   q[i] = E4M3(x[i] * inv_scale)   the product rounded to float32 first;
 //   amax = max |x[i]|               (optional; the value the history records)
 //
+// and the same quantisation fused with the expert MLP's gated activation
+// (h = silu(g) u from a [g | u] row), which feeds the E4M3 down projection.
+//
 // HBM-bound: each thread converts 16 elements per pass (16-byte output stores,
 // 32 or 64 bytes of input), grid-strided; the tail past a multiple of 16 is done
 // element by element.
@@ -93,7 +96,67 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, fl
     }
 }
 
+// Gated activation of the expert MLP, quantised for the E4M3 down projection:
+// for the rows r < offsets[E] (clamped to R_phys) of gu = [g | u] (2H wide),
+//   h = silu(g) * u in float32,  hq[r, c] = E4M3(h * inv),  amax = max |h|.
+// One thread per 16 consecutive columns of a row: two 32- or 64-byte loads (the
+// gate and the up half), one 16-byte store.  rows * H / 16 < 2^31 (host-checked).
+template <typename T>
+__global__ __launch_bounds__(256) void swiglu_quantize_kernel(const T* gu, const int32_t* offsets,
+                                                              int E, int64_t R_phys, int H16,
+                                                              float inv, uint8_t* hq,
+                                                              uint32_t* amax_bits) {
+    constexpr int kIn = 16 * (int)sizeof(T) / 16;
+    int64_t rows = offsets[E];
+    rows = rows < 0 ? 0 : rows > R_phys ? R_phys : rows;
+    const uint32_t groups = (uint32_t)rows * (uint32_t)H16;
+    const int64_t H = (int64_t)H16 * 16;
+    float m = 0.0f;
+    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < groups; g += gridDim.x * 256u) {
+        const uint32_t r = g / (uint32_t)H16;
+        const int64_t c = (int64_t)(g - r * (uint32_t)H16) * 16;
+        const T* gate = gu + (int64_t)r * 2 * H + c;
+        u32x4 gv[kIn], uv[kIn];
+#pragma unroll
+        for (int j = 0; j < kIn; j++) {
+            gv[j] = __builtin_nontemporal_load((const u32x4*)gate + j);
+            uv[j] = __builtin_nontemporal_load((const u32x4*)(gate + H) + j);
+        }
+        u32x4 out = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 16; e++) {
+            const float h = silu_f(group_elem<T>(gv, e)) * group_elem<T>(uv, e);
+            m = fmaxf(m, fabsf(h));
+            out[e >> 2] |= e4m3_code(h * inv) << (8 * (e & 3));
+        }
+        *(u32x4*)(hq + (int64_t)r * H + c) = out;
+    }
+    if (amax_bits) {
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
+    }
+}
+
 }  // namespace
+
+hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
+                                       int E, int64_t R_phys, int64_t H, float inv_scale,
+                                       uint8_t* hq, float* amax, hipStream_t s) {
+    uint32_t* ab = (uint32_t*)amax;
+    if (ab) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, ab);
+    if (R_phys <= 0) return hipGetLastError();
+    const int H16 = (int)(H / 16);
+    int64_t grid = (R_phys * H16 + 255) / 256;
+    if (grid > 4096) grid = 4096;
+    if (dt == MOE_BF16)
+        hipLaunchKernelGGL(swiglu_quantize_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
+                           (const bf16_t*)gu, offsets, E, R_phys, H16, inv_scale, hq, ab);
+    else
+        hipLaunchKernelGGL(swiglu_quantize_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s,
+                           (const float*)gu, offsets, E, R_phys, H16, inv_scale, hq, ab);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale,
                                 uint8_t* q, float* amax, hipStream_t s) {

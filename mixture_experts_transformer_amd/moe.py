@@ -71,6 +71,14 @@ _lib.moe_ragged_dot_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, _f32
                                      _vp, _sz, _vp]
 _lib.moe_quantize_e4m3.restype = C.c_int
 _lib.moe_quantize_e4m3.argtypes = [_vp, C.c_int, _i64, _f32, _vp, _vp, _vp]
+_lib.moe_swiglu_quantize_e4m3.restype = C.c_int
+_lib.moe_swiglu_quantize_e4m3.argtypes = [_vp, C.c_int, _vp, _i32, _i64, _i64, _f32, _vp, _vp,
+                                          _vp]
+_lib.moe_grouped_ffn_e4m3.restype = C.c_int
+_lib.moe_grouped_ffn_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _f32, _f32,
+                                      _f32, _vp, C.c_int, _vp, _vp, _sz, _vp]
+_lib.moe_grouped_ffn_e4m3_workspace_size.restype = _sz
+_lib.moe_grouped_ffn_e4m3_workspace_size.argtypes = [_i32, _i64, _i64]
 _lib.moe_ragged_dot_dlhs.restype = C.c_int
 _lib.moe_ragged_dot_dlhs.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, C.c_int, _vp, _vp, _sz,
                                      _vp]
@@ -250,6 +258,42 @@ def moe_ragged_dot_e4m3(Xq, offsets, Wq, scale: float, Z=None, z_dtype=torch.bfl
                                     _ptr(Z), _dt(Z), _ptr(ws), ws.numel(), _stream()),
            "moe_ragged_dot_e4m3")
     return Z
+
+
+def moe_swiglu_quantize_e4m3(gu, offsets, inv_scale: float, hq=None, amax=None):
+    """E4M3 codes of silu(g) u * inv_scale for the rows < offsets[E] of gu = [g | u]
+    ([R, 2H], float32 or bf16); amax (float32 [1]) optional."""
+    R, twoH = gu.shape
+    H = twoH // 2
+    E = offsets.numel() - 1
+    if hq is None:
+        hq = torch.empty((R, H), dtype=torch.uint8, device=gu.device)
+    _check(_lib.moe_swiglu_quantize_e4m3(_ptr(gu), _dt(gu), _ptr(offsets), E, R, H,
+                                         float(inv_scale), _ptr(hq), _ptr(amax), _stream()),
+           "moe_swiglu_quantize_e4m3")
+    return hq
+
+
+def moe_grouped_ffn_e4m3_workspace_size(E: int, R_phys: int, H: int) -> int:
+    return int(_lib.moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H))
+
+
+def moe_grouped_ffn_e4m3(Xq, offsets, W_gu_q, W_d_q, scale_gu: float, inv_scale_h: float,
+                         scale_d: float, Y=None, y_dtype=torch.bfloat16, amax_h=None, ws=None):
+    """The gated expert MLP on E4M3 codes (Xq [R, d], W_gu_q [E, 2H, d], W_d_q [E, d, H]):
+    Y[r] = scale_d W_d_q[e] E4M3(silu(g) u * inv_scale_h), [g | u] = scale_gu W_gu_q[e] Xq[r].
+    The workspace holds [g | u] (bf16) then h's codes."""
+    R, d = Xq.shape
+    E, twoH, _ = W_gu_q.shape
+    H = twoH // 2
+    if Y is None:
+        Y = torch.empty((R, d), dtype=y_dtype, device=Xq.device)
+    ws = _ws(moe_grouped_ffn_e4m3_workspace_size(E, R, H), Xq.device, ws)
+    _check(_lib.moe_grouped_ffn_e4m3(_ptr(Xq), _ptr(offsets), E, R, _ptr(W_gu_q), _ptr(W_d_q), d,
+                                     H, float(scale_gu), float(inv_scale_h), float(scale_d),
+                                     _ptr(Y), _dt(Y), _ptr(amax_h), _ptr(ws), ws.numel(),
+                                     _stream()), "moe_grouped_ffn_e4m3")
+    return Y
 
 
 # --------------------------------------------------------- ragged dot VJP --

@@ -7,4 +7,5 @@ CPU oracle.
 """
 from .configs import (CONFIGS, MLP_CONFIGS, ExpertMlpConfig, LayerConfig, PoolConfig,  # noqa: F401
                       by_name)
-from .gen import gen_expert_mlp, gen_layer, gen_pool, layer_shapes  # noqa: F401
+from .gen import (expert_mlp_routing, gen_expert_mlp, gen_layer, gen_pool, layer_shapes,  # noqa: F401
+                  small_int_tensor)

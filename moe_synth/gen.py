@@ -156,6 +156,40 @@ def gen_pool(cfg: PoolConfig, device="cpu", seed: int | None = None) -> dict:
                 sender_rows=n_s, sender_dropped=int((n_raw - n_s).sum()))
 
 
+def expert_mlp_routing(cfg: ExpertMlpConfig):
+    """Per-expert row counts and offsets [E+1] (int32) of an expert-MLP workload:
+    each token draws k distinct experts uniformly at random (k > 1), or one expert
+    with P(e) proportional to 1 / (e + 1)^zipf_s (k = 1).  Seed cfg.seed * 1000."""
+    rng = np.random.default_rng(cfg.seed * 1000)
+    if cfg.k == 1 and cfg.zipf_s > 0:
+        p = 1.0 / np.arange(1, cfg.E + 1) ** cfg.zipf_s
+        ids = rng.choice(cfg.E, size=cfg.T, p=p / p.sum())
+    else:
+        ids = np.argsort(rng.random((cfg.T, cfg.E)), axis=1)[:, :cfg.k].ravel()
+    counts = np.bincount(ids, minlength=cfg.E)
+    return counts, np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+
+
+SMALL_INT_VALUES = (0.0, 0.5, 1.0, 2.0, 3.0, 4.0)
+
+
+def small_int_tensor(shape, seed: int, device="cpu", dtype=torch.bfloat16):
+    """Values drawn uniformly from +-{0, 1/2, 1, 2, 3, 4} (each exact in bf16 and in
+    E4M3), for matmuls whose partial sums must be exact.  Drawn in 64 MB slices."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    vals = torch.tensor(SMALL_INT_VALUES, dtype=torch.float32, device=device)
+    out = torch.empty(shape, dtype=dtype, device=device)
+    flat = out.view(-1)
+    step = 16 << 20
+    for i in range(0, flat.numel(), step):
+        n = min(step, flat.numel() - i)
+        idx = torch.randint(0, len(SMALL_INT_VALUES), (n,), generator=g, device=device)
+        sign = torch.randint(0, 2, (n,), generator=g, device=device).float() * 2 - 1
+        flat[i:i + n] = (vals[idx] * sign).to(dtype)
+    return out
+
+
 def gen_expert_mlp(cfg: ExpertMlpConfig, device="cpu") -> dict:
     """Rows grouped by expert for the expert MLP forward and backward.
 
@@ -166,14 +200,7 @@ def gen_expert_mlp(cfg: ExpertMlpConfig, device="cpu") -> dict:
     W_d ~ N(0, 1/H) [E, d, H]; all stored in cfg.dtype.  Sub-seeds seed*1000 + 0..4
     in the order routing, X, dY, W_gu, W_d."""
     dt = _TORCH_DT[cfg.dtype]
-    rng = np.random.default_rng(cfg.seed * 1000)
-    if cfg.k == 1 and cfg.zipf_s > 0:
-        p = 1.0 / np.arange(1, cfg.E + 1) ** cfg.zipf_s
-        ids = rng.choice(cfg.E, size=cfg.T, p=p / p.sum())
-    else:
-        ids = np.argsort(rng.random((cfg.T, cfg.E)), axis=1)[:, :cfg.k].ravel()
-    counts = np.bincount(ids, minlength=cfg.E)
-    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    counts, offsets = expert_mlp_routing(cfg)
     out = {"counts": counts, "offsets": torch.from_numpy(offsets).to(device)}
     for i, (name, shape, std) in enumerate([("X", (cfg.R, cfg.d), 1.0),
                                             ("dY", (cfg.R, cfg.d), 1.0),

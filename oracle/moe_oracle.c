@@ -498,6 +498,7 @@ void moe_ref_quantize_e4m3(const void *x, int dt, int64_t n, float inv_scale, ui
                            float *amax)
 {
     float m = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : m)
     for (int64_t i = 0; i < n; i++) {
         float v = (float)ld(x, dt, i);
         float p = v * inv_scale;          /* one float32 rounding */
@@ -540,6 +541,7 @@ void moe_ref_swiglu_quantize_e4m3(const void *gu, int dt, int64_t n, int64_t H, 
                                   uint8_t *q, float *amax, double *h)
 {
     float m = 0.0f;
+#pragma omp parallel for schedule(static) reduction(max : m)
     for (int64_t r = 0; r < n; r++)
         for (int64_t i = 0; i < H; i++) {
             double g = ld(gu, dt, r * 2 * H + i);

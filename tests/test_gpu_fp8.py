@@ -78,7 +78,7 @@ def assert_fp8_close(got, Xq, Wq, off, scale, out, what):
     worst = int(np.argmax(err - allow)) if err.size else 0
     assert np.all(err <= allow), (f"{what}: |err| {err.flat[worst]:.3e} over the bound "
                                   f"{allow.flat[worst]:.3e} (sum|ab| {absum.flat[worst]:.3e})")
-    return ref
+    return ref, absum
 
 
 def _offsets(rng, E, kind, scale):
@@ -169,3 +169,203 @@ def test_fp8_expert_gemm_from_quantised_bf16(M):
     exact = O.ragged_dot(TB.host(X.cpu()), TB.host(W.cpu()), off)
     rel = float(np.sqrt(np.mean((Z.cpu().numpy() - exact) ** 2)) / np.sqrt(np.mean(exact ** 2)))
     assert rel < 0.08, rel
+
+
+_LUT = None
+
+
+def e4m3_values(codes):
+    global _LUT
+    if _LUT is None:
+        _LUT = np.array([O.e4m3_value(c) for c in range(256)])
+    return _LUT[codes]
+
+
+def h_code_window(h, dh, inv):
+    """Decoded values of the E4M3 codes at the two ends of [h - dh, h + dh] * inv (in
+    float32, as the kernels decide them): every h in the window gets a code between."""
+    lo, _ = O.quantize_e4m3(((h - dh) * inv).astype(np.float32), 1.0)
+    hi, _ = O.quantize_e4m3(((h + dh) * inv).astype(np.float32), 1.0)
+    return e4m3_values(lo), e4m3_values(hi)
+
+
+@pytest.mark.parametrize("dt,E,H,kind,scale,inv", [
+    ("bf16", 4, 256, "uniform", 150, 37.0), ("f32", 3, 64, "skewed", 120, 1.0),
+    ("bf16", 6, 48, "sparse", 0, 0.125)])
+def test_swiglu_quantize_e4m3_parity(M, dt, E, H, kind, scale, inv):
+    rng = np.random.default_rng(E * H)
+    off = _offsets(rng, E, kind, scale)
+    R = int(off[-1])
+    R_phys = R + 13
+    g = torch.Generator().manual_seed(E + H)
+    gu = (torch.randn((R_phys, 2 * H), generator=g) * 3).to(TDT[dt])
+    hq = torch.full((R_phys, H), 0x55, dtype=torch.uint8, device=DEV)
+    amax = torch.full((1,), -1.0, device=DEV)
+    M.moe_swiglu_quantize_e4m3(gu.to(DEV), torch.from_numpy(off).to(DEV), inv, hq=hq, amax=amax)
+    torch.cuda.synchronize()
+    q_ref, amax_ref, h = O.swiglu_quantize_e4m3(TB.host(gu)[:R], inv, want_h=True)
+    got = hq.cpu().numpy()
+    # the kernel's float32 silu(g) u is within a few units of the last place of h
+    lo, hi = h_code_window(h, 2.0 ** -20 * np.abs(h), inv)
+    sure = lo == hi
+    assert np.array_equal(got[:R][sure], q_ref[sure]), "codes differ away from a midpoint"
+    v = e4m3_values(got[:R])
+    assert np.all((v >= np.minimum(lo, hi)) & (v <= np.maximum(lo, hi)))
+    assert np.all(got[R:] == 0x55), "rows past offsets[E] were written"
+    assert abs(float(amax.item()) - amax_ref) <= 2.0 ** -20 * amax_ref
+
+
+def _codes(rng, shape, top=0x50):
+    c = rng.integers(0, top, shape).astype(np.uint8)
+    return c | (rng.integers(0, 2, shape) << 7).astype(np.uint8)
+
+
+# E4M3 codes of 0, 1/2, 1, 2, 3, 4: products of two are multiples of 1/4 up to 16, so
+# every partial sum of a gate/up reduction (d <= 4096) is exact in any accumulator the
+# fp8 instruction could use, and [g | u] is exact up to its bf16 storage.
+SMALL_INT_CODES = np.array([0x00, 0x30, 0x38, 0x40, 0x44, 0x48], np.uint8)
+
+
+def _small_int_codes(rng, shape):
+    c = SMALL_INT_CODES[rng.integers(0, len(SMALL_INT_CODES), shape)]
+    return c | (rng.integers(0, 2, shape) << 7).astype(np.uint8)
+
+
+def ws_views(ws, E, R_phys, H):
+    """[g | u] (bf16 bits, int16) and h's codes as moe_grouped_ffn_e4m3 lays them out in
+    its workspace: after the row-tile prefix, each region 256-byte aligned."""
+    base = ((E + 1) * 4 + 255) // 256 * 256
+    gu_bytes = R_phys * 2 * H * 2
+    hq_at = base + (gu_bytes + 255) // 256 * 256
+    return (ws[base:base + gu_bytes].view(torch.int16).view(R_phys, 2 * H),
+            ws[hq_at:hq_at + R_phys * H].view(R_phys, H))
+
+
+def check_ffn_e4m3(Xq, Wgu, Wd, off, sgu, inv_h, sd, Y, ws, amax_h, out, R_phys, ref=None):
+    """The fp8 expert MLP against the oracle, stage by stage, for X and W_gu of small
+    integer values (exact gate/up sums) and a power-of-two scale_gu:
+      [g | u] (read from the workspace) bit for bit;
+      h's codes equal the oracle's except where the kernel's float32 silu(g) u (within
+      2^-20 of h) can cross a rounding midpoint, and there lie between the two codes;
+      amax_h within 2^-20;
+      Y within the E4M3 matmul bound plus, for each such h, |W_d| times the width."""
+    E, twoH, d = Wgu.shape
+    H = twoH // 2
+    R = int(off[-1])
+    if ref is None:
+        ref = O.expert_mlp_e4m3(Xq, Wgu, Wd, off, sgu, inv_h, sd)
+    if isinstance(ws, tuple):                 # rows already taken out
+        gu_gpu, hq_gpu = ws
+    else:
+        gv, hv_ = ws_views(ws, E, R_phys, H)
+        gu_gpu, hq_gpu = gv[:R].cpu().numpy(), hv_[:R].cpu().numpy()
+    bad = gu_gpu.view(np.uint16) != ref["gu"]
+    assert not bad.any(), f"[g | u] differs in {int(bad.sum())} places"
+    lo, hi = h_code_window(ref["h"], 2.0 ** -20 * np.abs(ref["h"]), inv_h)
+    sure = lo == hi
+    assert np.array_equal(hq_gpu[sure], ref["hq"][sure]), "h codes differ away from a midpoint"
+    v = e4m3_values(hq_gpu)
+    assert np.all((v >= np.minimum(lo, hi)) & (v <= np.maximum(lo, hi))), "h code out of window"
+    if amax_h is not None:
+        assert abs(float(amax_h.item()) - ref["amax_h"]) <= 2.0 ** -20 * ref["amax_h"]
+    width = np.abs(hi - lo)
+    Wdd = e4m3_values(Wd)
+    hv = e4m3_values(ref["hq"])
+    slack = np.zeros((R, d))
+    absY = np.zeros((R, d))
+    for e in range(E):
+        rows = slice(off[e], off[e + 1])
+        slack[rows] = abs(sd) * width[rows] @ np.abs(Wdd[e]).T
+        absY[rows] = abs(sd) * (np.abs(hv[rows]) + width[rows]) @ np.abs(Wdd[e]).T
+    got = Y[:R].float().cpu().numpy() if isinstance(Y, torch.Tensor) else Y[:R]
+    err = np.abs(got - ref["Y"][:R])
+    allow = 2.0 ** -12 * absY + slack + STORE_REL[out] * np.abs(ref["Y"][:R])
+    worst = int(np.argmax(err - allow)) if err.size else 0
+    assert np.all(err <= allow), f"Y: |err| {err.flat[worst]:.3e} over {allow.flat[worst]:.3e}"
+    return float(sure.mean()) if sure.size else 1.0
+
+
+@pytest.mark.parametrize("out,E,d,H,kind,scale", [
+    ("bf16", 4, 256, 128, "uniform", 150), ("f32", 3, 128, 384, "skewed", 100),
+    ("bf16", 6, 128, 128, "sparse", 0), ("bf16", 2, 128, 256, "uniform", 700)])
+def test_grouped_ffn_e4m3_parity(M, out, E, d, H, kind, scale):
+    rng = np.random.default_rng(E * d + H)
+    off = _offsets(rng, E, kind, scale)
+    R = int(off[-1])
+    R_phys = R + 19
+    Xq, Wgu = _small_int_codes(rng, (R_phys, d)), _small_int_codes(rng, (E, 2 * H, d))
+    Wd = _codes(rng, (E, d, H))
+    sgu = 2.0 ** -round(math.log2(math.sqrt(d) * 2.6))   # [g | u] ~ 1..2 in RMS
+    inv_h = 16.0                                          # h * inv_h up to a few hundred
+    sd = 2.0 ** -9
+    Y = torch.full((R_phys, d), 9.0, dtype=TDT[out], device=DEV)
+    ws = torch.zeros(M.moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H), dtype=torch.uint8,
+                     device=DEV)
+    amax_h = torch.full((1,), -1.0, device=DEV)
+    M.moe_grouped_ffn_e4m3(torch.from_numpy(Xq).to(DEV), torch.from_numpy(off).to(DEV),
+                           torch.from_numpy(Wgu).to(DEV), torch.from_numpy(Wd).to(DEV), sgu, inv_h,
+                           sd, Y=Y, amax_h=amax_h, ws=ws)
+    torch.cuda.synchronize()
+    sure = check_ffn_e4m3(Xq, Wgu, Wd, off, sgu, inv_h, sd, Y, ws, amax_h, out, R_phys)
+    assert sure > 0.999
+    assert np.all(Y[R:].float().cpu().numpy() == 9.0), "rows past offsets[E] were written"
+
+
+def test_grouped_ffn_e4m3_full_size_sampled(M):
+    """The 535B expert shape in the benchmark's launch configuration (65,536 rows, 384
+    experts, d = H = 3,072), with X and W_gu of small integer values quantised by the
+    library (scale 1) and W_d ~ N(0, 1/H) quantised with its amax: the quantised codes,
+    [g | u], h's codes and Y of every row of one expert and two rows of five others
+    against the oracle, which quantises those rows and experts itself."""
+    from moe_synth import by_name, expert_mlp_routing, small_int_tensor
+
+    cfg = by_name("marin535b_experts_bf16_T8192_L3072_H3072_E384_k8")
+    R, d, H, E = cfg.R, cfg.d, cfg.H, cfg.E
+    counts, off = expert_mlp_routing(cfg)
+    X = small_int_tensor((R, d), 71, DEV)
+    W_gu = small_int_tensor((E, 2 * H, d), 72, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(73)
+    W_d = (torch.randn((E, d, H), generator=g, device=DEV) * H ** -0.5).to(torch.bfloat16)
+    aw = torch.zeros(1, device=DEV)
+    Xq = M.moe_quantize_e4m3(X, 1.0)
+    Wguq = M.moe_quantize_e4m3(W_gu, 1.0)
+    M.moe_quantize_e4m3(W_d, 1.0, q=torch.empty(W_d.shape, dtype=torch.uint8, device=DEV),
+                        amax=aw)
+    torch.cuda.synchronize()
+    sw = float(aw.item()) / 448.0
+    Wdq = M.moe_quantize_e4m3(W_d, 1.0 / sw)
+    sgu, inv_h = 2.0 ** -8, 16.0
+    sd = sw / inv_h
+    ws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, R, H), dtype=torch.uint8,
+                     device=DEV)
+    off_d = torch.from_numpy(off).to(DEV)
+    Y = M.moe_grouped_ffn_e4m3(Xq, off_d, Wguq, Wdq, sgu, inv_h, sd, ws=ws)
+    torch.cuda.synchronize()
+
+    rng = np.random.default_rng(9)
+    e_full = 201
+    others = rng.choice([e for e in range(E) if e != e_full and counts[e] >= 2], 5, replace=False)
+    experts = np.sort(np.concatenate([[e_full], others]))
+    take = [np.arange(off[e], off[e + 1]) if e == e_full
+            else np.sort(rng.choice(np.arange(off[e], off[e + 1]), 2, replace=False))
+            for e in experts]
+    rows = np.concatenate(take)
+    sub_off = np.concatenate([[0], np.cumsum([len(t) for t in take])]).astype(np.int32)
+    idx = torch.from_numpy(rows).to(DEV)
+    sel = torch.from_numpy(experts).to(DEV)
+    # the oracle's own codes from the generator's values
+    xq_o, _ = O.quantize_e4m3(TB.host(X[idx]), 1.0)
+    wgu_o, _ = O.quantize_e4m3(TB.host(W_gu[sel]), 1.0)
+    wd_o, amax_sel = O.quantize_e4m3(TB.host(W_d[sel]), 1.0 / sw)
+    assert amax_sel <= float(aw.item())
+    assert np.array_equal(Xq[idx].cpu().numpy(), xq_o), "X codes"
+    assert np.array_equal(Wguq[sel].cpu().numpy(), wgu_o), "W_gu codes"
+    assert np.array_equal(Wdq[sel].cpu().numpy(), wd_o), "W_d codes"
+    gv, hv = ws_views(ws, E, R, H)
+    ref = O.expert_mlp_e4m3(xq_o, wgu_o, wd_o, sub_off, sgu, inv_h, sd)
+    sure = check_ffn_e4m3(xq_o, wgu_o, wd_o, sub_off, sgu, inv_h, sd,
+                          Y[idx].float().cpu().numpy(),
+                          (gv[idx].cpu().numpy(), hv[idx].cpu().numpy()), None, "bf16",
+                          len(rows), ref)
+    assert sure > 0.999
