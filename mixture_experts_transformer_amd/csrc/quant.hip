@@ -18,25 +18,27 @@ namespace moe {
 
 namespace {
 
-// E4M3 code of a float32 value, from the format's definition: sign, 4 exponent
-// bits with bias 7, 3 mantissa bits, subnormal steps of 2^-9 below 2^-6.  The
-// nearest code, ties to the even mantissa (rintf rounds half to even, and the
-// scalings by powers of two are exact); magnitudes from 464 (the midpoint of 448
-// and the next step, 480) up and infinities saturate to 448; NaN gives 0x7F.
+// E4M3 codes of float32 values by the hardware conversion (v_cvt_pk_fp8_f32:
+// OCP E4M3, the nearest code with ties to the even mantissa), with the two rules
+// it does not apply by itself: magnitudes above 448 saturate to +-448 first (from
+// 464 up the nearest code would not be finite; between 448 and 464 it is 448
+// anyway), and a NaN, which the conversion encodes as 0xFF, becomes 0x7F.  After
+// saturation only NaN gives a byte with all seven low bits set, so adding 1 to
+// each byte's low seven bits carries into bit 7 exactly for NaN bytes, whose sign
+// bit is then cleared.
+__device__ __forceinline__ float e4m3_sat(float x) {
+    return fabsf(x) > 448.0f ? copysignf(448.0f, x) : x;   // NaN passes unchanged
+}
+__device__ __forceinline__ uint32_t e4m3_nan_fix(uint32_t w) {
+    return w & ~(((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u);
+}
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+    const int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(a), e4m3_sat(b), 0, false);
+    return e4m3_nan_fix(
+        (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(c), e4m3_sat(d), w, true));
+}
 __device__ __forceinline__ uint32_t e4m3_code(float x) {
-    const uint32_t u = __float_as_uint(x);
-    const uint32_t sign = (u >> 24) & 0x80u;
-    const float a = fabsf(x);
-    if (a != a) return 0x7Fu;
-    if (a >= 464.0f) return sign | 0x7Eu;
-    if (a < 0.015625f) return sign | (uint32_t)rintf(a * 512.0f);   // 0..8 (8 = 2^-6)
-    int e = (int)((u >> 23) & 0xFFu) - 127;                          // a is a normal float
-    float r = rintf(ldexpf(a, 3 - e));                               // 8..16
-    if (r == 16.0f) {
-        e += 1;
-        r = 8.0f;
-    }
-    return sign | (uint32_t)(((e + 7) << 3) | ((int)r - 8));
+    return e4m3_pack4(x, 0.0f, 0.0f, 0.0f) & 0xFFu;
 }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -60,26 +62,50 @@ template <> __device__ __forceinline__ float group_elem<bf16_t>(const u32x4* in,
 
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
+// max |.| over the block (256 threads) folded into *amax_bits with one atomic;
+// non-negative floats order as their bit patterns.  Every thread must call it.
+__device__ __forceinline__ void block_amax(float m, uint32_t* amax_bits) {
+    __shared__ float red[4];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(amax_bits, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, float inv,
                                                        uint8_t* q, uint32_t* amax_bits) {
     constexpr int kIn = 16 * (int)sizeof(T) / 16;          // 16-byte input vectors per group
     const int64_t groups = n / 16;
+    const int64_t stride = (int64_t)gridDim.x * 256;
     float m = 0.0f;
-    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups;
-         g += (int64_t)gridDim.x * 256) {
-        u32x4 in[kIn];
+    // two groups per pass, both loaded before either is converted
+    for (int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x; g < groups; g += 2 * stride) {
+        const bool two = g + stride < groups;
+        u32x4 in[2][kIn];
 #pragma unroll
-        for (int j = 0; j < kIn; j++)
-            in[j] = __builtin_nontemporal_load((const u32x4*)(x + g * 16) + j);
-        u32x4 out = {0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const float f = group_elem<T>(in, e);
-            m = fmaxf(m, fabsf(f));                           // NaN does not win
-            out[e >> 2] |= e4m3_code(f * inv) << (8 * (e & 3));
+        for (int j = 0; j < kIn; j++) {
+            in[0][j] = __builtin_nontemporal_load((const u32x4*)(x + g * 16) + j);
+            if (two) in[1][j] = __builtin_nontemporal_load((const u32x4*)(x + (g + stride) * 16) + j);
         }
-        __builtin_nontemporal_store(out, (u32x4*)(q + g * 16));
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            if (t == 1 && !two) break;
+            float p[16];
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const float f = group_elem<T>(in[t], e);
+                m = fmaxf(m, fabsf(f));                       // NaN does not win
+                p[e] = f * inv;
+            }
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                out[j] = e4m3_pack4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+            __builtin_nontemporal_store(out, (u32x4*)(q + (g + t * stride) * 16));
+        }
     }
     if (blockIdx.x == 0) {
         for (int64_t i = groups * 16 + threadIdx.x; i < n; i += 256) {
@@ -88,12 +114,7 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, fl
             q[i] = (uint8_t)e4m3_code(f * inv);
         }
     }
-    if (amax_bits) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        // non-negative floats order as their bit patterns
-        if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
-    }
+    if (amax_bits) block_amax(m, amax_bits);
 }
 
 // Gated activation of the expert MLP, quantised for the E4M3 down projection:
@@ -111,31 +132,45 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(const T* gu, const
     rows = rows < 0 ? 0 : rows > R_phys ? R_phys : rows;
     const uint32_t groups = (uint32_t)rows * (uint32_t)H16;
     const int64_t H = (int64_t)H16 * 16;
+    const uint32_t stride = gridDim.x * 256u;
     float m = 0.0f;
-    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < groups; g += gridDim.x * 256u) {
-        const uint32_t r = g / (uint32_t)H16;
-        const int64_t c = (int64_t)(g - r * (uint32_t)H16) * 16;
-        const T* gate = gu + (int64_t)r * 2 * H + c;
-        u32x4 gv[kIn], uv[kIn];
+    // two groups per pass, all four loads issued before either is converted
+    for (uint32_t g = blockIdx.x * 256u + threadIdx.x; g < groups; g += 2 * stride) {
+        const bool two = g + stride < groups;
+        int64_t at[2];
+        u32x4 gv[2][kIn], uv[2][kIn];
 #pragma unroll
-        for (int j = 0; j < kIn; j++) {
-            gv[j] = __builtin_nontemporal_load((const u32x4*)gate + j);
-            uv[j] = __builtin_nontemporal_load((const u32x4*)(gate + H) + j);
+        for (int t = 0; t < 2; t++) {
+            const uint32_t gg = g + t * stride;
+            const uint32_t r = gg / (uint32_t)H16;
+            const int64_t c = (int64_t)(gg - r * (uint32_t)H16) * 16;
+            at[t] = (int64_t)r * H + c;
+            if (t == 1 && !two) break;
+            const T* gate = gu + (int64_t)r * 2 * H + c;
+#pragma unroll
+            for (int j = 0; j < kIn; j++) {
+                gv[t][j] = __builtin_nontemporal_load((const u32x4*)gate + j);
+                uv[t][j] = __builtin_nontemporal_load((const u32x4*)(gate + H) + j);
+            }
         }
-        u32x4 out = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 16; e++) {
-            const float h = silu_f(group_elem<T>(gv, e)) * group_elem<T>(uv, e);
-            m = fmaxf(m, fabsf(h));
-            out[e >> 2] |= e4m3_code(h * inv) << (8 * (e & 3));
+        for (int t = 0; t < 2; t++) {
+            if (t == 1 && !two) break;
+            float p[16];
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const float h = silu_f(group_elem<T>(gv[t], e)) * group_elem<T>(uv[t], e);
+                m = fmaxf(m, fabsf(h));
+                p[e] = h * inv;
+            }
+            u32x4 out;
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                out[j] = e4m3_pack4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+            *(u32x4*)(hq + at[t]) = out;
         }
-        *(u32x4*)(hq + (int64_t)r * H + c) = out;
     }
-    if (amax_bits) {
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-        if ((threadIdx.x & 63) == 0) atomicMax(amax_bits, __float_as_uint(m));
-    }
+    if (amax_bits) block_amax(m, amax_bits);
 }
 
 }  // namespace

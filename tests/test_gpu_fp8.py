@@ -57,7 +57,10 @@ def test_quantize_e4m3_bit_exact(M, dt, n, inv):
     q = M.moe_quantize_e4m3(xt.to(DEV), inv, amax=amax)
     torch.cuda.synchronize()
     got = q.cpu().numpy()
-    assert np.array_equal(got, q_ref), f"{int((got != q_ref).sum())} codes differ"
+    bad = np.flatnonzero(got != q_ref)
+    assert bad.size == 0, (f"{bad.size} codes differ: " + ", ".join(
+        f"x={x[i]!r} (x*inv={np.float32(x[i]) * np.float32(inv)!r}) got {got[i]:#04x} "
+        f"want {q_ref[i]:#04x}" for i in bad[:6]))
     assert float(amax.item()) == (amax_ref if n > 0 else 0.0)
 
 
