@@ -100,6 +100,8 @@ FP8_CASES = [  # out, E, N, K, kind, scale
     ("bf16", 6, 64, 128, "sparse", 0),          # one K step, empty groups
     ("f32", 2, 256, 512, "uniform", 700),       # A's steps ahead (>= 2 row tiles per group)
     ("bf16", 2, 128, 128, "uniform", 4200),     # 8-row-tile swizzle (>= 16 row tiles per group)
+    ("bf16", 1024, 64, 128, "sparse", 0),       # the most groups, two of them non-empty
+    ("f32", 2, 64, 4096, "uniform", 100),       # a long reduction (32 K steps)
 ]
 
 
@@ -372,3 +374,26 @@ def test_grouped_ffn_e4m3_full_size_sampled(M):
                           (gv[idx].cpu().numpy(), hv[idx].cpu().numpy()), None, "bf16",
                           len(rows), ref)
     assert sure > 0.999
+
+
+@pytest.mark.parametrize("R_phys", [0, 37])
+def test_fp8_entry_points_with_no_routed_rows(M, R_phys):
+    """No rows at all, and rows whose groups are all empty: nothing is written past
+    offsets[E] (here 0) and the amax outputs are cleared to zero."""
+    E, d, H = 5, 128, 128
+    off = torch.zeros(E + 1, dtype=torch.int32, device=DEV)
+    Xq = torch.full((R_phys, d), 0x38, dtype=torch.uint8, device=DEV)
+    Wgu = torch.full((E, 2 * H, d), 0x38, dtype=torch.uint8, device=DEV)
+    Wd = torch.full((E, d, H), 0x38, dtype=torch.uint8, device=DEV)
+    Y = torch.full((R_phys, d), 9.0, dtype=torch.bfloat16, device=DEV)
+    Z = torch.full((R_phys, 2 * H), 9.0, dtype=torch.float32, device=DEV)
+    gu = torch.ones((R_phys, 2 * H), dtype=torch.bfloat16, device=DEV)
+    hq = torch.full((R_phys, H), 0x55, dtype=torch.uint8, device=DEV)
+    a1 = torch.full((1,), -1.0, device=DEV)
+    a2 = torch.full((1,), -1.0, device=DEV)
+    M.moe_grouped_ffn_e4m3(Xq, off, Wgu, Wd, 1.0, 1.0, 1.0, Y=Y, amax_h=a1)
+    M.moe_ragged_dot_e4m3(Xq, off, Wgu, 1.0, Z=Z)
+    M.moe_swiglu_quantize_e4m3(gu, off, 1.0, hq=hq, amax=a2)
+    torch.cuda.synchronize()
+    assert bool((Y == 9.0).all()) and bool((Z == 9.0).all()) and bool((hq == 0x55).all())
+    assert float(a1.item()) == 0.0 and float(a2.item()) == 0.0
