@@ -510,6 +510,26 @@ void moe_ref_quantize_e4m3(const void *x, int dt, int64_t n, float inv_scale, ui
         *amax = m;
 }
 
+/* Delayed scaling's state update for one tensor (the train-step state of the fp8
+ * lane in the same summary): the history holds the amax of the last len steps,
+ * newest first.  The update shifts it by one and puts this step's amax first; the
+ * next step's dequantisation scale is m / 448 for m the largest finite entry (the
+ * value that maps to E4M3's largest code), or 1 when m is 0.  scale[1] receives the
+ * quantisation factor 1 / scale[0], rounded to float32. */
+void moe_ref_fp8_scale_update(float *history, int32_t len, float amax, float *scale)
+{
+    for (int32_t i = len - 1; i > 0; i--)
+        history[i] = history[i - 1];
+    if (len > 0)
+        history[0] = amax;
+    float m = 0.0f;
+    for (int32_t i = 0; i < len; i++)
+        if (isfinite(history[i]) && history[i] > m)
+            m = history[i];
+    scale[0] = m > 0.0f ? m / 448.0f : 1.0f;
+    scale[1] = 1.0f / scale[0];
+}
+
 /* The grouped matmul on E4M3 operands: Z[r] = scale * W[e] X[r] for the rows r of
  * group e, X [R, K] and W [E, N, K] as E4M3 codes, the products of the decoded
  * values summed in double (ascending k), Z [R, N] unrounded; rows >= offsets[E]

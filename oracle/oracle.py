@@ -72,6 +72,7 @@ def lib():
             L.moe_ref_to_e4m3.restype = C.c_uint8
             L.moe_ref_to_e4m3.argtypes = [f64]
             L.moe_ref_quantize_e4m3.argtypes = [vp, C.c_int, i64, C.c_float, vp, vp]
+            L.moe_ref_fp8_scale_update.argtypes = [vp, i32, C.c_float, vp]
             L.moe_ref_swiglu_quantize_e4m3.argtypes = [vp, C.c_int, i64, i64, C.c_float, vp, vp,
                                                        vp]
             L.moe_ref_ragged_dot_e4m3.argtypes = [vp, vp, vp, i32, i64, i64, f64, vp]
@@ -209,6 +210,14 @@ def quantize_e4m3(x, inv_scale: float):
     amax = C.c_float()
     lib().moe_ref_quantize_e4m3(_p(x), _dt_of(x), x.size, inv_scale, _p(q), C.byref(amax))
     return q, amax.value
+
+
+def fp8_scale_update(history, amax: float):
+    """Delayed scaling's update: returns (new history [len] float32, scale, 1/scale)."""
+    h = np.array(history, dtype=np.float32)
+    sc = np.zeros(2, np.float32)
+    lib().moe_ref_fp8_scale_update(_p(h), h.size, float(amax), _p(sc))
+    return h, float(sc[0]), float(sc[1])
 
 
 def ragged_dot_e4m3(X, W, offsets, scale: float):

@@ -173,3 +173,15 @@ def test_expert_mlp_e4m3_stages_are_block_matmuls():
         np.testing.assert_allclose(out["Y"][rows], sd * torch_decode(ref) @ Wdd[e].T, rtol=1e-13,
                                    atol=1e-300)
     assert np.all(np.isnan(out["Y"][R:]))
+
+
+def test_delayed_scale_update_by_hand():
+    h, s, inv = O.fp8_scale_update([3.0, 7.0, 1.0, 0.0], 2.0)
+    assert h.tolist() == [2.0, 3.0, 7.0, 1.0]                 # newest first, oldest dropped
+    assert s == np.float32(7.0) / np.float32(448.0) and inv == np.float32(1.0) / np.float32(s)
+    h, s, _ = O.fp8_scale_update([0.0, 0.0], 0.0)
+    assert s == 1.0                                           # nothing seen yet
+    h, s, _ = O.fp8_scale_update([5.0, float("inf")], float("nan"))
+    assert s == np.float32(5.0) / np.float32(448.0)           # non-finite entries ignored
+    h, s, _ = O.fp8_scale_update([448.0 * 3], 896.0)
+    assert h.tolist() == [896.0] and s == 2.0                 # history of one: this amax alone
