@@ -557,12 +557,14 @@ FP8_DEFAULT = "marin535b_experts_bf16_T8192_L3072_H3072_E384_k8"
 
 
 def bench_fp8(args, cfg, M, dev):
-    """The expert MLP forward on E4M3 operands: per step, the rows are quantised
-    (moe_quantize_e4m3, recording their amax) and moe_grouped_ffn_e4m3 runs the gate/up
-    ragged dot, the activation quantised to E4M3 and the down ragged dot.  Delayed
-    scaling: the rows' and h's scales come from the amax history of the warmup steps.
-    The weights are quantised once per optimizer step (timed separately, not part of
-    the step).  The bf16 expert MLP (moe_grouped_ffn) is timed on the same data."""
+    """The expert MLP forward on E4M3 operands with delayed scaling kept on the device:
+    per step, the rows are quantised with the scale their amax history gives
+    (moe_quantize_e4m3, recording this step's amax), moe_grouped_ffn_e4m3 runs the
+    gate/up ragged dot, the activation quantised to E4M3 with h's history scale and the
+    down ragged dot, and moe_fp8_scale_update rolls both histories (16 steps) into the
+    next step's scales.  No host round trip.  The weights are quantised once per
+    optimizer step (timed separately, not part of the step).  The bf16 expert MLP
+    (moe_grouped_ffn) is timed on the same data."""
     import numpy as np
     import torch
 
@@ -573,48 +575,48 @@ def bench_fp8(args, cfg, M, dev):
     X, W_gu, W_d, off = data["X"], data["W_gu"], data["W_d"], data["offsets"]
     R, d, H, E = cfg.R, cfg.d, cfg.H, cfg.E
     u8 = dict(dtype=torch.uint8, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
     Xq, Wguq, Wdq = torch.empty(X.shape, **u8), torch.empty(W_gu.shape, **u8), \
         torch.empty(W_d.shape, **u8)
-    a_x, a_h, a_gu, a_d = (torch.zeros(1, device=dev) for _ in range(4))
+    a_x, a_h, a_gu, a_d = (torch.zeros(1, **f32) for _ in range(4))
+    HIST = 16
+    hist_x, hist_h = torch.zeros(HIST, **f32), torch.zeros(HIST, **f32)
+    hist_gu, hist_d = torch.zeros(1, **f32), torch.zeros(1, **f32)
+    s_x, s_h, s_gu, s_d = (torch.ones(1, **f32) for _ in range(4))
 
     def quantize_weights():
-        M.moe_quantize_e4m3(W_gu, 1.0, q=Wguq, amax=a_gu)
-        M.moe_quantize_e4m3(W_d, 1.0, q=Wdq, amax=a_d)
-        torch.cuda.synchronize()
-        s_gu, s_d = float(a_gu.item()) / 448.0, float(a_d.item()) / 448.0
-        M.moe_quantize_e4m3(W_gu, 1.0 / s_gu, q=Wguq)
-        M.moe_quantize_e4m3(W_d, 1.0 / s_d, q=Wdq)
-        return s_gu, s_d
+        # once per optimizer step, delayed as well: quantised with the scale the last
+        # step's amax gave (a history of one), recording this step's amax
+        M.moe_quantize_e4m3(W_gu, s_gu, q=Wguq, amax=a_gu)
+        M.moe_quantize_e4m3(W_d, s_d, q=Wdq, amax=a_d)
+        M.moe_fp8_scale_update(hist_gu, a_gu, s_gu)
+        M.moe_fp8_scale_update(hist_d, a_d, s_d)
 
-    s_gu, s_d = quantize_weights()
-    wq_ms = time_ms(lambda: (M.moe_quantize_e4m3(W_gu, 1.0 / s_gu, q=Wguq, amax=a_gu),
-                             M.moe_quantize_e4m3(W_d, 1.0 / s_d, q=Wdq, amax=a_d)), reps=2)
+    quantize_weights()                            # the first pass only records the amax
+    wq_ms = time_ms(quantize_weights, reps=2)     # the weights stay as they are, so the
+    quantize_weights()                            # codes match the scales in s_gu, s_d
     Y = torch.empty_like(X)
     ws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, R, H), **u8)
-    scale = {"x": 1.0, "h": 1.0}
-    hist = {"x": [], "h": []}
 
     def step(ev=None):
         if ev:
             ev[0].record()
-        M.moe_quantize_e4m3(X, 1.0 / scale["x"], q=Xq, amax=a_x)
+        M.moe_quantize_e4m3(X, s_x, q=Xq, amax=a_x)
         if ev:
             ev[1].record()
-        M.moe_grouped_ffn_e4m3(Xq, off, Wguq, Wdq, scale["x"] * s_gu, 1.0 / scale["h"],
-                               scale["h"] * s_d, Y=Y, amax_h=a_h, ws=ws)
+        M.moe_grouped_ffn_e4m3(Xq, off, Wguq, Wdq, s_x, s_gu, s_h, s_d, Y=Y, amax_h=a_h, ws=ws)
         if ev:
             ev[2].record()
+        M.moe_fp8_scale_update(hist_x, a_x, s_x)
+        M.moe_fp8_scale_update(hist_h, a_h, s_h)
+        if ev:
+            ev[3].record()
 
-    # warmup: record the amax history and derive the delayed scales from it
+    # warm-up: the first step runs with unit scales and fills the histories
     for _ in range(max(2, args.warmup)):
         step()
-        torch.cuda.synchronize()
-        hist["x"].append(float(a_x.item()))
-        hist["h"].append(float(a_h.item()))
-        scale["x"] = max(hist["x"]) / 448.0
-        scale["h"] = max(hist["h"]) / 448.0
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for s in range(args.steps):
         step(evs[s])
@@ -623,13 +625,17 @@ def bench_fp8(args, cfg, M, dev):
     ms = wall * 1e3 / args.steps
     q_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
     mlp_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    su_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps
     ff = cfg.flops_fwd()
     tflops = ff / (ms * 1e-3) / 1e12
-    # saturation of h under the delayed scale (the last step's amax against the history)
-    h_over = float(a_h.item()) / max(hist["h"])
+    scale = {"x": float(s_x.item()), "h": float(s_h.item())}
+    s_gu_v, s_d_v = float(s_gu.item()), float(s_d.item())
+    # h's last amax against the largest its history held before it (1 = no saturation)
+    hh = hist_h.cpu().numpy()
+    h_over = float(hh[0] / max(hh[1:].max(), 1e-30))
     # the gate/up ragged dot alone in E4M3 and in bf16, and the bf16 expert MLP
     gu8 = torch.empty((R, 2 * H), dtype=torch.bfloat16, device=dev)
-    g8_ms = time_ms(lambda: M.moe_ragged_dot_e4m3(Xq, off, Wguq, scale["x"] * s_gu, Z=gu8))
+    g8_ms = time_ms(lambda: M.moe_ragged_dot_e4m3(Xq, off, Wguq, s_x, s_gu, Z=gu8))
     g16_ms = time_ms(lambda: M.moe_ragged_dot(X, off, W_gu, Z=gu8))
     del gu8
     fws = torch.empty(M.moe_grouped_ffn_workspace_size(E, R, H, X.dtype), **u8)
@@ -657,10 +663,11 @@ def bench_fp8(args, cfg, M, dev):
         "config": {"workload": cfg.name, "tokens": cfg.T, "top_k": cfg.k, "rows": R, "width": d,
                    "expert_hidden": H, "experts": E, "operands": "E4M3",
                    "intermediate": "[g | u] bf16", "output": "bf16",
-                   "scaling": "per tensor, delayed (warmup amax history)",
+                   "scaling": f"per tensor, delayed: amax history of {HIST} steps on the device",
                    "parallelism": "none (1 GPU)"},
         "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS["fp8"], 2),
-        "stage_ms": {"quantize_rows": round(q_ms, 4), "expert_mlp_e4m3": round(mlp_ms, 4)},
+        "stage_ms": {"quantize_rows": round(q_ms, 4), "expert_mlp_e4m3": round(mlp_ms, 4),
+                     "scale_updates": round(su_ms, 4)},
         "weight_quantization_ms": round(wq_ms, 4),
         "bf16_expert_mlp_ms": round(bf16_ms, 4),
         "speedup_vs_bf16": round(bf16_ms / ms, 3),
@@ -678,7 +685,7 @@ def bench_fp8(args, cfg, M, dev):
                         "per_expert_max": int(data["counts"].max())},
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_fp8(cfg, data, scale, s_gu, s_d, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline_fp8(cfg, data, scale, s_gu_v, s_d_v, args.cpu_seconds)
     return line
 
 
@@ -696,8 +703,9 @@ def cpu_baseline_fp8(cfg, data, scale, s_gu, s_d, target_s: float) -> dict:
     rng = np.random.default_rng(0)
     experts = np.sort(rng.choice(np.flatnonzero(counts), min(2, int(np.count_nonzero(counts))),
                                  replace=False))
-    wgu, _ = O.quantize_e4m3(TB.host(data["W_gu"][experts.tolist()]), 1.0 / s_gu)
-    wd, _ = O.quantize_e4m3(TB.host(data["W_d"][experts.tolist()]), 1.0 / s_d)
+    inv = lambda v: float(np.float32(1.0) / np.float32(v))
+    wgu, _ = O.quantize_e4m3(TB.host(data["W_gu"][experts.tolist()]), inv(s_gu))
+    wd, _ = O.quantize_e4m3(TB.host(data["W_d"][experts.tolist()]), inv(s_d))
 
     def run(per_expert):
         take = [np.sort(rng.choice(counts[e], min(per_expert, counts[e]), replace=False))
@@ -706,9 +714,9 @@ def cpu_baseline_fp8(cfg, data, scale, s_gu, s_d, target_s: float) -> dict:
         sub_off = np.concatenate([[0], np.cumsum([len(t) for t in take])]).astype(np.int32)
         X = TB.host(data["X"][rows])
         t0 = time.perf_counter()
-        xq, _ = O.quantize_e4m3(X, 1.0 / scale["x"])
-        O.expert_mlp_e4m3(xq, wgu, wd, sub_off, scale["x"] * s_gu, 1.0 / scale["h"],
-                          scale["h"] * s_d)
+        xq, _ = O.quantize_e4m3(X, inv(scale["x"]))
+        O.expert_mlp_e4m3(xq, wgu, wd, sub_off, float(np.float32(scale["x"]) * np.float32(s_gu)),
+                          inv(scale["h"]), float(np.float32(scale["h"]) * np.float32(s_d)))
         return time.perf_counter() - t0, int(len(rows))
 
     t, n = run(2)

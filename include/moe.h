@@ -159,55 +159,70 @@ size_t moe_ragged_dot_workspace_size(int32_t E);
  * E4M3: sign, 4 exponent bits with bias 7, 3 mantissa bits, no infinity,
  * S.1111.111 = NaN, largest finite magnitude 448.
  *
- * moe_quantize_e4m3:  q[i] = E4M3(x[i] * inv_scale), the product rounded to float32
- *   first, then the nearest code with ties to the even mantissa; magnitudes of 464
- *   and up (and infinities) saturate to 448, NaN becomes 0x7F.  amax (device, nullable)
- *   receives max |x[i]| (NaN ignored), the value a delayed-scaling history records.
- *   x (device) [n] in dt (MOE_F32 or MOE_BF16); q (device) [n] bytes.  No workspace.
- * moe_ragged_dot_e4m3:  Z[r] = scale * W[e] X[r] with X [R_phys, K] and W [E, N, K] as
- *   E4M3 codes (scale = the product of the two tensors' dequantisation scales);
- *   the fp8 matrix instruction sums each run of 64 products below float32 precision
+ * Scales are per tensor and live in device memory, so that a training loop keeps its
+ * delayed-scaling state on the GPU and never waits for the host.  A scale s is a
+ * dequantisation scale: a code c stands for s * E4M3(c).  Every scale pointer below
+ * is a device float (4-byte aligned); NULL means s = 1.
+ *
+ * moe_quantize_e4m3:  q[i] = E4M3(x[i] * inv), inv = 1 / scale[0] rounded to float32,
+ *   the product rounded to float32 first, then the nearest code with ties to the even
+ *   mantissa; magnitudes of 464 and up (and infinities) saturate to 448, NaN becomes
+ *   0x7F.  amax (device, nullable) receives max |x[i]| (NaN ignored), the value the
+ *   delayed-scaling history records.  x (device) [n] in dt (MOE_F32 or MOE_BF16);
+ *   q (device) [n] bytes.  No workspace.
+ * moe_ragged_dot_e4m3:  Z[r] = (scale_x[0] * scale_w[0]) * W[e] X[r] with X [R_phys, K]
+ *   and W [E, N, K] as E4M3 codes (the product of the scales rounded to float32); the
+ *   fp8 matrix instruction sums each run of 64 products below float32 precision
  *   (measured: within 2^-14 of the sum of their magnitudes), the runs accumulate in
- *   float32, then scale is applied; Z in z_dt (MOE_BF16 or MOE_F32),
- *   rows >= offsets[E] untouched.  ws as moe_ragged_dot.  Limits: K a multiple of
- *   128, N a multiple of 64, 1 <= E <= 1024.
- * Pointers 16-byte aligned (amax 4-byte); nothing is allocated. */
-moe_status moe_quantize_e4m3(const void *x, moe_dtype dt, int64_t n, float inv_scale, uint8_t *q,
-                             float *amax, moe_stream stream);
-moe_status moe_ragged_dot_e4m3(const uint8_t *Xq, const int32_t *offsets, int32_t E,
-                               int64_t R_phys, const uint8_t *Wq, int64_t N, int64_t K,
-                               float scale, void *Z, moe_dtype z_dt, void *ws, size_t ws_bytes,
-                               moe_stream stream);
-
-/* moe_swiglu_quantize_e4m3:  the expert MLP's gated activation (Marin: Week of July
- *   6th summary, the JaxPP paragraph: SwiGLU with the exact activation) quantised
- *   for an E4M3 down projection.  For the rows r < offsets[E] (at most R_phys) of
- *   gu = [g | u] (device, [R_phys, 2H] in dt, gate columns first):
- *     h = silu(g) u in float32,  hq[r, c] = E4M3(h * inv_scale) (product rounded to
- *     float32, then as moe_quantize_e4m3),  amax (device, nullable) = max |h|.
+ *   float32, then the scale is applied; Z in z_dt (MOE_BF16 or MOE_F32), rows >=
+ *   offsets[E] untouched.  ws as moe_ragged_dot.  Limits: K a multiple of 128, N a
+ *   multiple of 64, 1 <= E <= 1024.
+ * moe_swiglu_quantize_e4m3:  the expert MLP's gated activation (the JaxPP paragraph of
+ *   the same summary: SwiGLU with the exact activation) quantised for an E4M3 down
+ *   projection.  For the rows r < offsets[E] (at most R_phys) of gu = [g | u] (device,
+ *   [R_phys, 2H] in dt, gate columns first):
+ *     h = silu(g) u in float32,  hq[r, c] = E4M3(h * inv) as moe_quantize_e4m3 with
+ *     scale,  amax (device, nullable) = max |h|.
  *   hq (device) [R_phys, H]; its rows past offsets[E] are not touched.
  *   Limits: H a multiple of 16, R_phys * H / 16 < 2^31.  No workspace.
- * moe_grouped_ffn_e4m3:  the gated expert MLP with E4M3 operands in both ragged
- *   dots (the same paragraph as above: the fp8 ragged dots threaded through the
- *   expert MLP), for the rows of group e = [offsets[e], offsets[e+1]):
- *     [g | u] = scale_gu * W_gu_q[e] Xq[r], stored in bf16 (workspace);
- *     hq = moe_swiglu_quantize_e4m3([g | u], inv_scale_h), amax_h = max |h|;
- *     Y[r] = scale_d * W_d_q[e] hq[r]  in y_dt (MOE_BF16 or MOE_F32).
- *   Xq [R_phys, d], W_gu_q [E, 2H, d], W_d_q [E, d, H] E4M3 codes (device).  With
- *   per-tensor dequantisation scales s: scale_gu = s_X s_Wgu, scale_d = s_h s_Wd,
- *   inv_scale_h = 1 / s_h, where s_h comes from earlier steps' amax_h (delayed
- *   scaling).  Rows >= offsets[E] of Y are not touched.  ws (device)
- *   moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H) bytes.  Limits: d and H
- *   multiples of 128, 1 <= E <= 1024.  Accumulation as moe_ragged_dot_e4m3. */
+ * moe_grouped_ffn_e4m3:  the gated expert MLP with E4M3 operands in both ragged dots
+ *   (the same paragraph: the fp8 ragged dots threaded through the expert MLP), for the
+ *   rows of group e = [offsets[e], offsets[e+1]):
+ *     [g | u] = (scale_x[0] * scale_gu[0]) * W_gu_q[e] Xq[r], stored in bf16 (workspace);
+ *     hq = moe_swiglu_quantize_e4m3([g | u], scale_h), amax_h = max |h|;
+ *     Y[r] = (scale_h[0] * scale_d[0]) * W_d_q[e] hq[r]  in y_dt (MOE_BF16 or MOE_F32).
+ *   Xq [R_phys, d], W_gu_q [E, 2H, d], W_d_q [E, d, H] E4M3 codes (device); scale_x,
+ *   scale_gu, scale_d the scales they were quantised with; scale_h the scale for h
+ *   (from earlier steps' amax_h: delayed scaling).  Rows >= offsets[E] of Y are not
+ *   touched.  ws (device) moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H) bytes.
+ *   Limits: d and H multiples of 128, 1 <= E <= 1024.  Accumulation as
+ *   moe_ragged_dot_e4m3.
+ * moe_fp8_scale_update:  delayed scaling's state update for one tensor.  history
+ *   (device float [len], in/out) holds the amax of the last len steps, newest first;
+ *   it is shifted by one with amax[0] (device) in front, and scale[0] (device, out)
+ *   becomes m / 448 for m the largest finite entry (the value that maps to E4M3's
+ *   largest code), or 1 when m is 0.  1 <= len <= 1024.
+ * Pointers 16-byte aligned unless stated; nothing is allocated; calls on one stream
+ * run in order, so a scale written by moe_fp8_scale_update is the one the next
+ * call on that stream reads. */
+moe_status moe_quantize_e4m3(const void *x, moe_dtype dt, int64_t n, const float *scale,
+                             uint8_t *q, float *amax, moe_stream stream);
+moe_status moe_ragged_dot_e4m3(const uint8_t *Xq, const int32_t *offsets, int32_t E,
+                               int64_t R_phys, const uint8_t *Wq, int64_t N, int64_t K,
+                               const float *scale_x, const float *scale_w, void *Z,
+                               moe_dtype z_dt, void *ws, size_t ws_bytes, moe_stream stream);
 moe_status moe_swiglu_quantize_e4m3(const void *gu, moe_dtype dt, const int32_t *offsets,
-                                    int32_t E, int64_t R_phys, int64_t H, float inv_scale,
+                                    int32_t E, int64_t R_phys, int64_t H, const float *scale,
                                     uint8_t *hq, float *amax, moe_stream stream);
 moe_status moe_grouped_ffn_e4m3(const uint8_t *Xq, const int32_t *offsets, int32_t E,
                                 int64_t R_phys, const uint8_t *W_gu_q, const uint8_t *W_d_q,
-                                int64_t d, int64_t H, float scale_gu, float inv_scale_h,
-                                float scale_d, void *Y, moe_dtype y_dt, float *amax_h, void *ws,
-                                size_t ws_bytes, moe_stream stream);
+                                int64_t d, int64_t H, const float *scale_x,
+                                const float *scale_gu, const float *scale_h,
+                                const float *scale_d, void *Y, moe_dtype y_dt, float *amax_h,
+                                void *ws, size_t ws_bytes, moe_stream stream);
 size_t moe_grouped_ffn_e4m3_workspace_size(int32_t E, int64_t R_phys, int64_t H);
+moe_status moe_fp8_scale_update(float *history, int32_t len, const float *amax, float *scale,
+                                moe_stream stream);
 
 /* ------------------------------------------------------- ragged dot VJP -- */
 /* Backward of the grouped matmul (the pages' ragged_dot), split as the pages

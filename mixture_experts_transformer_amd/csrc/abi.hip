@@ -15,6 +15,7 @@ constexpr int kAbiVersion = 1;
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 inline int esize(moe_dtype dt) { return dt == MOE_BF16 ? 2 : dt == MOE_E4M3 ? 1 : 4; }
 inline bool dt_ok(moe_dtype dt) { return dt == MOE_F32 || dt == MOE_BF16; }
 inline hipStream_t hs(moe_stream s) { return (hipStream_t)s; }
@@ -212,8 +213,9 @@ moe_status drhs_impl(const void* X, const void* dZ, const int32_t* offsets, int 
 // ragged_dot forward in this library's output-major convention), in bf16, fp32
 // or E4M3 operands; Z in bf16 or fp32.
 moe_status ragged_dot_impl(const void* X, const int32_t* offsets, int E, int64_t R_phys,
-                           const void* W, int64_t N, int64_t K, moe_dtype dt, float scale,
-                           void* Z, bool out_f32, int32_t* tile_prefix, hipStream_t s) {
+                           const void* W, int64_t N, int64_t K, moe_dtype dt,
+                           const float* scale_a, const float* scale_b, void* Z, bool out_f32,
+                           int32_t* tile_prefix, hipStream_t s) {
     MOE_TRY(launch_tile_prefix(offsets, E, gemm_block_m(), tile_prefix, s));
     GemmParams p = gemm_base();
     p.group_m = grouped_group_m(R_phys, E);
@@ -228,7 +230,8 @@ moe_status ragged_dot_impl(const void* X, const int32_t* offsets, int E, int64_t
     p.nseg = 1;
     p.C = Z;
     p.ldc = N;
-    p.acc_scale = scale;
+    p.scale_a = scale_a;
+    p.scale_b = scale_b;
     MOE_TRY(launch_gemm(p, dt, out_f32, EPI_STORE, grouped_tile_bound(R_phys, E, N, EPI_STORE), s));
     return MOE_OK;
 }
@@ -440,48 +443,46 @@ moe_status moe_ragged_dot(const void* X, const int32_t* offsets, int32_t E, int6
     if (!dt_ok(dt) || (z_dt != dt && z_dt != MOE_F32)) return MOE_EDTYPE;
     moe_status st = check_ragged_dot(X, offsets, E, R_phys, W, N, K, dt, Z, z_dt, ws, ws_bytes);
     if (st != MOE_OK) return st;
-    return ragged_dot_impl(X, offsets, E, R_phys, W, N, K, dt, 1.0f, Z, z_dt == MOE_F32,
-                           (int32_t*)ws, hs(stream));
+    return ragged_dot_impl(X, offsets, E, R_phys, W, N, K, dt, nullptr, nullptr, Z,
+                           z_dt == MOE_F32, (int32_t*)ws, hs(stream));
 }
 
 moe_status moe_ragged_dot_e4m3(const uint8_t* Xq, const int32_t* offsets, int32_t E,
                                int64_t R_phys, const uint8_t* Wq, int64_t N, int64_t K,
-                               float scale, void* Z, moe_dtype z_dt, void* ws, size_t ws_bytes,
-                               moe_stream stream) {
+                               const float* scale_x, const float* scale_w, void* Z,
+                               moe_dtype z_dt, void* ws, size_t ws_bytes, moe_stream stream) {
     if (z_dt != MOE_BF16 && z_dt != MOE_F32) return MOE_EDTYPE;
-    if (!(scale == scale)) return MOE_EINVAL;
+    if (!aligned4(scale_x) || !aligned4(scale_w)) return MOE_EALIGN;
     moe_status st = check_ragged_dot(Xq, offsets, E, R_phys, Wq, N, K, MOE_E4M3, Z, z_dt, ws,
                                      ws_bytes);
     if (st != MOE_OK) return st;
-    return ragged_dot_impl(Xq, offsets, E, R_phys, Wq, N, K, MOE_E4M3, scale, Z,
+    return ragged_dot_impl(Xq, offsets, E, R_phys, Wq, N, K, MOE_E4M3, scale_x, scale_w, Z,
                            z_dt == MOE_F32, (int32_t*)ws, hs(stream));
 }
 
-moe_status moe_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale, uint8_t* q,
-                             float* amax, moe_stream stream) {
+moe_status moe_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, const float* scale,
+                             uint8_t* q, float* amax, moe_stream stream) {
     if (!dt_ok(dt)) return MOE_EDTYPE;
     if (n < 0) return MOE_ESHAPE;
-    if (!(inv_scale == inv_scale)) return MOE_EINVAL;
     if (n > 0 && (!x || !q)) return MOE_EINVAL;
-    if ((x && !aligned16(x)) || (q && !aligned16(q)) || ((uintptr_t)amax & 3u))
+    if ((x && !aligned16(x)) || (q && !aligned16(q)) || !aligned4(amax) || !aligned4(scale))
         return MOE_EALIGN;
-    MOE_TRY(launch_quantize_e4m3(x, dt, n, inv_scale, q, amax, hs(stream)));
+    MOE_TRY(launch_quantize_e4m3(x, dt, n, scale, q, amax, hs(stream)));
     return MOE_OK;
 }
 
 moe_status moe_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
-                                    int32_t E, int64_t R_phys, int64_t H, float inv_scale,
+                                    int32_t E, int64_t R_phys, int64_t H, const float* scale,
                                     uint8_t* hq, float* amax, moe_stream stream) {
     if (!dt_ok(dt)) return MOE_EDTYPE;
     if (E < 1 || E > 1024 || R_phys < 0 || H <= 0 || H % 16) return MOE_ESHAPE;
     if (R_phys * (H / 16) >= ((int64_t)1 << 31)) return MOE_ESHAPE;
-    if (!(inv_scale == inv_scale)) return MOE_EINVAL;
     if (!offsets || (R_phys > 0 && (!gu || !hq))) return MOE_EINVAL;
     const void* ptrs[] = {gu, offsets, hq};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_EALIGN;
-    if ((uintptr_t)amax & 3u) return MOE_EALIGN;
-    MOE_TRY(launch_swiglu_quantize_e4m3(gu, dt, offsets, E, R_phys, H, inv_scale, hq, amax,
+    if (!aligned4(amax) || !aligned4(scale)) return MOE_EALIGN;
+    MOE_TRY(launch_swiglu_quantize_e4m3(gu, dt, offsets, E, R_phys, H, scale, hq, amax,
                                         hs(stream)));
     return MOE_OK;
 }
@@ -499,21 +500,22 @@ size_t moe_grouped_ffn_e4m3_workspace_size(int32_t E, int64_t R_phys, int64_t H)
 // activation fused with h's quantisation, down ragged dot.
 moe_status moe_grouped_ffn_e4m3(const uint8_t* Xq, const int32_t* offsets, int32_t E,
                                 int64_t R_phys, const uint8_t* W_gu_q, const uint8_t* W_d_q,
-                                int64_t d, int64_t H, float scale_gu, float inv_scale_h,
-                                float scale_d, void* Y, moe_dtype y_dt, float* amax_h, void* ws,
-                                size_t ws_bytes, moe_stream stream) {
+                                int64_t d, int64_t H, const float* scale_x,
+                                const float* scale_gu, const float* scale_h,
+                                const float* scale_d, void* Y, moe_dtype y_dt, float* amax_h,
+                                void* ws, size_t ws_bytes, moe_stream stream) {
     if (E < 1 || E > 1024 || R_phys < 0 || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
     if (y_dt != MOE_BF16 && y_dt != MOE_F32) return MOE_EDTYPE;
     if (!width_ok(d, MOE_E4M3) || !width_ok(H, MOE_E4M3)) return MOE_ESHAPE;
     if (!under4g(2 * H + 1, d, MOE_E4M3) || !under4g(d + 1, H, MOE_E4M3)) return MOE_ESHAPE;
     if (R_phys * (H / 16) >= ((int64_t)1 << 31)) return MOE_ESHAPE;
-    if (!(scale_gu == scale_gu) || !(inv_scale_h == inv_scale_h) || !(scale_d == scale_d))
-        return MOE_EINVAL;
     if (!offsets || !W_gu_q || !W_d_q || (R_phys > 0 && (!Xq || !Y))) return MOE_EINVAL;
     const void* ptrs[] = {Xq, offsets, W_gu_q, W_d_q, Y, ws};
     for (const void* p : ptrs)
         if (p && !aligned16(p)) return MOE_EALIGN;
-    if ((uintptr_t)amax_h & 3u) return MOE_EALIGN;
+    if (!aligned4(amax_h) || !aligned4(scale_x) || !aligned4(scale_gu) || !aligned4(scale_h) ||
+        !aligned4(scale_d))
+        return MOE_EALIGN;
     if (!ws || ws_bytes < moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H))
         return MOE_EWORKSPACE;
     Carver cv(ws);
@@ -521,13 +523,22 @@ moe_status moe_grouped_ffn_e4m3(const uint8_t* Xq, const int32_t* offsets, int32
     void* gu = cv.take<char>((size_t)R_phys * 2 * H * 2);
     uint8_t* hq = cv.take<uint8_t>((size_t)R_phys * H);
     hipStream_t s = hs(stream);
-    moe_status st = ragged_dot_impl(Xq, offsets, E, R_phys, W_gu_q, 2 * H, d, MOE_E4M3, scale_gu,
-                                    gu, false, tp, s);
+    moe_status st = ragged_dot_impl(Xq, offsets, E, R_phys, W_gu_q, 2 * H, d, MOE_E4M3, scale_x,
+                                    scale_gu, gu, false, tp, s);
     if (st != MOE_OK) return st;
-    MOE_TRY(launch_swiglu_quantize_e4m3(gu, MOE_BF16, offsets, E, R_phys, H, inv_scale_h, hq,
-                                        amax_h, s));
-    return ragged_dot_impl(hq, offsets, E, R_phys, W_d_q, d, H, MOE_E4M3, scale_d, Y,
+    MOE_TRY(launch_swiglu_quantize_e4m3(gu, MOE_BF16, offsets, E, R_phys, H, scale_h, hq, amax_h,
+                                        s));
+    return ragged_dot_impl(hq, offsets, E, R_phys, W_d_q, d, H, MOE_E4M3, scale_h, scale_d, Y,
                            y_dt == MOE_F32, tp, s);
+}
+
+moe_status moe_fp8_scale_update(float* history, int32_t len, const float* amax, float* scale,
+                                moe_stream stream) {
+    if (len < 1 || len > 1024) return MOE_ESHAPE;
+    if (!history || !amax || !scale) return MOE_EINVAL;
+    if (!aligned4(history) || !aligned4(amax) || !aligned4(scale)) return MOE_EALIGN;
+    MOE_TRY(launch_fp8_scale_update(history, len, amax, scale, hs(stream)));
+    return MOE_OK;
 }
 
 // ------------------------------------------------- ragged dot backward ----

@@ -776,7 +776,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         OutT* const C = (OutT*)p.C;
         const bool nt_out = p.nt_store != 0;
         if constexpr (kFp8) {
-            const float sc = p.acc_scale;
+            const float sc = (p.scale_a ? *p.scale_a : 1.0f) * (p.scale_b ? *p.scale_b : 1.0f);
 #pragma unroll
             for (int i = 0; i < NACT; i++)
 #pragma unroll

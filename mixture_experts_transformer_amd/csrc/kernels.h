@@ -52,7 +52,10 @@ struct GemmParams {
     int64_t ldc2;
     int32_t layout;              // LAY_*
     const int64_t* xcd_split;    // LAY_DW: [9] tile range of each XCD (device), or nullptr
-    float acc_scale;             // fp8 operands: accumulators times this before the epilogue
+    // fp8 operands: the accumulators are multiplied by scale_a[0] * scale_b[0]
+    // (device memory, each nullable = 1) before the epilogue
+    const float* scale_a;
+    const float* scale_b;
 };
 
 int gemm_block_m();
@@ -70,11 +73,13 @@ hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int e
                        int64_t max_tiles, hipStream_t s);
 
 // ------------------------------------------------------------------- fp8 ---
-hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale,
+hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, const float* scale,
                                 uint8_t* q, float* amax, hipStream_t s);
 hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
-                                       int E, int64_t R_phys, int64_t H, float inv_scale,
+                                       int E, int64_t R_phys, int64_t H, const float* scale,
                                        uint8_t* hq, float* amax, hipStream_t s);
+hipError_t launch_fp8_scale_update(float* history, int len, const float* amax, float* scale,
+                                   hipStream_t s);
 
 // ----------------------------------------------------------------- route ---
 hipError_t launch_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d, const float* g,

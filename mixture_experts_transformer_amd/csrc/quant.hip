@@ -2,8 +2,9 @@
 // July 6th summary, the fp8 compute-lane paragraph: E4M3 in the forward, with
 // delayed scaling, i.e. a scale the caller derives from the amax history).
 //
-//   q[i] = E4M3(x[i] * inv_scale)   the product rounded to float32 first;
-//   amax = max |x[i]|               (optional; the value the history records)
+//   q[i] = E4M3(x[i] * inv)   inv = 1 / s rounded to float32, s the dequantisation
+//                             scale (device memory); the product rounded to float32;
+//   amax = max |x[i]|         (optional; the value the history records)
 //
 // and the same quantisation fused with the expert MLP's gated activation
 // (h = silu(g) u from a [g | u] row), which feeds the E4M3 down projection.
@@ -74,10 +75,16 @@ __device__ __forceinline__ void block_amax(float m, uint32_t* amax_bits) {
         atomicMax(amax_bits, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
+// 1 / s rounded to float32 (IEEE division), 1 without a scale
+__device__ __forceinline__ float inv_of(const float* scale) {
+    return scale ? 1.0f / scale[0] : 1.0f;
+}
+
 template <typename T>
-__global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, float inv,
+__global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, const float* scale,
                                                        uint8_t* q, uint32_t* amax_bits) {
     constexpr int kIn = 16 * (int)sizeof(T) / 16;          // 16-byte input vectors per group
+    const float inv = inv_of(scale);
     const int64_t groups = n / 16;
     const int64_t stride = (int64_t)gridDim.x * 256;
     float m = 0.0f;
@@ -125,9 +132,10 @@ __global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, fl
 template <typename T>
 __global__ __launch_bounds__(256) void swiglu_quantize_kernel(const T* gu, const int32_t* offsets,
                                                               int E, int64_t R_phys, int H16,
-                                                              float inv, uint8_t* hq,
+                                                              const float* scale, uint8_t* hq,
                                                               uint32_t* amax_bits) {
     constexpr int kIn = 16 * (int)sizeof(T) / 16;
+    const float inv = inv_of(scale);
     int64_t rows = offsets[E];
     rows = rows < 0 ? 0 : rows > R_phys ? R_phys : rows;
     const uint32_t groups = (uint32_t)rows * (uint32_t)H16;
@@ -173,10 +181,42 @@ __global__ __launch_bounds__(256) void swiglu_quantize_kernel(const T* gu, const
     if (amax_bits) block_amax(m, amax_bits);
 }
 
+// Delayed scaling's state update for one tensor: history (newest first) shifted
+// by one with this step's amax in front, then scale[0] = m / 448 for m the largest
+// finite entry (the value that maps to E4M3's largest code), or 1 when m is 0.
+// One block of 1024 threads, len <= 1024: every entry is read before any is written.
+__global__ __launch_bounds__(1024) void fp8_scale_update_kernel(float* history, int len,
+                                                                const float* amax,
+                                                                float* scale) {
+    __shared__ float red[16];
+    const int t = threadIdx.x;
+    float v = 0.0f;
+    if (t < len) v = t == 0 ? amax[0] : history[t - 1];
+    __syncthreads();
+    if (t < len) history[t] = v;
+    float m = (t < len && isfinite(v) && v > 0.0f) ? v : 0.0f;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    if (t == 0) {
+        float mm = 0.0f;
+        for (int w = 0; w < 16; w++) mm = fmaxf(mm, red[w]);
+        scale[0] = mm > 0.0f ? mm / 448.0f : 1.0f;
+    }
+}
+
 }  // namespace
 
+hipError_t launch_fp8_scale_update(float* history, int len, const float* amax, float* scale,
+                                   hipStream_t s) {
+    hipLaunchKernelGGL(fp8_scale_update_kernel, dim3(1), dim3(1024), 0, s, history, len, amax,
+                       scale);
+    return hipGetLastError();
+}
+
 hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
-                                       int E, int64_t R_phys, int64_t H, float inv_scale,
+                                       int E, int64_t R_phys, int64_t H, const float* scale,
                                        uint8_t* hq, float* amax, hipStream_t s) {
     uint32_t* ab = (uint32_t*)amax;
     if (ab) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, ab);
@@ -186,14 +226,14 @@ hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32
     if (grid > 4096) grid = 4096;
     if (dt == MOE_BF16)
         hipLaunchKernelGGL(swiglu_quantize_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const bf16_t*)gu, offsets, E, R_phys, H16, inv_scale, hq, ab);
+                           (const bf16_t*)gu, offsets, E, R_phys, H16, scale, hq, ab);
     else
         hipLaunchKernelGGL(swiglu_quantize_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const float*)gu, offsets, E, R_phys, H16, inv_scale, hq, ab);
+                           (const float*)gu, offsets, E, R_phys, H16, scale, hq, ab);
     return hipGetLastError();
 }
 
-hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float inv_scale,
+hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, const float* scale,
                                 uint8_t* q, float* amax, hipStream_t s) {
     uint32_t* ab = (uint32_t*)amax;
     if (ab) hipLaunchKernelGGL(zero_u32_kernel, dim3(1), dim3(1), 0, s, ab);
@@ -204,10 +244,10 @@ hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, float in
     if (grid > 4096) grid = 4096;
     if (dt == MOE_BF16)
         hipLaunchKernelGGL(quantize_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const bf16_t*)x, n, inv_scale, q, ab);
+                           (const bf16_t*)x, n, scale, q, ab);
     else
         hipLaunchKernelGGL(quantize_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s,
-                           (const float*)x, n, inv_scale, q, ab);
+                           (const float*)x, n, scale, q, ab);
     return hipGetLastError();
 }
 

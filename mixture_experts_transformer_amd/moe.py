@@ -67,16 +67,18 @@ _lib.moe_ragged_dot.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, C.c_int, 
 _lib.moe_ragged_dot_workspace_size.restype = _sz
 _lib.moe_ragged_dot_workspace_size.argtypes = [_i32]
 _lib.moe_ragged_dot_e4m3.restype = C.c_int
-_lib.moe_ragged_dot_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, _f32, _vp, C.c_int,
-                                     _vp, _sz, _vp]
+_lib.moe_ragged_dot_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _i64, _i64, _vp, _vp, _vp,
+                                     C.c_int, _vp, _sz, _vp]
 _lib.moe_quantize_e4m3.restype = C.c_int
-_lib.moe_quantize_e4m3.argtypes = [_vp, C.c_int, _i64, _f32, _vp, _vp, _vp]
+_lib.moe_quantize_e4m3.argtypes = [_vp, C.c_int, _i64, _vp, _vp, _vp, _vp]
 _lib.moe_swiglu_quantize_e4m3.restype = C.c_int
-_lib.moe_swiglu_quantize_e4m3.argtypes = [_vp, C.c_int, _vp, _i32, _i64, _i64, _f32, _vp, _vp,
+_lib.moe_swiglu_quantize_e4m3.argtypes = [_vp, C.c_int, _vp, _i32, _i64, _i64, _vp, _vp, _vp,
                                           _vp]
 _lib.moe_grouped_ffn_e4m3.restype = C.c_int
-_lib.moe_grouped_ffn_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _f32, _f32,
-                                      _f32, _vp, C.c_int, _vp, _vp, _sz, _vp]
+_lib.moe_grouped_ffn_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
+                                      _vp, _vp, C.c_int, _vp, _vp, _sz, _vp]
+_lib.moe_fp8_scale_update.restype = C.c_int
+_lib.moe_fp8_scale_update.argtypes = [_vp, _i32, _vp, _vp, _vp]
 _lib.moe_grouped_ffn_e4m3_workspace_size.restype = _sz
 _lib.moe_grouped_ffn_e4m3_workspace_size.argtypes = [_i32, _i64, _i64]
 _lib.moe_ragged_dot_dlhs.restype = C.c_int
@@ -238,38 +240,50 @@ def moe_ragged_dot(X, offsets, W, Z=None, z_dtype=None, ws=None):
     return Z
 
 
-def moe_quantize_e4m3(x, inv_scale: float, q=None, amax=None):
-    """E4M3 codes (uint8 tensor of x's shape) of x * inv_scale; amax (float32 [1]) optional."""
+def _scale(t):
+    """Device pointer of a per-tensor scale (a float32 tensor of at least one element)
+    or None (scale 1)."""
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or t.numel() < 1:
+        raise ValueError("a scale is a float32 tensor of at least one element")
+    return _ptr(t)
+
+
+def moe_quantize_e4m3(x, scale=None, q=None, amax=None):
+    """E4M3 codes (uint8 tensor of x's shape) of x / scale[0]; amax (float32 [1]) optional.
+    scale: the dequantisation scale, a float32 device tensor, or None for 1."""
     if q is None:
         q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    _check(_lib.moe_quantize_e4m3(_ptr(x), _dt(x), x.numel(), float(inv_scale), _ptr(q),
-                                  _ptr(amax), _stream()), "moe_quantize_e4m3")
+    _check(_lib.moe_quantize_e4m3(_ptr(x), _dt(x), x.numel(), _scale(scale), _ptr(q), _ptr(amax),
+                                  _stream()), "moe_quantize_e4m3")
     return q
 
 
-def moe_ragged_dot_e4m3(Xq, offsets, Wq, scale: float, Z=None, z_dtype=torch.bfloat16, ws=None):
-    """Z[r] = scale * W[e] X[r] on E4M3 codes (uint8 tensors Xq [R, K], Wq [E, N, K])."""
+def moe_ragged_dot_e4m3(Xq, offsets, Wq, scale_x=None, scale_w=None, Z=None,
+                        z_dtype=torch.bfloat16, ws=None):
+    """Z[r] = scale_x[0] scale_w[0] W[e] X[r] on E4M3 codes (uint8 Xq [R, K], Wq [E, N, K])."""
     R, K = Xq.shape
     E, N, _ = Wq.shape
     if Z is None:
         Z = torch.empty((R, N), dtype=z_dtype, device=Xq.device)
     ws = _ws(int(_lib.moe_ragged_dot_workspace_size(E)), Xq.device, ws)
-    _check(_lib.moe_ragged_dot_e4m3(_ptr(Xq), _ptr(offsets), E, R, _ptr(Wq), N, K, float(scale),
-                                    _ptr(Z), _dt(Z), _ptr(ws), ws.numel(), _stream()),
-           "moe_ragged_dot_e4m3")
+    _check(_lib.moe_ragged_dot_e4m3(_ptr(Xq), _ptr(offsets), E, R, _ptr(Wq), N, K, _scale(scale_x),
+                                    _scale(scale_w), _ptr(Z), _dt(Z), _ptr(ws), ws.numel(),
+                                    _stream()), "moe_ragged_dot_e4m3")
     return Z
 
 
-def moe_swiglu_quantize_e4m3(gu, offsets, inv_scale: float, hq=None, amax=None):
-    """E4M3 codes of silu(g) u * inv_scale for the rows < offsets[E] of gu = [g | u]
+def moe_swiglu_quantize_e4m3(gu, offsets, scale=None, hq=None, amax=None):
+    """E4M3 codes of silu(g) u / scale[0] for the rows < offsets[E] of gu = [g | u]
     ([R, 2H], float32 or bf16); amax (float32 [1]) optional."""
     R, twoH = gu.shape
     H = twoH // 2
     E = offsets.numel() - 1
     if hq is None:
         hq = torch.empty((R, H), dtype=torch.uint8, device=gu.device)
-    _check(_lib.moe_swiglu_quantize_e4m3(_ptr(gu), _dt(gu), _ptr(offsets), E, R, H,
-                                         float(inv_scale), _ptr(hq), _ptr(amax), _stream()),
+    _check(_lib.moe_swiglu_quantize_e4m3(_ptr(gu), _dt(gu), _ptr(offsets), E, R, H, _scale(scale),
+                                         _ptr(hq), _ptr(amax), _stream()),
            "moe_swiglu_quantize_e4m3")
     return hq
 
@@ -278,11 +292,12 @@ def moe_grouped_ffn_e4m3_workspace_size(E: int, R_phys: int, H: int) -> int:
     return int(_lib.moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H))
 
 
-def moe_grouped_ffn_e4m3(Xq, offsets, W_gu_q, W_d_q, scale_gu: float, inv_scale_h: float,
-                         scale_d: float, Y=None, y_dtype=torch.bfloat16, amax_h=None, ws=None):
+def moe_grouped_ffn_e4m3(Xq, offsets, W_gu_q, W_d_q, scale_x=None, scale_gu=None, scale_h=None,
+                         scale_d=None, Y=None, y_dtype=torch.bfloat16, amax_h=None, ws=None):
     """The gated expert MLP on E4M3 codes (Xq [R, d], W_gu_q [E, 2H, d], W_d_q [E, d, H]):
-    Y[r] = scale_d W_d_q[e] E4M3(silu(g) u * inv_scale_h), [g | u] = scale_gu W_gu_q[e] Xq[r].
-    The workspace holds [g | u] (bf16) then h's codes."""
+    [g | u] = s_x s_gu W_gu_q[e] Xq[r] (bf16), h's codes = E4M3(silu(g) u / s_h),
+    Y[r] = s_h s_d W_d_q[e] hq[r].  Scales are float32 device tensors (None = 1).  The
+    workspace holds [g | u] then h's codes."""
     R, d = Xq.shape
     E, twoH, _ = W_gu_q.shape
     H = twoH // 2
@@ -290,10 +305,18 @@ def moe_grouped_ffn_e4m3(Xq, offsets, W_gu_q, W_d_q, scale_gu: float, inv_scale_
         Y = torch.empty((R, d), dtype=y_dtype, device=Xq.device)
     ws = _ws(moe_grouped_ffn_e4m3_workspace_size(E, R, H), Xq.device, ws)
     _check(_lib.moe_grouped_ffn_e4m3(_ptr(Xq), _ptr(offsets), E, R, _ptr(W_gu_q), _ptr(W_d_q), d,
-                                     H, float(scale_gu), float(inv_scale_h), float(scale_d),
-                                     _ptr(Y), _dt(Y), _ptr(amax_h), _ptr(ws), ws.numel(),
-                                     _stream()), "moe_grouped_ffn_e4m3")
+                                     H, _scale(scale_x), _scale(scale_gu), _scale(scale_h),
+                                     _scale(scale_d), _ptr(Y), _dt(Y), _ptr(amax_h), _ptr(ws),
+                                     ws.numel(), _stream()), "moe_grouped_ffn_e4m3")
     return Y
+
+
+def moe_fp8_scale_update(history, amax, scale):
+    """Delayed scaling: history (float32 [len], newest first) <- [amax, history[:-1]];
+    scale[0] <- largest finite entry / 448 (1 if none is positive).  All on the device."""
+    _check(_lib.moe_fp8_scale_update(_ptr(history), history.numel(), _scale(amax), _scale(scale),
+                                     _stream()), "moe_fp8_scale_update")
+    return scale
 
 
 # --------------------------------------------------------- ragged dot VJP --

@@ -164,9 +164,15 @@ def test_forward_ragged_dot_and_fp8_entry_points_reject_bad_arguments(lib):
     lib.moe_ragged_dot_workspace_size.argtypes = [i32]
     lib.moe_ragged_dot.argtypes = [vp, vp, i32, i64, vp, i64, i64, C.c_int, vp, C.c_int, vp, sz,
                                    vp]
-    lib.moe_ragged_dot_e4m3.argtypes = [vp, vp, i32, i64, vp, i64, i64, f32, vp, C.c_int, vp, sz,
-                                        vp]
-    lib.moe_quantize_e4m3.argtypes = [vp, C.c_int, i64, f32, vp, vp, vp]
+    lib.moe_ragged_dot_e4m3.argtypes = [vp, vp, i32, i64, vp, i64, i64, vp, vp, vp, C.c_int, vp,
+                                        sz, vp]
+    lib.moe_quantize_e4m3.argtypes = [vp, C.c_int, i64, vp, vp, vp, vp]
+    lib.moe_swiglu_quantize_e4m3.argtypes = [vp, C.c_int, vp, i32, i64, i64, vp, vp, vp, vp]
+    lib.moe_grouped_ffn_e4m3.argtypes = [vp, vp, i32, i64, vp, vp, i64, i64, vp, vp, vp, vp, vp,
+                                         C.c_int, vp, vp, sz, vp]
+    lib.moe_grouped_ffn_e4m3_workspace_size.restype = sz
+    lib.moe_grouped_ffn_e4m3_workspace_size.argtypes = [i32, i64, i64]
+    lib.moe_fp8_scale_update.argtypes = [vp, i32, vp, vp, vp]
     a = 4096
     need = lib.moe_ragged_dot_workspace_size(8)
     assert need >= 9 * 4 and lib.moe_ragged_dot_workspace_size(0) == 0
@@ -181,20 +187,42 @@ def test_forward_ragged_dot_and_fp8_entry_points_reject_bad_arguments(lib):
     assert rd(W=0) == 1
     assert rd(wsb=need - 1) == 5
     f8 = lambda **kw: lib.moe_ragged_dot_e4m3(
-        kw.get("X", a), a, 8, 1000, a, kw.get("N", 128), kw.get("K", 128), kw.get("s", 1.0), a,
-        kw.get("zdt", 1), a, kw.get("wsb", need), None)
+        kw.get("X", a), a, 8, 1000, a, kw.get("N", 128), kw.get("K", 128), kw.get("sx", a),
+        kw.get("sw", None), a, kw.get("zdt", 1), a, kw.get("wsb", need), None)
     assert f8(K=64) == 2                    # E4M3 rows of 64 bytes
     assert f8(N=32) == 2
     assert f8(zdt=2) == 3                   # no E4M3 output
-    assert f8(s=float("nan")) == 1
+    assert f8(sx=a + 2) == 4                # a scale is a 4-byte aligned float
     assert f8(X=a + 8) == 4
     assert f8(wsb=need - 1) == 5
     qz = lambda **kw: lib.moe_quantize_e4m3(
-        kw.get("x", a), kw.get("dt", 1), kw.get("n", 100), kw.get("inv", 1.0), kw.get("q", a),
+        kw.get("x", a), kw.get("dt", 1), kw.get("n", 100), kw.get("s", a), kw.get("q", a),
         kw.get("amax", a), None)
     assert qz(dt=2) == 3
     assert qz(n=-1) == 2
-    assert qz(inv=float("nan")) == 1
     assert qz(q=0) == 1
     assert qz(q=a + 1) == 4
     assert qz(amax=a + 2) == 4
+    assert qz(s=a + 1) == 4
+    sq = lambda **kw: lib.moe_swiglu_quantize_e4m3(
+        a, kw.get("dt", 1), a, kw.get("E", 8), 1000, kw.get("H", 64), kw.get("s", None),
+        kw.get("hq", a), None, None)
+    assert sq(H=40) == 2                    # not whole 16-column groups
+    assert sq(E=0) == 2
+    assert sq(dt=2) == 3
+    assert sq(hq=0) == 1
+    assert sq(s=a + 3) == 4
+    fneed = lib.moe_grouped_ffn_e4m3_workspace_size(8, 1000, 128)
+    assert fneed >= 1000 * 128 * 5
+    ff = lambda **kw: lib.moe_grouped_ffn_e4m3(
+        a, a, 8, 1000, a, a, kw.get("d", 128), kw.get("H", 128), None, None, kw.get("sh", None),
+        None, a, kw.get("ydt", 1), kw.get("amax", None), a, kw.get("wsb", fneed), None)
+    assert ff(d=64) == 2 and ff(H=192) == 2  # multiples of 128
+    assert ff(ydt=2) == 3
+    assert ff(sh=a + 1) == 4 and ff(amax=a + 2) == 4
+    assert ff(wsb=fneed - 1) == 5
+    su = lambda **kw: lib.moe_fp8_scale_update(kw.get("h", a), kw.get("n", 16), kw.get("am", a),
+                                               kw.get("s", a), None)
+    assert su(n=0) == 2 and su(n=1025) == 2
+    assert su(h=0) == 1 and su(s=0) == 1
+    assert su(am=a + 2) == 4

@@ -22,6 +22,16 @@ DEV = "cuda:0"
 TDT = {"bf16": torch.bfloat16, "f32": torch.float32}
 
 
+def dev_scale(v):
+    """A per-tensor scale in device memory (None stays None: scale 1)."""
+    return None if v is None else torch.tensor([v], dtype=torch.float32, device=DEV)
+
+
+def inv_f32(s):
+    """1 / s rounded to float32, as the kernels form it from a device scale."""
+    return 1.0 if s is None else float(np.float32(1.0) / np.float32(s))
+
+
 @pytest.fixture(scope="module")
 def M():
     import mixture_experts_transformer_amd as m
@@ -41,10 +51,11 @@ def _special_values():
     return np.concatenate([v, -v])
 
 
-@pytest.mark.parametrize("dt,n,inv", [("f32", 0, 1.0), ("f32", 1, 1.0), ("f32", 1237, 1.0),
-                                      ("bf16", 4099, 1.0), ("f32", 65536 + 5, 37.25),
-                                      ("bf16", 300001, 0.0625)])
-def test_quantize_e4m3_bit_exact(M, dt, n, inv):
+@pytest.mark.parametrize("dt,n,scale", [("f32", 0, None), ("f32", 1, 1.0), ("f32", 1237, None),
+                                        ("bf16", 4099, 1.0), ("f32", 65536 + 5, 1 / 37.25),
+                                        ("bf16", 300001, 16.0)])
+def test_quantize_e4m3_bit_exact(M, dt, n, scale):
+    inv = inv_f32(scale)
     rng = np.random.default_rng(n)
     x = (rng.standard_normal(n) * np.exp(3 * rng.standard_normal(n))).astype(np.float32)
     sp = _special_values()
@@ -54,7 +65,7 @@ def test_quantize_e4m3_bit_exact(M, dt, n, inv):
     host = TB.host(xt)
     q_ref, amax_ref = O.quantize_e4m3(host, inv)
     amax = torch.full((1,), -1.0, dtype=torch.float32, device=DEV)
-    q = M.moe_quantize_e4m3(xt.to(DEV), inv, amax=amax)
+    q = M.moe_quantize_e4m3(xt.to(DEV), dev_scale(scale), amax=amax)
     torch.cuda.synchronize()
     got = q.cpu().numpy()
     bad = np.flatnonzero(got != q_ref)
@@ -120,7 +131,8 @@ def test_ragged_dot_e4m3_parity(M, out, E, N, K, kind, scale):
     scale = 2.0 ** -6
     Z = torch.full((R_phys, N), 9.0, dtype=TDT[out], device=DEV)
     M.moe_ragged_dot_e4m3(torch.from_numpy(Xq).to(DEV), torch.from_numpy(off).to(DEV),
-                          torch.from_numpy(Wq).to(DEV), scale, Z=Z)
+                          torch.from_numpy(Wq).to(DEV), dev_scale(2.0 ** -3), dev_scale(2.0 ** -3),
+                          Z=Z)
     torch.cuda.synchronize()
     got = Z.float().cpu().numpy()
     assert_fp8_close(got, Xq, Wq, off, scale, out, "Z")
@@ -159,17 +171,20 @@ def test_fp8_expert_gemm_from_quantised_bf16(M):
     W = (torch.randn((E, N, K), generator=g) / math.sqrt(K)).to(torch.bfloat16).to(DEV)
     ax = torch.zeros(1, device=DEV)
     aw = torch.zeros(1, device=DEV)
-    M.moe_quantize_e4m3(X, 1.0, amax=ax)          # this step's amax: the next step's scale
-    M.moe_quantize_e4m3(W, 1.0, amax=aw)
-    torch.cuda.synchronize()
-    sx, sw = float(ax.item()) / 448.0, float(aw.item()) / 448.0
-    Xq = M.moe_quantize_e4m3(X, 1.0 / sx)
-    Wq = M.moe_quantize_e4m3(W, 1.0 / sw)
-    Z = M.moe_ragged_dot_e4m3(Xq, torch.from_numpy(off).to(DEV), Wq, sx * sw,
+    M.moe_quantize_e4m3(X, amax=ax)               # this step's amax: the next step's scale
+    M.moe_quantize_e4m3(W, amax=aw)
+    sx_t, sw_t = ax / 448.0, aw / 448.0           # scales stay on the device
+    Xq = M.moe_quantize_e4m3(X, sx_t)
+    Wq = M.moe_quantize_e4m3(W, sw_t)
+    Z = M.moe_ragged_dot_e4m3(Xq, torch.from_numpy(off).to(DEV), Wq, sx_t, sw_t,
                               z_dtype=torch.float32)
     torch.cuda.synchronize()
-    assert_fp8_close(Z.cpu().numpy(), Xq.cpu().numpy(), Wq.cpu().numpy(), off, sx * sw, "f32",
-                     "Z")
+    sx, sw = np.float32(sx_t.item()), np.float32(sw_t.item())
+    assert sx == np.float32(ax.item()) / np.float32(448.0)
+    xq_o, _ = O.quantize_e4m3(TB.host(X.cpu()), inv_f32(sx))
+    wq_o, _ = O.quantize_e4m3(TB.host(W.cpu()), inv_f32(sw))
+    assert np.array_equal(Xq.cpu().numpy(), xq_o) and np.array_equal(Wq.cpu().numpy(), wq_o)
+    assert_fp8_close(Z.cpu().numpy(), xq_o, wq_o, off, float(sx * sw), "f32", "Z")
     # and the quantisation error against the bf16 product stays at E4M3's level
     exact = O.ragged_dot(TB.host(X.cpu()), TB.host(W.cpu()), off)
     rel = float(np.sqrt(np.mean((Z.cpu().numpy() - exact) ** 2)) / np.sqrt(np.mean(exact ** 2)))
@@ -194,10 +209,11 @@ def h_code_window(h, dh, inv):
     return e4m3_values(lo), e4m3_values(hi)
 
 
-@pytest.mark.parametrize("dt,E,H,kind,scale,inv", [
-    ("bf16", 4, 256, "uniform", 150, 37.0), ("f32", 3, 64, "skewed", 120, 1.0),
-    ("bf16", 6, 48, "sparse", 0, 0.125)])
-def test_swiglu_quantize_e4m3_parity(M, dt, E, H, kind, scale, inv):
+@pytest.mark.parametrize("dt,E,H,kind,scale,s_h", [
+    ("bf16", 4, 256, "uniform", 150, 1 / 37.0), ("f32", 3, 64, "skewed", 120, None),
+    ("bf16", 6, 48, "sparse", 0, 8.0)])
+def test_swiglu_quantize_e4m3_parity(M, dt, E, H, kind, scale, s_h):
+    inv = inv_f32(s_h)
     rng = np.random.default_rng(E * H)
     off = _offsets(rng, E, kind, scale)
     R = int(off[-1])
@@ -206,7 +222,8 @@ def test_swiglu_quantize_e4m3_parity(M, dt, E, H, kind, scale, inv):
     gu = (torch.randn((R_phys, 2 * H), generator=g) * 3).to(TDT[dt])
     hq = torch.full((R_phys, H), 0x55, dtype=torch.uint8, device=DEV)
     amax = torch.full((1,), -1.0, device=DEV)
-    M.moe_swiglu_quantize_e4m3(gu.to(DEV), torch.from_numpy(off).to(DEV), inv, hq=hq, amax=amax)
+    M.moe_swiglu_quantize_e4m3(gu.to(DEV), torch.from_numpy(off).to(DEV), dev_scale(s_h), hq=hq,
+                               amax=amax)
     torch.cuda.synchronize()
     q_ref, amax_ref, h = O.swiglu_quantize_e4m3(TB.host(gu)[:R], inv, want_h=True)
     got = hq.cpu().numpy()
@@ -307,9 +324,11 @@ def test_grouped_ffn_e4m3_parity(M, out, E, d, H, kind, scale):
     ws = torch.zeros(M.moe_grouped_ffn_e4m3_workspace_size(E, R_phys, H), dtype=torch.uint8,
                      device=DEV)
     amax_h = torch.full((1,), -1.0, device=DEV)
+    # scales as a training step holds them: s_x s_gu = sgu, 1 / s_h = inv_h, s_h s_d = sd
     M.moe_grouped_ffn_e4m3(torch.from_numpy(Xq).to(DEV), torch.from_numpy(off).to(DEV),
-                           torch.from_numpy(Wgu).to(DEV), torch.from_numpy(Wd).to(DEV), sgu, inv_h,
-                           sd, Y=Y, amax_h=amax_h, ws=ws)
+                           torch.from_numpy(Wgu).to(DEV), torch.from_numpy(Wd).to(DEV),
+                           dev_scale(2.0), dev_scale(sgu / 2.0), dev_scale(1.0 / inv_h),
+                           dev_scale(sd * inv_h), Y=Y, amax_h=amax_h, ws=ws)
     torch.cuda.synchronize()
     sure = check_ffn_e4m3(Xq, Wgu, Wd, off, sgu, inv_h, sd, Y, ws, amax_h, out, R_phys)
     assert sure > 0.999
@@ -333,20 +352,20 @@ def test_grouped_ffn_e4m3_full_size_sampled(M):
     g.manual_seed(73)
     W_d = (torch.randn((E, d, H), generator=g, device=DEV) * H ** -0.5).to(torch.bfloat16)
     aw = torch.zeros(1, device=DEV)
-    Xq = M.moe_quantize_e4m3(X, 1.0)
-    Wguq = M.moe_quantize_e4m3(W_gu, 1.0)
-    M.moe_quantize_e4m3(W_d, 1.0, q=torch.empty(W_d.shape, dtype=torch.uint8, device=DEV),
-                        amax=aw)
-    torch.cuda.synchronize()
-    sw = float(aw.item()) / 448.0
-    Wdq = M.moe_quantize_e4m3(W_d, 1.0 / sw)
+    Xq = M.moe_quantize_e4m3(X)
+    Wguq = M.moe_quantize_e4m3(W_gu)
+    M.moe_quantize_e4m3(W_d, q=torch.empty(W_d.shape, dtype=torch.uint8, device=DEV), amax=aw)
+    sw_t = aw / 448.0
+    Wdq = M.moe_quantize_e4m3(W_d, sw_t)
     sgu, inv_h = 2.0 ** -8, 16.0
-    sd = sw / inv_h
     ws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, R, H), dtype=torch.uint8,
                      device=DEV)
     off_d = torch.from_numpy(off).to(DEV)
-    Y = M.moe_grouped_ffn_e4m3(Xq, off_d, Wguq, Wdq, sgu, inv_h, sd, ws=ws)
+    Y = M.moe_grouped_ffn_e4m3(Xq, off_d, Wguq, Wdq, None, dev_scale(sgu), dev_scale(1 / inv_h),
+                               sw_t, ws=ws)
     torch.cuda.synchronize()
+    sw = float(np.float32(sw_t.item()))
+    sd = sw / inv_h                               # exact: a power of two times sw
 
     rng = np.random.default_rng(9)
     e_full = 201
@@ -362,7 +381,7 @@ def test_grouped_ffn_e4m3_full_size_sampled(M):
     # the oracle's own codes from the generator's values
     xq_o, _ = O.quantize_e4m3(TB.host(X[idx]), 1.0)
     wgu_o, _ = O.quantize_e4m3(TB.host(W_gu[sel]), 1.0)
-    wd_o, amax_sel = O.quantize_e4m3(TB.host(W_d[sel]), 1.0 / sw)
+    wd_o, amax_sel = O.quantize_e4m3(TB.host(W_d[sel]), inv_f32(sw))
     assert amax_sel <= float(aw.item())
     assert np.array_equal(Xq[idx].cpu().numpy(), xq_o), "X codes"
     assert np.array_equal(Wguq[sel].cpu().numpy(), wgu_o), "W_gu codes"
@@ -391,9 +410,92 @@ def test_fp8_entry_points_with_no_routed_rows(M, R_phys):
     hq = torch.full((R_phys, H), 0x55, dtype=torch.uint8, device=DEV)
     a1 = torch.full((1,), -1.0, device=DEV)
     a2 = torch.full((1,), -1.0, device=DEV)
-    M.moe_grouped_ffn_e4m3(Xq, off, Wgu, Wd, 1.0, 1.0, 1.0, Y=Y, amax_h=a1)
-    M.moe_ragged_dot_e4m3(Xq, off, Wgu, 1.0, Z=Z)
-    M.moe_swiglu_quantize_e4m3(gu, off, 1.0, hq=hq, amax=a2)
+    M.moe_grouped_ffn_e4m3(Xq, off, Wgu, Wd, Y=Y, amax_h=a1)
+    M.moe_ragged_dot_e4m3(Xq, off, Wgu, Z=Z)
+    M.moe_swiglu_quantize_e4m3(gu, off, hq=hq, amax=a2)
     torch.cuda.synchronize()
     assert bool((Y == 9.0).all()) and bool((Z == 9.0).all()) and bool((hq == 0x55).all())
     assert float(a1.item()) == 0.0 and float(a2.item()) == 0.0
+
+
+@pytest.mark.parametrize("length", [1, 16, 1000, 1024])
+def test_fp8_scale_update_parity(M, length):
+    """Delayed scaling's update on the device, three steps in a row, against the oracle:
+    the history bit for bit (with infinities and NaN among the entries) and the scale."""
+    rng = np.random.default_rng(length)
+    hist = (np.abs(rng.standard_normal(length)) * 10).astype(np.float32)
+    if length > 3:
+        hist[1], hist[2] = np.inf, np.nan
+    h_dev = torch.from_numpy(hist.copy()).to(DEV)
+    sc = torch.full((1,), -1.0, device=DEV)
+    for amax in (np.float32(3.5), np.float32(0.0), np.float32(1e4)):
+        M.moe_fp8_scale_update(h_dev, torch.tensor([amax], device=DEV), sc)
+        hist, s_ref, _ = O.fp8_scale_update(hist, float(amax))
+        torch.cuda.synchronize()
+        got = h_dev.cpu().numpy()
+        assert np.array_equal(got, hist, equal_nan=True)
+        assert float(sc.item()) == s_ref
+
+
+def test_fp8_step_with_device_delayed_scaling_in_a_graph(M):
+    """One fp8 expert-MLP step whose scales never leave the device: the rows quantised
+    with the scale the history gives, the E4M3 MLP, then both histories updated.  The
+    step is captured in a HIP graph and replayed; each replay must equal the same step
+    run eagerly from the same state, with eager work and synchronisation in between."""
+    rng = np.random.default_rng(31)
+    E, d, H = 4, 128, 128
+    off = torch.from_numpy(_offsets(rng, E, "uniform", 120)).to(DEV)
+    R = 600
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    X = torch.randn((R, d), generator=g, device=DEV).to(torch.bfloat16)
+    W_gu = (torch.randn((E, 2 * H, d), generator=g, device=DEV) / d ** 0.5).to(torch.bfloat16)
+    W_d = (torch.randn((E, d, H), generator=g, device=DEV) / H ** 0.5).to(torch.bfloat16)
+    aw = torch.zeros(2, device=DEV)
+    M.moe_quantize_e4m3(W_gu, amax=aw[0:1])
+    M.moe_quantize_e4m3(W_d, amax=aw[1:2])
+    s_w = aw / 448.0
+    Wguq, Wdq = M.moe_quantize_e4m3(W_gu, s_w[0:1]), M.moe_quantize_e4m3(W_d, s_w[1:2])
+    L = 16
+    hist_x, hist_h = torch.zeros(L, device=DEV), torch.zeros(L, device=DEV)
+    s_x, s_h = torch.ones(1, device=DEV), torch.ones(1, device=DEV)
+    a_x, a_h = torch.zeros(1, device=DEV), torch.zeros(1, device=DEV)
+    Xq = torch.empty((R, d), dtype=torch.uint8, device=DEV)
+    Y = torch.zeros((R, d), dtype=torch.bfloat16, device=DEV)   # rows past the groups stay 0
+    ws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, R, H), dtype=torch.uint8,
+                     device=DEV)
+
+    def bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+    def step():
+        M.moe_quantize_e4m3(X, s_x, q=Xq, amax=a_x)
+        M.moe_grouped_ffn_e4m3(Xq, off, Wguq, Wdq, s_x, s_w[0:1], s_h, s_w[1:2], Y=Y,
+                               amax_h=a_h, ws=ws)
+        M.moe_fp8_scale_update(hist_x, a_x, s_x)
+        M.moe_fp8_scale_update(hist_h, a_h, s_h)
+
+    state = [hist_x, hist_h, s_x, s_h]
+    for _ in range(2):                            # warm the histories eagerly
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    saved = [t.clone() for t in state]
+    with torch.cuda.graph(graph):
+        step()
+    for t, v in zip(state, saved):                # capture must not have run the step
+        t.copy_(v)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        before = [t.clone() for t in state]
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [Y.clone(), Xq.clone()] + [t.clone() for t in state]
+        for t, v in zip(state, before):           # the same step, eagerly, from the same state
+            t.copy_(v)
+        step()
+        torch.cuda.synchronize()
+        want = [Y, Xq] + state
+        for a, b in zip(got, want):
+            assert torch.equal(bits(a), bits(b)), f"replay {rep} differs from the eager step"
+        assert float(s_x.item()) > 0 and float(s_h.item()) > 0
