@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from moe_synth import CONFIGS, LayerConfig, by_name, gen_layer, gen_pool
+from moe_synth import LayerConfig, by_name, gen_layer, gen_pool
 from moe_synth.gen import hot_experts
 from oracle import oracle as O
 from oracle import torch_bridge as TB
@@ -89,8 +89,9 @@ def sample_tokens(T, n, seed):
     return np.sort(rng.choice(T, size=min(n, T), replace=False)).astype(np.int32)
 
 
-@pytest.mark.parametrize("name,n_tok", [(CONFIGS[0].name, 256), (CONFIGS[1].name, 192),
-                                        (CONFIGS[2].name, 24)])
+@pytest.mark.parametrize("name,n_tok", [("tiny_f32_T256_D256_L128_E16_k2", 256),
+                                        ("grug67b_bf16_T8192_D2048_E64_k4", 192),
+                                        ("marin535b_bf16_T8192_D6144_L3072_E384_k8", 24)])
 def test_layer_parity(M, name, n_tok):
     cfg = by_name(name)
     inp = gen_layer(cfg, DEV)
