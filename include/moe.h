@@ -224,6 +224,22 @@ size_t moe_grouped_ffn_e4m3_workspace_size(int32_t E, int64_t R_phys, int64_t H)
 moe_status moe_fp8_scale_update(float *history, int32_t len, const float *amax, float *scale,
                                 moe_stream stream);
 
+/* moe_permute_e4m3:  moe_permute whose row copy writes E4M3 codes: the grouping
+ *   outputs exactly as moe_permute's, and dst[r] = E4M3(src[row_src[r] / src_div] * inv)
+ *   for r < offsets[E] as moe_quantize_e4m3 converts (inv = 1 / scale[0]), so the rows
+ *   enter the E4M3 expert MLP already quantised: the local part of the fp8
+ *   permutation leg (Marin: Week of July 6th summary, the fp8 compute-lane paragraph:
+ *   E4M3 in the forward on the permutation legs).  amax (device, nullable) receives
+ *   max |x| over the source rows read, those with at least one kept assignment.
+ *   src (device) [n_src, width] in dt (MOE_F32 or MOE_BF16); dst (device) [R_phys,
+ *   width] bytes.  Limits as moe_permute, and width a multiple of 16. */
+moe_status moe_permute_e4m3(const int32_t *ids, int64_t n_assign, int32_t E, int64_t capacity,
+                            const void *src, moe_dtype dt, int64_t width, int32_t src_div,
+                            uint8_t *dst, int64_t R_phys, int32_t *slot_row, int32_t *row_src,
+                            int32_t *counts, int32_t *offsets, int64_t *n_dropped,
+                            const float *scale, float *amax, void *ws, size_t ws_bytes,
+                            moe_stream stream);
+
 /* ------------------------------------------------------- ragged dot VJP -- */
 /* Backward of the grouped matmul (the pages' ragged_dot), split as the pages
  * split their custom VJP (Marin: Week of April 26th summary, the paragraph on

@@ -8,7 +8,8 @@ loudly if the library has not been built.
 from .moe import (  # noqa: F401
     LayerDesc, MoeError, abi_version, layer_desc, moe_combine, moe_grouped_ffn,
     moe_grouped_ffn_bwd, moe_grouped_ffn_bwd_workspace_size, moe_grouped_ffn_workspace_size,
-    moe_layer_fwd, moe_layer_workspace_size, moe_permute, moe_permute_workspace_size,
+    moe_layer_fwd, moe_layer_workspace_size, moe_permute, moe_permute_e4m3,
+    moe_permute_workspace_size,
     moe_fp8_scale_update, moe_grouped_ffn_e4m3, moe_grouped_ffn_e4m3_workspace_size,
     moe_quantize_e4m3,
     moe_ragged_dot, moe_ragged_dot_dlhs, moe_ragged_dot_drhs, moe_ragged_dot_e4m3, moe_route,

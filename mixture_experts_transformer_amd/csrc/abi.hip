@@ -398,6 +398,33 @@ moe_status moe_permute(const int32_t* ids, int64_t n_assign, int32_t E, int64_t 
     return MOE_OK;
 }
 
+moe_status moe_permute_e4m3(const int32_t* ids, int64_t n_assign, int32_t E, int64_t capacity,
+                            const void* src, moe_dtype dt, int64_t width, int32_t src_div,
+                            uint8_t* dst, int64_t R_phys, int32_t* slot_row, int32_t* row_src,
+                            int32_t* counts, int32_t* offsets, int64_t* n_dropped,
+                            const float* scale, float* amax, void* ws, size_t ws_bytes,
+                            moe_stream stream) {
+    if (E < 1 || E > 1024) return MOE_ESHAPE;
+    if (n_assign < 0 || n_assign >= ((int64_t)1 << 31) || R_phys < 0) return MOE_ESHAPE;
+    const int64_t max_kept = capacity < 0 ? n_assign
+                                          : (capacity * E < n_assign ? capacity * E : n_assign);
+    if (R_phys < max_kept || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (width <= 0 || width % 16 || src_div < 1) return MOE_ESHAPE;
+    if (!counts || !offsets || !n_dropped || !src || !dst) return MOE_EINVAL;
+    if (n_assign > 0 && (!ids || !slot_row)) return MOE_EINVAL;
+    if (R_phys > 0 && !row_src) return MOE_EINVAL;
+    const void* ptrs[] = {ids, src, dst, slot_row, row_src, counts, offsets, n_dropped, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if (!aligned4(scale) || !aligned4(amax)) return MOE_EALIGN;
+    if (!ws || ws_bytes < permute_ws_bytes(n_assign, E)) return MOE_EWORKSPACE;
+    MOE_TRY(launch_permute(ids, n_assign, E, capacity, src, esize(dt), width, src_div, dst,
+                           R_phys, slot_row, row_src, counts, offsets, n_dropped, nullptr, 0, ws,
+                           hs(stream), true, scale, amax));
+    return MOE_OK;
+}
+
 // ---------------------------------------------------------- grouped FFN ----
 size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt) {
     if (E < 1 || R_phys < 0 || H <= 0 || !dt_ok(dt)) return 0;

@@ -78,6 +78,7 @@ hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, const fl
 hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32_t* offsets,
                                        int E, int64_t R_phys, int64_t H, const float* scale,
                                        uint8_t* hq, float* amax, hipStream_t s);
+hipError_t launch_zero_u32(uint32_t* p, hipStream_t s);
 hipError_t launch_fp8_scale_update(float* history, int len, const float* amax, float* scale,
                                    hipStream_t s);
 
@@ -93,7 +94,8 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                           int elem_bytes, int64_t width, int src_div, void* dst, int64_t R_phys,
                           int32_t* slot_row, int32_t* row_src, int32_t* counts, int32_t* offsets,
                           int64_t* n_dropped, int32_t* tile_prefix, int tile_bm, void* ws,
-                          hipStream_t s);
+                          hipStream_t s, bool out_e4m3 = false, const float* scale = nullptr,
+                          float* amax = nullptr);
 
 // --------------------------------------------------------------- combine ---
 hipError_t launch_combine(const void* Y, moe_dtype dt, const int32_t* slot_row, const float* w,

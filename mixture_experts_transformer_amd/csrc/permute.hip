@@ -24,6 +24,7 @@
 //           and marks the rows past the last kept one empty.
 //   pass 5  (only with a source) one wave per destination row copies the row.
 #include "common.h"
+#include "e4m3.h"
 #include "kernels.h"
 
 namespace moe {
@@ -183,7 +184,6 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t 
 // end re-read its last chunk and store nothing.  Every row is read once and
 // written once, so loads and stores are both non-temporal.
 constexpr int kCopyChunks = 8;
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E, int64_t R_phys,
                                                    const int32_t* row_src, const char* src,
@@ -252,6 +252,116 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(const int32_t* slot_r
     }
 }
 
+// The same two copies writing E4M3 codes of the rows divided by the scale (the
+// fp8 permutation leg: the rows leave the grouping step already quantised, as
+// moe_quantize_e4m3 would quantise them).  A lane converts 16 elements (32 or 64
+// bytes read, 16 bytes written) and keeps kCopyChunks 16-byte loads in flight.
+// amax: max |x| over the source rows read, i.e. those with a kept assignment.
+template <typename T>
+__global__ __launch_bounds__(256) void copy_e4m3_kernel(const int32_t* offsets, int E,
+                                                        int64_t R_phys, const int32_t* row_src,
+                                                        const T* src, uint8_t* dst, int64_t width,
+                                                        const float* scale, uint32_t* amax_bits) {
+    constexpr int kIn = (int)sizeof(T);               // 16-byte loads per 16 codes
+    constexpr int kOut = kCopyChunks / kIn;
+    const float inv = inv_of(scale);
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    float m = 0.0f;
+    if (r < R_phys && r < offsets[E]) {
+        const T* sp = src + (int64_t)row_src[r] * width;
+        uint8_t* d = dst + r * width;
+        const int64_t nout = width / 16;
+        for (int64_t c0 = 0; c0 < nout; c0 += 64 * kOut) {
+            u32x4 v[kOut][kIn];
+#pragma unroll
+            for (int q = 0; q < kOut; q++) {
+                const int64_t c = min(c0 + lane + 64 * q, nout - 1);
+#pragma unroll
+                for (int j = 0; j < kIn; j++)
+                    v[q][j] = __builtin_nontemporal_load((const u32x4*)(sp + c * 16) + j);
+            }
+#pragma unroll
+            for (int q = 0; q < kOut; q++) {
+                const int64_t c = c0 + lane + 64 * q;
+                if (c >= nout) continue;
+                float p[16];
+#pragma unroll
+                for (int e = 0; e < 16; e++) {
+                    const float f = group_elem<T>(v[q], e);
+                    m = fmaxf(m, fabsf(f));
+                    p[e] = f * inv;
+                }
+                u32x4 out;
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    out[j] = e4m3_pack4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+                __builtin_nontemporal_store(out, (u32x4*)(d + c * 16));
+            }
+        }
+    }
+    if (amax_bits) block_amax(m, amax_bits);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void scatter_copy_e4m3_kernel(
+    const int32_t* slot_row, int64_t n, int64_t n_src, const T* src, uint8_t* dst, int64_t width,
+    int src_div, const float* scale, uint32_t* amax_bits) {
+    constexpr int kIn = (int)sizeof(T);
+    constexpr int kOut = kCopyChunks / kIn;
+    const float inv = inv_of(scale);
+    const int lane = threadIdx.x & 63;
+    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    float m = 0.0f;
+    if (s < n_src) {
+        const int64_t a0 = s * src_div;
+        const int64_t na = min((int64_t)src_div, n - a0);
+        const T* sp = src + s * width;
+        const int64_t nout = width / 16;
+        for (int64_t jb = 0; jb < na; jb += 64) {
+            const int32_t my = jb + lane < na ? slot_row[a0 + jb + lane] : -1;
+            const uint64_t kept = __ballot(my >= 0);
+            if (!kept) continue;
+            for (int64_t c0 = 0; c0 < nout; c0 += 64 * kOut) {
+                u32x4 v[kOut][kIn];
+#pragma unroll
+                for (int q = 0; q < kOut; q++) {
+                    const int64_t c = min(c0 + lane + 64 * q, nout - 1);
+#pragma unroll
+                    for (int j = 0; j < kIn; j++)
+                        v[q][j] = __builtin_nontemporal_load((const u32x4*)(sp + c * 16) + j);
+                }
+                u32x4 out[kOut];
+#pragma unroll
+                for (int q = 0; q < kOut; q++) {
+                    float p[16];
+                    const bool valid = c0 + lane + 64 * q < nout;
+#pragma unroll
+                    for (int e = 0; e < 16; e++) {
+                        const float f = group_elem<T>(v[q], e);
+                        if (valid) m = fmaxf(m, fabsf(f));
+                        p[e] = f * inv;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        out[q][j] = e4m3_pack4(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+                }
+                for (uint64_t mk = kept; mk; mk &= mk - 1) {
+                    const int j = __builtin_ctzll(mk);
+                    const int64_t r = __builtin_amdgcn_readlane(my, j);
+                    uint8_t* d = dst + r * width;
+#pragma unroll
+                    for (int q = 0; q < kOut; q++) {
+                        const int64_t c = c0 + lane + 64 * q;
+                        if (c < nout) __builtin_nontemporal_store(out[q], (u32x4*)(d + c * 16));
+                    }
+                }
+            }
+        }
+    }
+    if (amax_bits) block_amax(m, amax_bits);
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -265,7 +375,7 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                           int elem_bytes, int64_t width, int src_div, void* dst, int64_t R_phys,
                           int32_t* slot_row, int32_t* row_src, int32_t* counts, int32_t* offsets,
                           int64_t* n_dropped, int32_t* tile_prefix, int tile_bm, void* ws,
-                          hipStream_t s) {
+                          hipStream_t s, bool out_e4m3, const float* scale, float* amax) {
     const int64_t seg_n = seg_len(n);
     const int64_t nseg = (n + seg_n - 1) / seg_n;
     int32_t* local_rank = (int32_t*)ws;
@@ -283,6 +393,39 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
         hipLaunchKernelGGL(place_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, ids,
                            n, seg_n, E, capacity, local_rank, seg_count, offsets, R_phys, slot_row,
                            row_src);
+    }
+    if (out_e4m3) {
+        // dst holds E4M3 codes of width bytes a row; elem_bytes is the source's
+        uint32_t* ab = (uint32_t*)amax;
+        if (ab) {
+            hipError_t e = launch_zero_u32(ab, s);
+            if (e != hipSuccess) return e;
+        }
+        if (!src || R_phys <= 0 || n <= 0) return hipGetLastError();
+        const bool bf = elem_bytes == 2;
+        if (src_div == 1) {
+            const dim3 g((unsigned)((R_phys + 3) / 4));
+            if (bf)
+                hipLaunchKernelGGL(copy_e4m3_kernel<bf16_t>, g, dim3(256), 0, s, offsets, E,
+                                   R_phys, row_src, (const bf16_t*)src, (uint8_t*)dst, width,
+                                   scale, ab);
+            else
+                hipLaunchKernelGGL(copy_e4m3_kernel<float>, g, dim3(256), 0, s, offsets, E,
+                                   R_phys, row_src, (const float*)src, (uint8_t*)dst, width,
+                                   scale, ab);
+        } else {
+            const int64_t n_src = (n + src_div - 1) / src_div;
+            const dim3 g((unsigned)((n_src + 3) / 4));
+            if (bf)
+                hipLaunchKernelGGL(scatter_copy_e4m3_kernel<bf16_t>, g, dim3(256), 0, s, slot_row,
+                                   n, n_src, (const bf16_t*)src, (uint8_t*)dst, width, src_div,
+                                   scale, ab);
+            else
+                hipLaunchKernelGGL(scatter_copy_e4m3_kernel<float>, g, dim3(256), 0, s, slot_row,
+                                   n, n_src, (const float*)src, (uint8_t*)dst, width, src_div,
+                                   scale, ab);
+        }
+        return hipGetLastError();
     }
     if (src && R_phys > 0) {
         if (src_div == 1) {

@@ -77,6 +77,9 @@ _lib.moe_swiglu_quantize_e4m3.argtypes = [_vp, C.c_int, _vp, _i32, _i64, _i64, _
 _lib.moe_grouped_ffn_e4m3.restype = C.c_int
 _lib.moe_grouped_ffn_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, _vp, _vp, _vp,
                                       _vp, _vp, C.c_int, _vp, _vp, _sz, _vp]
+_lib.moe_permute_e4m3.restype = C.c_int
+_lib.moe_permute_e4m3.argtypes = [_vp, _i64, _i32, _i64, _vp, C.c_int, _i64, _i32, _vp, _i64, _vp,
+                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_fp8_scale_update.restype = C.c_int
 _lib.moe_fp8_scale_update.argtypes = [_vp, _i32, _vp, _vp, _vp]
 _lib.moe_grouped_ffn_e4m3_workspace_size.restype = _sz
@@ -202,6 +205,37 @@ def moe_permute(ids, E, capacity=-1, src=None, src_div=1, dst=None, R_phys=None,
                             R_phys, _ptr(out["slot_row"]), _ptr(out["row_src"]),
                             _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["n_dropped"]),
                             _ptr(ws), ws.numel(), _stream()), "moe_permute")
+    out["row_src"] = out["row_src"][:R_phys]
+    return out
+
+
+def moe_permute_e4m3(ids, E, src, dst, capacity=-1, src_div=1, R_phys=None, scale=None,
+                     amax=None, ws=None, out=None):
+    """moe_permute whose row copy writes E4M3 codes of src / scale[0] into dst (uint8
+    [R_phys, width]); amax (float32 [1]) receives max |x| over the rows read."""
+    ids = ids.reshape(-1)
+    n = ids.numel()
+    R_phys = n if R_phys is None else R_phys
+    dev = ids.device
+    if out is None:
+        out = dict(slot_row=torch.empty(n, dtype=torch.int32, device=dev),
+                   row_src=torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev),
+                   counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    else:
+        out = dict(out)
+        if (out["slot_row"].numel() < n or out["row_src"].numel() < max(R_phys, 1)
+                or out["counts"].numel() < E or out["offsets"].numel() < E + 1):
+            raise ValueError("moe_permute_e4m3: an `out` tensor is too small")
+    if dst.dtype != torch.uint8 or dst.shape[-1] != src.shape[-1]:
+        raise ValueError("moe_permute_e4m3: dst is uint8 codes of src's width")
+    ws = _ws(moe_permute_workspace_size(n, E), dev, ws)
+    _check(_lib.moe_permute_e4m3(_ptr(ids), n, E, capacity, _ptr(src), _dt(src), src.shape[-1],
+                                 src_div, _ptr(dst), R_phys, _ptr(out["slot_row"]),
+                                 _ptr(out["row_src"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+                                 _ptr(out["n_dropped"]), _scale(scale), _ptr(amax), _ptr(ws),
+                                 ws.numel(), _stream()), "moe_permute_e4m3")
     out["row_src"] = out["row_src"][:R_phys]
     return out
 

@@ -221,6 +221,22 @@ def test_forward_ragged_dot_and_fp8_entry_points_reject_bad_arguments(lib):
     assert ff(ydt=2) == 3
     assert ff(sh=a + 1) == 4 and ff(amax=a + 2) == 4
     assert ff(wsb=fneed - 1) == 5
+    lib.moe_permute_e4m3.argtypes = [vp, i64, i32, i64, vp, C.c_int, i64, i32, vp, i64, vp, vp, vp,
+                                     vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_permute_workspace_size.restype = sz
+    lib.moe_permute_workspace_size.argtypes = [i64, i32]
+    pneed = lib.moe_permute_workspace_size(1000, 8)
+    pe = lambda **kw: lib.moe_permute_e4m3(
+        a, 1000, 8, -1, kw.get("src", a), kw.get("dt", 1), kw.get("w", 64), kw.get("div", 1),
+        kw.get("dst", a), kw.get("R", 1000), a, a, a, a, a, kw.get("s", None), None, a,
+        kw.get("wsb", pneed), None)
+    assert pe(w=40) == 2                    # not whole 16-byte code chunks
+    assert pe(div=0) == 2
+    assert pe(R=999) == 2                   # fewer rows than assignments, dropless
+    assert pe(dt=2) == 3
+    assert pe(dst=0) == 1 and pe(src=0) == 1
+    assert pe(s=a + 1) == 4
+    assert pe(wsb=pneed - 1) == 5
     su = lambda **kw: lib.moe_fp8_scale_update(kw.get("h", a), kw.get("n", 16), kw.get("am", a),
                                                kw.get("s", a), None)
     assert su(n=0) == 2 and su(n=1025) == 2

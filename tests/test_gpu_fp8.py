@@ -499,3 +499,42 @@ def test_fp8_step_with_device_delayed_scaling_in_a_graph(M):
         for a, b in zip(got, want):
             assert torch.equal(bits(a), bits(b)), f"replay {rep} differs from the eager step"
         assert float(s_x.item()) > 0 and float(s_h.item()) > 0
+
+
+@pytest.mark.parametrize("dt,width,div,n,E,cap,pad,s", [
+    ("bf16", 3072, 8, 4000, 24, -1, 0.0, 1 / 64),   # one source row per token, k = 8
+    ("f32", 128, 2, 4000, 24, -1, 0.0, None),
+    ("bf16", 64, 1, 4000, 24, -1, 0.0, 0.25),       # one source row per assignment
+    ("bf16", 3072, 8, 4003, 24, -1, 0.0, 1 / 64),   # last source row has 3 assignments
+    ("bf16", 256, 3, 6000, 16, 200, 0.1, 2.0),      # capacity drops and padding ids
+    ("f32", 64, 70, 7000, 5, -1, 0.3, 1 / 8),       # more than 64 assignments per source row
+    ("bf16", 128, 4, 4096, 8, 0, 0.0, None),        # capacity 0: nothing kept, nothing copied
+    ("f32", 1040, 1, 3000, 12, 300, 0.2, 1 / 3),    # pool rows with padding, a ragged pass
+])
+def test_permute_e4m3_bit_exact(M, dt, width, div, n, E, cap, pad, s):
+    """The grouping as moe_permute's, and every kept row as the oracle's E4M3 codes of
+    its source row; amax over the source rows with a kept assignment."""
+    rng = np.random.default_rng(width + n + 1)
+    ids = rng.integers(0, E, n).astype(np.int32)
+    ids[rng.random(n) < pad] = -1
+    n_src = -(-n // div)
+    src = (torch.randn((n_src, width), generator=torch.Generator().manual_seed(2)) * 20).to(TDT[dt])
+    dst = torch.full((n, width), 0x55, dtype=torch.uint8, device=DEV)
+    amax = torch.full((1,), -1.0, device=DEV)
+    out = M.moe_permute_e4m3(torch.from_numpy(ids).to(DEV), E, src.to(DEV), dst, capacity=cap,
+                             src_div=div, scale=dev_scale(s), amax=amax)
+    torch.cuda.synchronize()
+    ref = O.permute(ids, E, capacity=cap, R_phys=n)
+    kept = int(ref["offsets"][-1])
+    for key in ("counts", "offsets", "slot_row"):
+        assert np.array_equal(out[key].cpu().numpy(), ref[key]), key
+    assert np.array_equal(out["row_src"].cpu().numpy()[:kept], ref["row_src"][:kept])
+    rows = ref["row_src"][:kept] // div
+    host = TB.host(src)
+    q_ref, _ = O.quantize_e4m3(host[rows], inv_f32(s))
+    got = dst.cpu().numpy()
+    assert np.array_equal(got[:kept], q_ref), f"{int((got[:kept] != q_ref).sum())} codes differ"
+    assert np.all(got[kept:] == 0x55), "rows past the kept total were written"
+    read = np.unique(rows)
+    _, amax_ref = O.quantize_e4m3(host[read], 1.0) if read.size else (None, 0.0)
+    assert float(amax.item()) == amax_ref
