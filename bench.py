@@ -731,6 +731,142 @@ def cpu_baseline_fp8(cfg, data, scale, s_gu, s_d, target_s: float) -> dict:
                       f"the two experts' weights quantised beforehand, untimed"}
 
 
+POOL_FP8_METRIC = ("EP-share pool step (permute, expert MLP, unpermute) TFLOP/s with E4M3 "
+                   "ragged dots (model FLOPs), % of fp8 MFMA peak (1 MI355X)")
+
+
+def bench_pool_fp8(args, cfg, M, dev):
+    """The receiver pool's step with the fp8 permutation leg and E4M3 expert MLP: the
+    pool rows are grouped and quantised in one pass (moe_permute_e4m3, with the rows'
+    delayed scale), the expert MLP runs on E4M3 operands (moe_grouped_ffn_e4m3), the
+    output rows go back to pool order (moe_combine, k = 1), and both amax histories
+    roll into the next step's scales on the device.  The bf16 step (moe_permute with
+    the row copy, moe_grouped_ffn, moe_combine) is timed on the same pool."""
+    import numpy as np
+    import torch
+
+    from moe_synth import gen_pool
+    from oracle import oracle as O
+
+    pool = gen_pool(cfg, dev)
+    P, L, H, E = cfg.P, cfg.L, cfg.H, cfg.E
+    ids = pool["ids"]
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    u8 = dict(dtype=torch.uint8, device=dev)
+    W_gu, W_d = pool["W_gu"], pool["W_d"]
+    Wguq, Wdq = torch.empty(W_gu.shape, **u8), torch.empty(W_d.shape, **u8)
+    HIST = 16
+    hist_x, hist_h = torch.zeros(HIST, **f32), torch.zeros(HIST, **f32)
+    hist_gu, hist_d = torch.zeros(1, **f32), torch.zeros(1, **f32)
+    s_x, s_h, s_gu, s_d = (torch.ones(1, **f32) for _ in range(4))
+    a_x, a_h, a_gu, a_d = (torch.zeros(1, **f32) for _ in range(4))
+
+    def quantize_weights():
+        M.moe_quantize_e4m3(W_gu, s_gu, q=Wguq, amax=a_gu)
+        M.moe_quantize_e4m3(W_d, s_d, q=Wdq, amax=a_d)
+        M.moe_fp8_scale_update(hist_gu, a_gu, s_gu)
+        M.moe_fp8_scale_update(hist_d, a_d, s_d)
+
+    quantize_weights()
+    quantize_weights()
+    Xq_perm = torch.empty((P, L), **u8)
+    Y_perm = torch.empty((P, L), dtype=torch.bfloat16, device=dev)
+    out = torch.full((P, L), 0.0, dtype=torch.bfloat16, device=dev)
+    pws = torch.empty(M.moe_permute_workspace_size(P, E), **u8)
+    fws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, P, H), **u8)
+    g = dict(slot_row=torch.empty(P, **i32), row_src=torch.empty(P, **i32),
+             counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+             n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        M.moe_permute_e4m3(ids, E, pool["X"], Xq_perm, src_div=1, R_phys=P, scale=s_x,
+                           amax=a_x, ws=pws, out=g)
+        if ev:
+            ev[1].record()
+        M.moe_grouped_ffn_e4m3(Xq_perm, g["offsets"], Wguq, Wdq, s_x, s_gu, s_h, s_d, Y=Y_perm,
+                               amax_h=a_h, ws=fws)
+        if ev:
+            ev[2].record()
+        M.moe_combine(Y_perm, g["slot_row"], None, P, 1, out=out,
+                      flags=M.MOE_COMBINE_KEEP_UNROUTED)
+        M.moe_fp8_scale_update(hist_x, a_x, s_x)
+        M.moe_fp8_scale_update(hist_h, a_h, s_h)
+        if ev:
+            ev[3].record()
+
+    for _ in range(max(2, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for st in range(args.steps):
+        step(evs[st])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["permute_e4m3", "expert_mlp_e4m3", "unpermute_and_scale_updates"]
+    stage_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
+                for i, n in enumerate(names)}
+    cnt = g["counts"].cpu().numpy().astype(np.int64)
+    valid = int(cnt.sum())
+    ms = wall * 1e3 / args.steps
+    flops = cfg.flops(valid)
+    tflops = flops / (ms * 1e-3) / 1e12
+    # the bf16 step on the same pool
+    X_perm = torch.empty((P, L), dtype=torch.bfloat16, device=dev)
+    bws = torch.empty(M.moe_grouped_ffn_workspace_size(E, P, H, torch.bfloat16), **u8)
+    g2 = {k: torch.empty_like(v) for k, v in g.items()}
+
+    def step16():
+        M.moe_permute(ids, E, src=pool["X"], src_div=1, dst=X_perm, R_phys=P, ws=pws, out=g2)
+        M.moe_grouped_ffn(X_perm, g2["offsets"], W_gu, W_d, Y=Y_perm, ws=bws)
+        M.moe_combine(Y_perm, g2["slot_row"], None, P, 1, out=out,
+                      flags=M.MOE_COMBINE_KEEP_UNROUTED)
+
+    bf16_ms = time_ms(step16, reps=10)
+    ffn_bytes = E * 3 * H * L + valid * (L + H) + valid * (2 * H * 2 * 2 + L * 2)
+    line = {
+        "metric": POOL_FP8_METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s (model FLOPs)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic (seeded receiver pool; rows ~ N(0,1) at unit RMS, Zipf(1) local "
+                "expert ids, weights ~ N(0,1/fan_in)), quantised to E4M3 with per-tensor scales",
+        "config": {"workload": cfg.name, "pool_rows": P, "valid_rows": valid, "latent": L,
+                   "local_experts": E, "expert_hidden": H, "operands": "E4M3",
+                   "scaling": f"per tensor, delayed: amax history of {HIST} steps on the device",
+                   "parallelism": "none (1 GPU)"},
+        "rows_per_s": round(valid / (ms * 1e-3), 1),
+        "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS["fp8"], 2),
+        "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "bf16_step_ms": round(bf16_ms, 4),
+        "speedup_vs_bf16": round(bf16_ms / ms, 3),
+        "roofline": gemm_roofline("E4M3 expert MLP (gate/up and down ragged dots, activation "
+                                  "quantisation)", flops, ffn_bytes,
+                                  stage_ms["expert_mlp_e4m3"], "fp8"),
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's own grouping of the pool picks the rows it samples
+        ref = O.permute(ids.cpu().numpy(), E, R_phys=P)
+        kept = int(ref["offsets"][-1])
+        rows = torch.from_numpy(ref["row_src"][:kept].astype(np.int64)).to(dev)
+        data = {"counts": np.diff(ref["offsets"]).astype(np.int64), "X": pool["X"][rows],
+                "W_gu": W_gu, "W_d": W_d}
+        sc = {"x": float(s_x.item()), "h": float(s_h.item())}
+        line["cpu_baseline"] = cpu_baseline_fp8(cfg, data, sc, float(s_gu.item()),
+                                                float(s_d.item()), args.cpu_seconds)
+    return line
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -749,7 +885,11 @@ def main():
         line = bench_backward(args, by_name(name), M, dev)
     elif args.fp8:
         name = args.workload if args.workload != DEFAULT_WORKLOAD else FP8_DEFAULT
-        line = bench_fp8(args, by_name(name), M, dev)
+        cfg8 = by_name(name)
+        if isinstance(cfg8, PoolConfig):
+            line = bench_pool_fp8(args, cfg8, M, dev)
+        else:
+            line = bench_fp8(args, cfg8, M, dev)
     else:
         cfg = by_name(args.workload)
         if isinstance(cfg, PoolConfig):

@@ -257,6 +257,9 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(const int32_t* slot_r
 // moe_quantize_e4m3 would quantise them).  A lane converts 16 elements (32 or 64
 // bytes read, 16 bytes written) and keeps kCopyChunks 16-byte loads in flight.
 // amax: max |x| over the source rows read, i.e. those with a kept assignment.
+// Waves stride over the rows on a grid of at most kE4m3Blocks blocks, so the
+// amax takes one atomic per block, not per four rows.
+constexpr int kE4m3Blocks = 2048;
 template <typename T>
 __global__ __launch_bounds__(256) void copy_e4m3_kernel(const int32_t* offsets, int E,
                                                         int64_t R_phys, const int32_t* row_src,
@@ -266,9 +269,10 @@ __global__ __launch_bounds__(256) void copy_e4m3_kernel(const int32_t* offsets, 
     constexpr int kOut = kCopyChunks / kIn;
     const float inv = inv_of(scale);
     const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t rows = min(R_phys, (int64_t)offsets[E]);
     float m = 0.0f;
-    if (r < R_phys && r < offsets[E]) {
+    for (int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); r < rows;
+         r += (int64_t)gridDim.x * 4) {
         const T* sp = src + (int64_t)row_src[r] * width;
         uint8_t* d = dst + r * width;
         const int64_t nout = width / 16;
@@ -311,9 +315,9 @@ __global__ __launch_bounds__(256) void scatter_copy_e4m3_kernel(
     constexpr int kOut = kCopyChunks / kIn;
     const float inv = inv_of(scale);
     const int lane = threadIdx.x & 63;
-    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     float m = 0.0f;
-    if (s < n_src) {
+    for (int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); s < n_src;
+         s += (int64_t)gridDim.x * 4) {
         const int64_t a0 = s * src_div;
         const int64_t na = min((int64_t)src_div, n - a0);
         const T* sp = src + s * width;
@@ -404,7 +408,7 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
         if (!src || R_phys <= 0 || n <= 0) return hipGetLastError();
         const bool bf = elem_bytes == 2;
         if (src_div == 1) {
-            const dim3 g((unsigned)((R_phys + 3) / 4));
+            const dim3 g((unsigned)std::min<int64_t>((R_phys + 3) / 4, kE4m3Blocks));
             if (bf)
                 hipLaunchKernelGGL(copy_e4m3_kernel<bf16_t>, g, dim3(256), 0, s, offsets, E,
                                    R_phys, row_src, (const bf16_t*)src, (uint8_t*)dst, width,
@@ -415,7 +419,7 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                                    scale, ab);
         } else {
             const int64_t n_src = (n + src_div - 1) / src_div;
-            const dim3 g((unsigned)((n_src + 3) / 4));
+            const dim3 g((unsigned)std::min<int64_t>((n_src + 3) / 4, kE4m3Blocks));
             if (bf)
                 hipLaunchKernelGGL(scatter_copy_e4m3_kernel<bf16_t>, g, dim3(256), 0, s, slot_row,
                                    n, n_src, (const bf16_t*)src, (uint8_t*)dst, width, src_div,
