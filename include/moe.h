@@ -1,5 +1,6 @@
 /*
- * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts layer forward.
+ * moe.h -- C ABI of the MI355X (gfx950) routed mixture-of-experts layer forward,
+ * its expert backward and its fp8 expert path.
  *
  * The layer (Marin 535B-A23B: the half of a training run nobody usually shows
  * you, section "What is actually being trained"; Marin Begins Open Training of a
@@ -10,6 +11,11 @@
  *   Y_a = W_d[e] (silu(W_g[e] z) * (W_u[e] z))   per kept assignment a = (t, j)
  *   c_t = sum_j w_tj Y_(t,j)                      ordered, dropped j contribute 0
  *   y   = c W_up^T + sum_i SwiGLU_i(x)            shared experts see every token
+ *
+ * Beside the forward, the grouped expert matmuls' backward (Marin: Week of April
+ * 26th summary, the custom-VJP paragraph) and the expert MLP on OCP E4M3 operands
+ * with per-tensor delayed scaling kept on the device (Marin: Week of July 6th
+ * summary, the fp8 compute-lane paragraph), including the E4M3 permutation leg.
  *
  * Conventions for every entry point:
  *   - Pointers marked (device) are device memory on the current HIP device; the
