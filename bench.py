@@ -325,6 +325,25 @@ def bench_layer(args, cfg, M, dev):
         hbm["permute_with_row_copy"] = hbm_entry(perm_bytes, pms)
         hbm["permute_grouping_only"] = {"ms": round(stage_ms["permute"], 4),
                                         "bytes": T * k * 4 * 4}
+        # the sender's half of an expert-parallel dispatch to 64 peers (6 experts each)
+        # with the pages' 1.10 sender capacity, on the same rows
+        if cfg.E % 64 == 0:
+            cap = -(-11 * T * k // (10 * 64))
+            sent = torch.empty((T * k, de), dtype=src.dtype, device=dev)
+            sexp = torch.empty(T * k, **i32)
+            dws = torch.empty(M.moe_dispatch_pack_workspace_size(T * k, 64), dtype=torch.uint8,
+                              device=dev)
+            dout = dict(slot_row=torch.empty(T * k, **i32), row_src=torch.empty(T * k, **i32),
+                        counts=torch.empty(64, **i32), offsets=torch.empty(65, **i32),
+                        n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+            dms = time_ms(lambda: M.moe_dispatch_pack(aux["ids"], cfg.E, 64, src, capacity=cap,
+                                                      send_rows=sent, send_expert=sexp, ws=dws,
+                                                      out=dout))
+            kept = int(dout["offsets"][64].item())
+            hbm["dispatch_pack_64_peers"] = hbm_entry(T * de * es + kept * (de * es + 4)
+                                                      + T * k * 4 * 5, dms)
+            hbm["dispatch_pack_64_peers"]["sender_drops"] = int(dout["n_dropped"].item())
+            del sent, sexp, dws
         del src, dst
     line["hbm_kernels"] = hbm
     return line, inp

@@ -230,6 +230,28 @@ size_t moe_grouped_ffn_e4m3_workspace_size(int32_t E, int64_t R_phys, int64_t H)
 moe_status moe_fp8_scale_update(float *history, int32_t len, const float *amax, float *scale,
                                 moe_stream stream);
 
+/* moe_dispatch_pack:  the sender's half of the expert-parallel dispatch (Marin Begins
+ *   Open Training of a 535B-Parameter MoE Model, section 2: routed rows travel to the
+ *   GPU that owns their expert, with the expert id carried beside the row and a
+ *   sender-side capacity; the exchange itself needs the peers and is not here).
+ *   Experts are dealt to n_peers peers in contiguous blocks of epp = E / n_peers.  The
+ *   T*k assignments expert_ids [T, k] (device, int32, -1 = none) are grouped by peer as
+ *   moe_permute groups them by expert (ids / epp), with capacity_per_peer (-1 = none):
+ *   counts, offsets [n_peers + 1], slot_row, row_src and n_dropped as there; each kept
+ *   row r < offsets[n_peers] of send_rows (device, [R_phys, width] in dt) is token
+ *   row_src[r] / k of x (device, [T, width] in dt), and send_expert[r] (device, int32
+ *   [R_phys]) is its expert's local id, expert_ids[row_src[r]] % epp (-1 past the kept
+ *   rows): the payload a receiver groups by.  ws (device)
+ *   moe_dispatch_pack_workspace_size(T * k, n_peers) bytes.  Limits: E a multiple of
+ *   n_peers, 1 <= n_peers <= 1024, k <= 16, width * element size a multiple of 16. */
+moe_status moe_dispatch_pack(const int32_t *expert_ids, int64_t T, int32_t k, int32_t E,
+                             int32_t n_peers, int64_t capacity_per_peer, const void *x,
+                             moe_dtype dt, int64_t width, void *send_rows, int32_t *send_expert,
+                             int64_t R_phys, int32_t *slot_row, int32_t *row_src, int32_t *counts,
+                             int32_t *offsets, int64_t *n_dropped, void *ws, size_t ws_bytes,
+                             moe_stream stream);
+size_t moe_dispatch_pack_workspace_size(int64_t n_assign, int32_t n_peers);
+
 /* moe_permute_e4m3:  moe_permute whose row copy writes E4M3 codes: the grouping
  *   outputs exactly as moe_permute's, and dst[r] = E4M3(src[row_src[r] / src_div] * inv)
  *   for r < offsets[E] as moe_quantize_e4m3 converts (inv = 1 / scale[0]), so the rows

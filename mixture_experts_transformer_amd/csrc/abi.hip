@@ -425,6 +425,50 @@ moe_status moe_permute_e4m3(const int32_t* ids, int64_t n_assign, int32_t E, int
     return MOE_OK;
 }
 
+// ------------------------------------------------ EP dispatch, sender side ----
+size_t moe_dispatch_pack_workspace_size(int64_t n_assign, int32_t n_peers) {
+    if (n_assign < 0 || n_peers < 1) return 0;
+    return a256((size_t)(n_assign > 0 ? n_assign : 1) * 4) + permute_ws_bytes(n_assign, n_peers);
+}
+
+moe_status moe_dispatch_pack(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                             int32_t n_peers, int64_t capacity_per_peer, const void* x,
+                             moe_dtype dt, int64_t width, void* send_rows, int32_t* send_expert,
+                             int64_t R_phys, int32_t* slot_row, int32_t* row_src, int32_t* counts,
+                             int32_t* offsets, int64_t* n_dropped, void* ws, size_t ws_bytes,
+                             moe_stream stream) {
+    if (T < 0 || k < 1 || k > 16) return MOE_ESHAPE;
+    if (n_peers < 1 || n_peers > 1024 || E < n_peers || E % n_peers) return MOE_ESHAPE;
+    const int64_t n = T * k;
+    if (n >= ((int64_t)1 << 31) || R_phys < 0) return MOE_ESHAPE;
+    const int64_t max_kept = capacity_per_peer < 0
+                                 ? n
+                                 : (capacity_per_peer * n_peers < n ? capacity_per_peer * n_peers
+                                                                    : n);
+    if (R_phys < max_kept || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!dt_ok(dt)) return MOE_EDTYPE;
+    if (width <= 0 || (width * esize(dt)) % 16) return MOE_ESHAPE;
+    if (!counts || !offsets || !n_dropped || !x || !send_rows) return MOE_EINVAL;
+    if (n > 0 && (!expert_ids || !slot_row)) return MOE_EINVAL;
+    if (R_phys > 0 && (!row_src || !send_expert)) return MOE_EINVAL;
+    const void* ptrs[] = {expert_ids, x, send_rows, send_expert, slot_row, row_src, counts,
+                          offsets, n_dropped, ws};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    if (!ws || ws_bytes < moe_dispatch_pack_workspace_size(n, n_peers)) return MOE_EWORKSPACE;
+    const int epp = E / n_peers;
+    hipStream_t s = hs(stream);
+    int32_t* peer = (int32_t*)ws;
+    void* pws = (char*)ws + a256((size_t)(n > 0 ? n : 1) * 4);
+    MOE_TRY(launch_peer_of(expert_ids, n, epp, peer, s));
+    MOE_TRY(launch_permute(peer, n, n_peers, capacity_per_peer, x, esize(dt), width, k, send_rows,
+                           R_phys, slot_row, row_src, counts, offsets, n_dropped, nullptr, 0, pws,
+                           s));
+    MOE_TRY(launch_payload_ids(expert_ids, row_src, offsets, n_peers, R_phys, epp, send_expert,
+                               s));
+    return MOE_OK;
+}
+
 // ---------------------------------------------------------- grouped FFN ----
 size_t moe_grouped_ffn_workspace_size(int32_t E, int64_t R_phys, int64_t H, moe_dtype dt) {
     if (E < 1 || R_phys < 0 || H <= 0 || !dt_ok(dt)) return 0;

@@ -90,6 +90,11 @@ hipError_t launch_route(const void* h, moe_dtype h_dt, int64_t T, int64_t d, con
 
 // --------------------------------------------------------------- permute ---
 size_t permute_ws_bytes(int64_t n, int E);
+// expert-parallel dispatch, sender side: peer[i] = ids[i] / epp (-1 stays -1), and
+// payload[r] = ids[row_src[r]] % epp for r < offsets[P], -1 past it
+hipError_t launch_peer_of(const int32_t* ids, int64_t n, int epp, int32_t* peer, hipStream_t s);
+hipError_t launch_payload_ids(const int32_t* ids, const int32_t* row_src, const int32_t* offsets,
+                              int P, int64_t R_phys, int epp, int32_t* payload, hipStream_t s);
 hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity, const void* src,
                           int elem_bytes, int64_t width, int src_div, void* dst, int64_t R_phys,
                           int32_t* slot_row, int32_t* row_src, int32_t* counts, int32_t* offsets,

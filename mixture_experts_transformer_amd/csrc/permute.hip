@@ -366,6 +366,25 @@ __global__ __launch_bounds__(256) void scatter_copy_e4m3_kernel(
     if (amax_bits) block_amax(m, amax_bits);
 }
 
+// Expert-parallel dispatch, sender side: the destination peer of each assignment
+// (experts are dealt to peers in contiguous blocks of epp) ...
+__global__ __launch_bounds__(256) void peer_of_kernel(const int32_t* ids, int64_t n, int epp,
+                                                      int32_t* peer) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) peer[i] = ids[i] < 0 ? -1 : ids[i] / epp;
+}
+
+// ... and, once the rows are grouped by peer, the local expert id each sent row
+// carries with it (-1 for the rows past the kept total).
+__global__ __launch_bounds__(256) void payload_ids_kernel(const int32_t* ids,
+                                                          const int32_t* row_src,
+                                                          const int32_t* offsets, int P,
+                                                          int64_t R_phys, int epp,
+                                                          int32_t* payload) {
+    const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (r < R_phys) payload[r] = r < offsets[P] ? ids[row_src[r]] % epp : -1;
+}
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -443,6 +462,21 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                                width * elem_bytes, src_div);
         }
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_peer_of(const int32_t* ids, int64_t n, int epp, int32_t* peer, hipStream_t s) {
+    if (n > 0)
+        hipLaunchKernelGGL(peer_of_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ids,
+                           n, epp, peer);
+    return hipGetLastError();
+}
+
+hipError_t launch_payload_ids(const int32_t* ids, const int32_t* row_src, const int32_t* offsets,
+                              int P, int64_t R_phys, int epp, int32_t* payload, hipStream_t s) {
+    if (R_phys > 0)
+        hipLaunchKernelGGL(payload_ids_kernel, dim3((unsigned)((R_phys + 255) / 256)), dim3(256), 0,
+                           s, ids, row_src, offsets, P, R_phys, epp, payload);
     return hipGetLastError();
 }
 

@@ -80,6 +80,11 @@ _lib.moe_grouped_ffn_e4m3.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64
 _lib.moe_permute_e4m3.restype = C.c_int
 _lib.moe_permute_e4m3.argtypes = [_vp, _i64, _i32, _i64, _vp, C.c_int, _i64, _i32, _vp, _i64, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_dispatch_pack.restype = C.c_int
+_lib.moe_dispatch_pack.argtypes = [_vp, _i64, _i32, _i32, _i32, _i64, _vp, C.c_int, _i64, _vp, _vp,
+                                   _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_dispatch_pack_workspace_size.restype = _sz
+_lib.moe_dispatch_pack_workspace_size.argtypes = [_i64, _i32]
 _lib.moe_fp8_scale_update.restype = C.c_int
 _lib.moe_fp8_scale_update.argtypes = [_vp, _i32, _vp, _vp, _vp]
 _lib.moe_grouped_ffn_e4m3_workspace_size.restype = _sz
@@ -237,6 +242,43 @@ def moe_permute_e4m3(ids, E, src, dst, capacity=-1, src_div=1, R_phys=None, scal
                                  _ptr(out["n_dropped"]), _scale(scale), _ptr(amax), _ptr(ws),
                                  ws.numel(), _stream()), "moe_permute_e4m3")
     out["row_src"] = out["row_src"][:R_phys]
+    return out
+
+
+def moe_dispatch_pack_workspace_size(n_assign: int, n_peers: int) -> int:
+    return int(_lib.moe_dispatch_pack_workspace_size(n_assign, n_peers))
+
+
+def moe_dispatch_pack(expert_ids, E, n_peers, x, capacity=-1, R_phys=None, send_rows=None,
+                      send_expert=None, ws=None, out=None):
+    """The sender's half of an expert-parallel dispatch: the assignments expert_ids [T, k]
+    grouped by destination peer (experts in contiguous blocks of E / n_peers), each kept
+    row of x copied into send_rows and its local expert id into send_expert.  Returns
+    dict(send_rows, send_expert, slot_row, row_src, counts, offsets, n_dropped)."""
+    T, k = expert_ids.shape
+    n = T * k
+    R_phys = n if R_phys is None else R_phys
+    dev = expert_ids.device
+    if out is None:
+        out = dict(slot_row=torch.empty(n, dtype=torch.int32, device=dev),
+                   row_src=torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev),
+                   counts=torch.empty(n_peers, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(n_peers + 1, dtype=torch.int32, device=dev),
+                   n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    else:
+        out = dict(out)
+    if send_rows is None:
+        send_rows = torch.empty((R_phys, x.shape[-1]), dtype=x.dtype, device=dev)
+    if send_expert is None:
+        send_expert = torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev)
+    ws = _ws(moe_dispatch_pack_workspace_size(n, n_peers), dev, ws)
+    _check(_lib.moe_dispatch_pack(_ptr(expert_ids), T, k, E, n_peers, capacity, _ptr(x), _dt(x),
+                                  x.shape[-1], _ptr(send_rows), _ptr(send_expert), R_phys,
+                                  _ptr(out["slot_row"]), _ptr(out["row_src"]), _ptr(out["counts"]),
+                                  _ptr(out["offsets"]), _ptr(out["n_dropped"]), _ptr(ws),
+                                  ws.numel(), _stream()), "moe_dispatch_pack")
+    out.update(send_rows=send_rows, send_expert=send_expert[:R_phys],
+               row_src=out["row_src"][:R_phys])
     return out
 
 

@@ -237,6 +237,20 @@ def test_forward_ragged_dot_and_fp8_entry_points_reject_bad_arguments(lib):
     assert pe(dst=0) == 1 and pe(src=0) == 1
     assert pe(s=a + 1) == 4
     assert pe(wsb=pneed - 1) == 5
+    lib.moe_dispatch_pack.argtypes = [vp, i64, i32, i32, i32, i64, vp, C.c_int, i64, vp, vp, i64,
+                                      vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_dispatch_pack_workspace_size.restype = sz
+    lib.moe_dispatch_pack_workspace_size.argtypes = [i64, i32]
+    dneed2 = lib.moe_dispatch_pack_workspace_size(8000, 64)
+    assert dneed2 >= 8000 * 4
+    dp = lambda **kw: lib.moe_dispatch_pack(
+        a, 1000, kw.get("k", 8), kw.get("E", 384), kw.get("P", 64), -1, a, 1, kw.get("w", 64), a,
+        a, kw.get("R", 8000), a, a, a, a, a, a, kw.get("wsb", dneed2), None)
+    assert dp(E=380) == 2                   # experts not a multiple of the peers
+    assert dp(k=17) == 2
+    assert dp(R=7999) == 2                  # fewer rows than assignments, no cap
+    assert dp(w=4) == 2                     # 8-byte rows
+    assert dp(wsb=dneed2 - 1) == 5
     su = lambda **kw: lib.moe_fp8_scale_update(kw.get("h", a), kw.get("n", 16), kw.get("am", a),
                                                kw.get("s", a), None)
     assert su(n=0) == 2 and su(n=1025) == 2

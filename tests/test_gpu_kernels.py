@@ -303,3 +303,34 @@ def test_errors_are_reported_not_launched(M):
     assert "shape" in str(e.value)
     with pytest.raises(M.MoeError):
         M.moe_route(torch.zeros((4, 24), device=DEV), torch.zeros((4, 24), device=DEV), 2)
+
+
+@pytest.mark.parametrize("T,k,E,P,cap_f,pad,width", [
+    (2048, 8, 384, 64, 1.10, 0.0, 256),     # the 535B layer's 64-way split, sender cap 1.10
+    (1000, 4, 16, 4, None, 0.05, 128),      # no cap, some assignments absent
+    (3000, 2, 24, 8, 0.5, 0.0, 64),         # heavy sender drops
+])
+def test_dispatch_pack_bit_exact(M, T, k, E, P, cap_f, pad, width):
+    """The sender's half of the expert-parallel dispatch: the grouping by peer as the
+    oracle's permutation of ids // (E / P) with the sender capacity, every kept row the
+    token's row, and the payload each row's local expert id."""
+    rng = np.random.default_rng(T + E)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    ids[rng.random((T, k)) < pad] = -1
+    epp = E // P
+    cap = -1 if cap_f is None else int(np.ceil(cap_f * T * k / P))
+    x = torch.randn((T, width), generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    out = M.moe_dispatch_pack(torch.from_numpy(ids).to(DEV), E, P, x.to(DEV), capacity=cap)
+    torch.cuda.synchronize()
+    peer = np.where(ids < 0, -1, ids // epp)
+    ref = O.permute(peer, P, capacity=cap, R_phys=T * k)
+    for key in ("counts", "offsets", "slot_row"):
+        assert np.array_equal(out[key].cpu().numpy(), ref[key]), key
+    assert int(out["n_dropped"].item()) == ref["n_dropped"]
+    kept = int(ref["offsets"][-1])
+    rs = ref["row_src"][:kept]
+    assert np.array_equal(out["row_src"].cpu().numpy()[:kept], rs)
+    assert torch.equal(out["send_rows"][:kept].cpu(), x[torch.from_numpy(rs // k).long()])
+    se = out["send_expert"].cpu().numpy()
+    assert np.array_equal(se[:kept], ids.ravel()[rs] % epp)
+    assert np.all(se[kept:] == -1)
