@@ -343,7 +343,17 @@ def bench_layer(args, cfg, M, dev):
             hbm["dispatch_pack_64_peers"] = hbm_entry(T * de * es + kept * (de * es + 4)
                                                       + T * k * 4 * 5, dms)
             hbm["dispatch_pack_64_peers"]["sender_drops"] = int(dout["n_dropped"].item())
-            del sent, sexp, dws
+            # the same with the rows sent as E4M3 codes (the fp8 wire format)
+            sent8 = torch.empty((T * k, de), dtype=torch.uint8, device=dev)
+            s8 = torch.ones(1, dtype=torch.float32, device=dev)
+            a8 = torch.zeros(1, dtype=torch.float32, device=dev)
+            d8ms = time_ms(lambda: M.moe_dispatch_pack_e4m3(aux["ids"], cfg.E, 64, src,
+                                                            capacity=cap, scale=s8, amax=a8,
+                                                            send_rows=sent8, send_expert=sexp,
+                                                            ws=dws))
+            hbm["dispatch_pack_e4m3_64_peers"] = hbm_entry(T * de * es + kept * (de + 4)
+                                                           + T * k * 4 * 5, d8ms)
+            del sent, sent8, sexp, dws
         del src, dst
     line["hbm_kernels"] = hbm
     return line, inp

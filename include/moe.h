@@ -251,6 +251,19 @@ moe_status moe_dispatch_pack(const int32_t *expert_ids, int64_t T, int32_t k, in
                              int32_t *offsets, int64_t *n_dropped, void *ws, size_t ws_bytes,
                              moe_stream stream);
 size_t moe_dispatch_pack_workspace_size(int64_t n_assign, int32_t n_peers);
+/* moe_dispatch_pack_e4m3:  moe_dispatch_pack with the rows sent as E4M3 codes, the fp8
+ *   wire format of the forward's permutation leg (Marin: Week of July 6th summary, the
+ *   fp8 compute-lane paragraph: E4M3 forward on the permutation legs): send_rows
+ *   (device, [R_phys, width] bytes) holds E4M3(x / scale[0]) as moe_quantize_e4m3
+ *   converts, and amax (device, nullable) max |x| over the token rows sent.  scale is a
+ *   device float (NULL = 1).  Limits as moe_dispatch_pack, and width a multiple of 16. */
+moe_status moe_dispatch_pack_e4m3(const int32_t *expert_ids, int64_t T, int32_t k, int32_t E,
+                                  int32_t n_peers, int64_t capacity_per_peer, const void *x,
+                                  moe_dtype dt, int64_t width, uint8_t *send_rows,
+                                  int32_t *send_expert, int64_t R_phys, int32_t *slot_row,
+                                  int32_t *row_src, int32_t *counts, int32_t *offsets,
+                                  int64_t *n_dropped, const float *scale, float *amax, void *ws,
+                                  size_t ws_bytes, moe_stream stream);
 
 /* moe_permute_e4m3:  moe_permute whose row copy writes E4M3 codes: the grouping
  *   outputs exactly as moe_permute's, and dst[r] = E4M3(src[row_src[r] / src_div] * inv)

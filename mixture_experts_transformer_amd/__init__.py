@@ -10,7 +10,8 @@ from .moe import (  # noqa: F401
     moe_grouped_ffn_bwd, moe_grouped_ffn_bwd_workspace_size, moe_grouped_ffn_workspace_size,
     moe_layer_fwd, moe_layer_workspace_size, moe_permute, moe_permute_e4m3,
     moe_permute_workspace_size,
-    moe_dispatch_pack, moe_dispatch_pack_workspace_size, moe_fp8_scale_update,
+    moe_dispatch_pack, moe_dispatch_pack_e4m3, moe_dispatch_pack_workspace_size,
+    moe_fp8_scale_update,
     moe_grouped_ffn_e4m3, moe_grouped_ffn_e4m3_workspace_size,
     moe_quantize_e4m3,
     moe_ragged_dot, moe_ragged_dot_dlhs, moe_ragged_dot_drhs, moe_ragged_dot_e4m3, moe_route,

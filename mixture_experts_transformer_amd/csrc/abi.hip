@@ -431,12 +431,14 @@ size_t moe_dispatch_pack_workspace_size(int64_t n_assign, int32_t n_peers) {
     return a256((size_t)(n_assign > 0 ? n_assign : 1) * 4) + permute_ws_bytes(n_assign, n_peers);
 }
 
-moe_status moe_dispatch_pack(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
-                             int32_t n_peers, int64_t capacity_per_peer, const void* x,
-                             moe_dtype dt, int64_t width, void* send_rows, int32_t* send_expert,
-                             int64_t R_phys, int32_t* slot_row, int32_t* row_src, int32_t* counts,
-                             int32_t* offsets, int64_t* n_dropped, void* ws, size_t ws_bytes,
-                             moe_stream stream) {
+namespace {
+moe_status dispatch_pack_impl(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                              int32_t n_peers, int64_t capacity_per_peer, const void* x,
+                              moe_dtype dt, int64_t width, void* send_rows, int32_t* send_expert,
+                              int64_t R_phys, int32_t* slot_row, int32_t* row_src,
+                              int32_t* counts, int32_t* offsets, int64_t* n_dropped, void* ws,
+                              size_t ws_bytes, moe_stream stream, bool e4m3, const float* scale,
+                              float* amax) {
     if (T < 0 || k < 1 || k > 16) return MOE_ESHAPE;
     if (n_peers < 1 || n_peers > 1024 || E < n_peers || E % n_peers) return MOE_ESHAPE;
     const int64_t n = T * k;
@@ -447,7 +449,8 @@ moe_status moe_dispatch_pack(const int32_t* expert_ids, int64_t T, int32_t k, in
                                                                     : n);
     if (R_phys < max_kept || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
     if (!dt_ok(dt)) return MOE_EDTYPE;
-    if (width <= 0 || (width * esize(dt)) % 16) return MOE_ESHAPE;
+    if (width <= 0 || (width * (e4m3 ? 1 : esize(dt))) % 16) return MOE_ESHAPE;
+    if (!aligned4(scale) || !aligned4(amax)) return MOE_EALIGN;
     if (!counts || !offsets || !n_dropped || !x || !send_rows) return MOE_EINVAL;
     if (n > 0 && (!expert_ids || !slot_row)) return MOE_EINVAL;
     if (R_phys > 0 && (!row_src || !send_expert)) return MOE_EINVAL;
@@ -463,10 +466,34 @@ moe_status moe_dispatch_pack(const int32_t* expert_ids, int64_t T, int32_t k, in
     MOE_TRY(launch_peer_of(expert_ids, n, epp, peer, s));
     MOE_TRY(launch_permute(peer, n, n_peers, capacity_per_peer, x, esize(dt), width, k, send_rows,
                            R_phys, slot_row, row_src, counts, offsets, n_dropped, nullptr, 0, pws,
-                           s));
+                           s, e4m3, scale, amax));
     MOE_TRY(launch_payload_ids(expert_ids, row_src, offsets, n_peers, R_phys, epp, send_expert,
                                s));
     return MOE_OK;
+}
+}  // namespace
+
+moe_status moe_dispatch_pack(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                             int32_t n_peers, int64_t capacity_per_peer, const void* x,
+                             moe_dtype dt, int64_t width, void* send_rows, int32_t* send_expert,
+                             int64_t R_phys, int32_t* slot_row, int32_t* row_src, int32_t* counts,
+                             int32_t* offsets, int64_t* n_dropped, void* ws, size_t ws_bytes,
+                             moe_stream stream) {
+    return dispatch_pack_impl(expert_ids, T, k, E, n_peers, capacity_per_peer, x, dt, width,
+                              send_rows, send_expert, R_phys, slot_row, row_src, counts, offsets,
+                              n_dropped, ws, ws_bytes, stream, false, nullptr, nullptr);
+}
+
+moe_status moe_dispatch_pack_e4m3(const int32_t* expert_ids, int64_t T, int32_t k, int32_t E,
+                                  int32_t n_peers, int64_t capacity_per_peer, const void* x,
+                                  moe_dtype dt, int64_t width, uint8_t* send_rows,
+                                  int32_t* send_expert, int64_t R_phys, int32_t* slot_row,
+                                  int32_t* row_src, int32_t* counts, int32_t* offsets,
+                                  int64_t* n_dropped, const float* scale, float* amax, void* ws,
+                                  size_t ws_bytes, moe_stream stream) {
+    return dispatch_pack_impl(expert_ids, T, k, E, n_peers, capacity_per_peer, x, dt, width,
+                              send_rows, send_expert, R_phys, slot_row, row_src, counts, offsets,
+                              n_dropped, ws, ws_bytes, stream, true, scale, amax);
 }
 
 // ---------------------------------------------------------- grouped FFN ----

@@ -83,6 +83,10 @@ _lib.moe_permute_e4m3.argtypes = [_vp, _i64, _i32, _i64, _vp, C.c_int, _i64, _i3
 _lib.moe_dispatch_pack.restype = C.c_int
 _lib.moe_dispatch_pack.argtypes = [_vp, _i64, _i32, _i32, _i32, _i64, _vp, C.c_int, _i64, _vp, _vp,
                                    _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.moe_dispatch_pack_e4m3.restype = C.c_int
+_lib.moe_dispatch_pack_e4m3.argtypes = [_vp, _i64, _i32, _i32, _i32, _i64, _vp, C.c_int, _i64, _vp,
+                                        _vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz,
+                                        _vp]
 _lib.moe_dispatch_pack_workspace_size.restype = _sz
 _lib.moe_dispatch_pack_workspace_size.argtypes = [_i64, _i32]
 _lib.moe_fp8_scale_update.restype = C.c_int
@@ -277,6 +281,34 @@ def moe_dispatch_pack(expert_ids, E, n_peers, x, capacity=-1, R_phys=None, send_
                                   _ptr(out["slot_row"]), _ptr(out["row_src"]), _ptr(out["counts"]),
                                   _ptr(out["offsets"]), _ptr(out["n_dropped"]), _ptr(ws),
                                   ws.numel(), _stream()), "moe_dispatch_pack")
+    out.update(send_rows=send_rows, send_expert=send_expert[:R_phys],
+               row_src=out["row_src"][:R_phys])
+    return out
+
+
+def moe_dispatch_pack_e4m3(expert_ids, E, n_peers, x, capacity=-1, R_phys=None, scale=None,
+                           amax=None, send_rows=None, send_expert=None, ws=None):
+    """moe_dispatch_pack sending E4M3 codes of x / scale[0] (uint8 send_rows)."""
+    T, k = expert_ids.shape
+    n = T * k
+    R_phys = n if R_phys is None else R_phys
+    dev = expert_ids.device
+    out = dict(slot_row=torch.empty(n, dtype=torch.int32, device=dev),
+               row_src=torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev),
+               counts=torch.empty(n_peers, dtype=torch.int32, device=dev),
+               offsets=torch.empty(n_peers + 1, dtype=torch.int32, device=dev),
+               n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    if send_rows is None:
+        send_rows = torch.empty((R_phys, x.shape[-1]), dtype=torch.uint8, device=dev)
+    if send_expert is None:
+        send_expert = torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev)
+    ws = _ws(moe_dispatch_pack_workspace_size(n, n_peers), dev, ws)
+    _check(_lib.moe_dispatch_pack_e4m3(_ptr(expert_ids), T, k, E, n_peers, capacity, _ptr(x),
+                                       _dt(x), x.shape[-1], _ptr(send_rows), _ptr(send_expert),
+                                       R_phys, _ptr(out["slot_row"]), _ptr(out["row_src"]),
+                                       _ptr(out["counts"]), _ptr(out["offsets"]),
+                                       _ptr(out["n_dropped"]), _scale(scale), _ptr(amax),
+                                       _ptr(ws), ws.numel(), _stream()), "moe_dispatch_pack_e4m3")
     out.update(send_rows=send_rows, send_expert=send_expert[:R_phys],
                row_src=out["row_src"][:R_phys])
     return out

@@ -538,3 +538,29 @@ def test_permute_e4m3_bit_exact(M, dt, width, div, n, E, cap, pad, s):
     read = np.unique(rows)
     _, amax_ref = O.quantize_e4m3(host[read], 1.0) if read.size else (None, 0.0)
     assert float(amax.item()) == amax_ref
+
+
+def test_dispatch_pack_e4m3_bit_exact(M):
+    """The fp8 wire format of the dispatch: the grouping by peer as moe_dispatch_pack's,
+    each sent row the oracle's E4M3 codes of its token row, amax over the rows sent."""
+    rng = np.random.default_rng(77)
+    T, k, E, P, width = 2048, 8, 384, 64, 512
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    cap = int(np.ceil(0.9 * T * k / P))                  # some sender drops
+    x = (torch.randn((T, width), generator=torch.Generator().manual_seed(4)) * 5).to(torch.bfloat16)
+    amax = torch.full((1,), -1.0, device=DEV)
+    s = 1 / 32
+    out = M.moe_dispatch_pack_e4m3(torch.from_numpy(ids).to(DEV), E, P, x.to(DEV), capacity=cap,
+                                   scale=dev_scale(s), amax=amax)
+    torch.cuda.synchronize()
+    ref = O.permute(ids // (E // P), P, capacity=cap, R_phys=T * k)
+    kept = int(ref["offsets"][-1])
+    assert ref["n_dropped"] > 0 and int(out["n_dropped"].item()) == ref["n_dropped"]
+    assert np.array_equal(out["offsets"].cpu().numpy(), ref["offsets"])
+    rs = ref["row_src"][:kept]
+    host = TB.host(x)
+    q_ref, _ = O.quantize_e4m3(host[rs // k], inv_f32(s))
+    assert np.array_equal(out["send_rows"][:kept].cpu().numpy(), q_ref)
+    assert np.array_equal(out["send_expert"].cpu().numpy()[:kept], ids.ravel()[rs] % (E // P))
+    _, amax_ref = O.quantize_e4m3(host[np.unique(rs // k)], 1.0)
+    assert float(amax.item()) == amax_ref
