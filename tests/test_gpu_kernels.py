@@ -334,3 +334,46 @@ def test_dispatch_pack_bit_exact(M, T, k, E, P, cap_f, pad, width):
     se = out["send_expert"].cpu().numpy()
     assert np.array_equal(se[:kept], ids.ravel()[rs] % epp)
     assert np.all(se[kept:] == -1)
+
+
+def test_expert_parallel_legs_reproduce_the_local_routed_output(M):
+    """The expert-parallel path on one GPU with the exchange as the identity: the sender's
+    dispatch pack, each peer's receiver grouping by local expert, its grouped FFN and
+    unpermute, the rows returned to their slots, and the sender's ordered combine give
+    the same routed output, bit for bit, as the single-GPU permute, grouped FFN and
+    combine (each output row depends only on its own row and expert, with a fixed
+    reduction order)."""
+    rng = np.random.default_rng(12)
+    T, k, E, P, L, H = 768, 8, 64, 8, 256, 128
+    epp = E // P
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    g = torch.Generator().manual_seed(8)
+    X = torch.randn((T, L), generator=g).to(torch.bfloat16).to(DEV)
+    W_gu = (torch.randn((E, 2 * H, L), generator=g) / L ** 0.5).to(torch.bfloat16).to(DEV)
+    W_d = (torch.randn((E, L, H), generator=g) / H ** 0.5).to(torch.bfloat16).to(DEV)
+    ids_d, w_d = torch.from_numpy(ids).to(DEV), torch.from_numpy(w).to(DEV)
+    # single GPU
+    rows = torch.empty((T * k, L), dtype=torch.bfloat16, device=DEV)
+    loc = M.moe_permute(ids_d, E, src=X, src_div=k, dst=rows)
+    Y = M.moe_grouped_ffn(rows, loc["offsets"], W_gu, W_d)
+    c_local = M.moe_combine(Y, loc["slot_row"], w_d, T, k)
+    # expert parallel, exchange = identity
+    d = M.moe_dispatch_pack(ids_d, E, P, X)
+    off = d["offsets"].cpu().numpy()
+    ret = torch.zeros((T * k, L), dtype=torch.bfloat16, device=DEV)
+    for p in range(P):
+        n_p = int(off[p + 1] - off[p])
+        if n_p == 0:
+            continue
+        recv = d["send_rows"][off[p]:off[p + 1]].clone()        # what peer p receives
+        recv_ids = d["send_expert"][off[p]:off[p + 1]].clone()
+        pool_rows = torch.empty_like(recv)
+        grp = M.moe_permute(recv_ids, epp, src=recv, src_div=1, dst=pool_rows)
+        Y_p = M.moe_grouped_ffn(pool_rows, grp["offsets"], W_gu[p * epp:(p + 1) * epp].contiguous(),
+                                W_d[p * epp:(p + 1) * epp].contiguous())
+        M.moe_combine(Y_p, grp["slot_row"], None, n_p, 1, out=ret[off[p]:off[p + 1]],
+                      flags=M.MOE_COMBINE_KEEP_UNROUTED)
+    c_ep = M.moe_combine(ret, d["slot_row"], w_d, T, k)
+    torch.cuda.synchronize()
+    assert torch.equal(c_ep.view(torch.int16), c_local.view(torch.int16))
