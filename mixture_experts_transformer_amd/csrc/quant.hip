@@ -22,6 +22,11 @@ namespace {
 
 __global__ void zero_u32_kernel(uint32_t* p) { *p = 0u; }
 
+// Grid cap of the grid-strided quantising kernels: each block folds its amax into
+// the result with one atomic, so fewer, longer-lived blocks mean fewer atomics on
+// one address.
+constexpr int64_t kQuantBlocks = 2048;
+
 
 template <typename T>
 __global__ __launch_bounds__(256) void quantize_kernel(const T* x, int64_t n, const float* scale,
@@ -171,7 +176,7 @@ hipError_t launch_swiglu_quantize_e4m3(const void* gu, moe_dtype dt, const int32
     if (R_phys <= 0) return hipGetLastError();
     const int H16 = (int)(H / 16);
     int64_t grid = (R_phys * H16 + 255) / 256;
-    if (grid > 4096) grid = 4096;
+    if (grid > kQuantBlocks) grid = kQuantBlocks;
     if (dt == MOE_BF16)
         hipLaunchKernelGGL(swiglu_quantize_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
                            (const bf16_t*)gu, offsets, E, R_phys, H16, scale, hq, ab);
@@ -189,7 +194,7 @@ hipError_t launch_quantize_e4m3(const void* x, moe_dtype dt, int64_t n, const fl
     const int64_t groups = n / 16;
     int64_t grid = (groups + 255) / 256;
     if (grid < 1) grid = 1;
-    if (grid > 4096) grid = 4096;
+    if (grid > kQuantBlocks) grid = kQuantBlocks;
     if (dt == MOE_BF16)
         hipLaunchKernelGGL(quantize_kernel<bf16_t>, dim3((unsigned)grid), dim3(256), 0, s,
                            (const bf16_t*)x, n, scale, q, ab);
