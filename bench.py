@@ -10,6 +10,14 @@ ids) it is moe_permute (with the row copy), moe_grouped_ffn and the unpermute
 
 Default workload: the 535B-A23B-shaped layer (8,192 tokens, width 6,144,
 latent 3,072, 384 experts top-8, two shared experts).
+
+Other modes, each printing its own JSON line:
+  --backward  the expert MLP forward + backward (moe_grouped_ffn, moe_grouped_ffn_bwd)
+              on an expert-MLP workload;
+  --fp8       the expert MLP with E4M3 ragged dots and delayed scaling kept on the
+              device (moe_quantize_e4m3, moe_grouped_ffn_e4m3, moe_fp8_scale_update), or,
+              on a pool workload, the pool step with the E4M3 permute; each beside its
+              bf16 counterpart.
 """
 from __future__ import annotations
 
