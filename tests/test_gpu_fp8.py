@@ -564,3 +564,59 @@ def test_dispatch_pack_e4m3_bit_exact(M):
     assert np.array_equal(out["send_expert"].cpu().numpy()[:kept], ids.ravel()[rs] % (E // P))
     _, amax_ref = O.quantize_e4m3(host[np.unique(rs // k)], 1.0)
     assert float(amax.item()) == amax_ref
+
+
+def test_fp8_pool_step_full_size_sampled(M):
+    """The receiver pool's fp8 step in the benchmark's launch configuration (65,536-row
+    pool with padding, 6 local experts, latent and hidden 3,072): the E4M3 permute and
+    the E4M3 expert MLP, with pool rows and W_gu of small integer values (exact gate/up
+    sums) and W_d ~ N(0, 1/H) at its amax scale.  Checked on two rows of every expert:
+    their codes bit for bit, and [g | u], h's codes and Y as in check_ffn_e4m3, against
+    the oracle, which quantises those rows and all six experts itself."""
+    from moe_synth import by_name, gen_pool, small_int_tensor
+
+    cfg = by_name("marin535b_ep_share_bf16_P65536_E6")
+    P, L, H, E = cfg.P, cfg.L, cfg.H, cfg.E
+    pool = gen_pool(cfg, DEV)
+    ids = pool["ids"]
+    X = small_int_tensor((P, L), 81, DEV)
+    W_gu = small_int_tensor((E, 2 * H, L), 82, DEV)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(83)
+    W_d = (torch.randn((E, L, H), generator=g, device=DEV) * H ** -0.5).to(torch.bfloat16)
+    aw = torch.zeros(1, device=DEV)
+    M.moe_quantize_e4m3(W_d, amax=aw)
+    sw_t = aw / 448.0
+    Wguq, Wdq = M.moe_quantize_e4m3(W_gu), M.moe_quantize_e4m3(W_d, sw_t)
+    Xq = torch.empty((P, L), dtype=torch.uint8, device=DEV)
+    a_x = torch.zeros(1, device=DEV)
+    grp = M.moe_permute_e4m3(ids, E, X, Xq, src_div=1, R_phys=P, amax=a_x)
+    sgu, inv_h = 2.0 ** -8, 16.0
+    ws = torch.empty(M.moe_grouped_ffn_e4m3_workspace_size(E, P, H), dtype=torch.uint8,
+                     device=DEV)
+    Y = M.moe_grouped_ffn_e4m3(Xq, grp["offsets"], Wguq, Wdq, None, dev_scale(sgu),
+                               dev_scale(1 / inv_h), sw_t, ws=ws)
+    torch.cuda.synchronize()
+    sw = float(np.float32(sw_t.item()))
+    ids_h = ids.cpu().numpy()
+    ref = O.permute(ids_h, E, R_phys=P)
+    off = ref["offsets"]
+    assert np.array_equal(grp["offsets"].cpu().numpy(), off)
+    rng = np.random.default_rng(21)
+    take = np.concatenate([np.sort(rng.choice(np.arange(off[e], off[e + 1]), 2, replace=False))
+                           for e in range(E)])
+    sub_off = np.arange(0, 2 * E + 1, 2, dtype=np.int32)
+    src_rows = ref["row_src"][take]
+    xq_o, _ = O.quantize_e4m3(TB.host(X[torch.from_numpy(src_rows.astype(np.int64)).to(DEV)]), 1.0)
+    idx = torch.from_numpy(take.astype(np.int64)).to(DEV)
+    assert np.array_equal(Xq[idx].cpu().numpy(), xq_o), "permuted E4M3 rows"
+    wgu_o, _ = O.quantize_e4m3(TB.host(W_gu), 1.0)
+    wd_o, _ = O.quantize_e4m3(TB.host(W_d), inv_f32(sw))
+    assert np.array_equal(Wguq.cpu().numpy(), wgu_o) and np.array_equal(Wdq.cpu().numpy(), wd_o)
+    gv, hv = ws_views(ws, E, P, H)
+    ref_mlp = O.expert_mlp_e4m3(xq_o, wgu_o, wd_o, sub_off, sgu, inv_h, sw / inv_h)
+    sure = check_ffn_e4m3(xq_o, wgu_o, wd_o, sub_off, sgu, inv_h, sw / inv_h,
+                          Y[idx].float().cpu().numpy(),
+                          (gv[idx].cpu().numpy(), hv[idx].cpu().numpy()), None, "bf16",
+                          len(take), ref_mlp)
+    assert sure > 0.99
