@@ -27,6 +27,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -34,6 +35,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 DEFAULT_WORKLOAD = "marin535b_bf16_T8192_D6144_L3072_E384_k8"
+EP_SHARE_WORKLOAD = "marin535b_ep_share_bf16_P65536_E6"
+LONGCTX_WORKLOAD = "marin535b_longctx_bf16_T65536_D6144_L3072_E384_k8"
 METRIC = "MoE layer fwd TFLOP/s + tokens/s, % of bf16 MFMA peak (1 MI355X)"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3, "fp8": 5000.0}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0                          # MI355X HBM3E
@@ -46,8 +49,8 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles",
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -89,6 +92,10 @@ class HipEvents:
         ms = C.c_float()
         assert self.hip.hipEventElapsedTime(C.byref(ms), C.c_void_p(a), C.c_void_p(b)) == 0
         return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(C.c_void_p(e))
 
 
 def gemm_source_hash() -> str:
@@ -160,6 +167,42 @@ def time_ms(fn, reps=5) -> float:
 
 
 # ---------------------------------------------------------------- CPU oracle --
+def cpu_model() -> str:
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_both(fn, target_s: float) -> dict:
+    """The oracle timed with all its threads and with one; fn(target_s) runs one
+    bounded sample and returns its figures."""
+    from oracle import oracle as O
+
+    full = fn(target_s)
+    prev = O.set_threads(1)
+    try:
+        one = fn(target_s / 2)
+    finally:
+        O.set_threads(prev)
+    full["single_thread"] = {"value": one["value"], "unit": one["unit"], "cores": 1,
+                             "sample": one["sample"]}
+    full["cpu_model"] = cpu_model()
+    full["host_cpus"] = os.cpu_count()
+    return full
+
+
 def cpu_baseline_layer(cfg, inp, target_s: float) -> dict:
     """The oracle as it stands, on a bounded sample of the same workload's tokens."""
     import numpy as np
@@ -167,7 +210,7 @@ def cpu_baseline_layer(cfg, inp, target_s: float) -> dict:
     from oracle import oracle as O
     from oracle import torch_bridge as TB
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = int(O.lib().moe_ref_max_threads())
     x_host = TB.host(inp["x"])
     base = TB.layer_weights(inp, experts=[])        # dense weights, copied once
     gu = [None] * cfg.E
@@ -210,7 +253,7 @@ def cpu_baseline_pool(cfg, pool, target_s: float) -> dict:
     from oracle import oracle as O
     from oracle import torch_bridge as TB
 
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = int(O.lib().moe_ref_max_threads())
     ids = pool["ids"].cpu().numpy()
     valid = np.flatnonzero(ids >= 0)
     W_gu = [TB.host(pool["W_gu"][e]) for e in range(cfg.E)]
@@ -232,6 +275,59 @@ def cpu_baseline_pool(cfg, pool, target_s: float) -> dict:
 
 
 # ------------------------------------------------------------------ workloads --
+def stats_ms(vals) -> dict:
+    import numpy as np
+    a = np.asarray(vals, np.float64)
+    return {"mean": round(float(a.mean()), 4), "median": round(float(np.median(a)), 4),
+            "min": round(float(a.min()), 4), "max": round(float(a.max()), 4)}
+
+
+def layer_rooflines(cfg, kept, cnt, stage_ms, dtype):
+    """Rooflines of the two grouped GEMMs of a layer step from their mean stage times."""
+    es = 2 if dtype == "bf16" else 4
+    de, H = cfg.d_e, cfg.H
+    active = int((cnt > 0).sum())
+    # gate/up + SwiGLU: every active expert's [2H, de] weights, each routed row of
+    # the expert input read once, each hidden row written once.
+    g1_bytes = active * 2 * H * de * es + kept * de * es + kept * H * es
+    g1_flops = 2 * kept * de * 2 * H
+    g2_bytes = active * de * H * es + kept * H * es + kept * de * es
+    g2_flops = 2 * kept * H * de
+    return (gemm_roofline("grouped gate/up + SwiGLU GEMM", g1_flops, g1_bytes, stage_ms["gemm1"],
+                          dtype),
+            gemm_roofline("grouped down GEMM", g2_flops, g2_bytes, stage_ms["gemm2"], dtype))
+
+
+N_ROTATE = 3     # input/output copies used in turn (each x is 100 MB at the 535B layer)
+
+
+def time_layer(M, desc, W, xs, ys, aux, ws, warmup, steps):
+    """warmup + steps layer calls, the inputs and outputs taken in turn from xs/ys so
+    that no step finds the previous one's x or y in the 256 MB last-level cache.
+    Returns the wall time of the timed steps and each step's per-stage event times."""
+    import torch
+
+    def run(s, ev=None):
+        M.moe_layer_fwd(desc, W, xs[s % len(xs)], y=ys[s % len(ys)], aux=aux, ws=ws, events=ev)
+
+    for s in range(warmup):
+        run(s)
+    torch.cuda.synchronize()
+    hip = HipEvents()
+    evs = [hip.create(M.MOE_EV_COUNT) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        run(warmup + s, evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_stage = {n: [hip.elapsed_ms(evs[s][i - 1], evs[s][i]) for s in range(steps)]
+                 for i, n in enumerate(M.EV_NAMES) if i > 0}
+    per_step = [hip.elapsed_ms(evs[s][0], evs[s][-1]) for s in range(steps)]
+    hip.destroy([e for ev in evs for e in ev])
+    return wall, per_stage, per_step
+
+
 def bench_layer(args, cfg, M, dev):
     import numpy as np
     import torch
@@ -242,31 +338,16 @@ def bench_layer(args, cfg, M, dev):
     desc = M.layer_desc(cfg.T, cfg.D, cfg.L, cfg.E, cfg.k, cfg.H, cfg.n_shared, cfg.Hs,
                         cfg.dtype, cfg.eps)
     ws = torch.empty(M.moe_layer_workspace_size(desc), dtype=torch.uint8, device=dev)
-    y = torch.empty_like(inp["x"])
+    xs = [inp["x"]] + [inp["x"].clone() for _ in range(N_ROTATE - 1)]
+    ys = [torch.empty_like(inp["x"]) for _ in range(N_ROTATE)]
     i32 = dict(dtype=torch.int32, device=dev)
     aux = dict(ids=torch.empty((cfg.T, cfg.k), **i32),
                w=torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
                counts=torch.empty(cfg.E, **i32),
                n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
-
-    for _ in range(args.warmup):
-        M.moe_layer_fwd(desc, inp, inp["x"], y=y, aux=aux, ws=ws)
-    torch.cuda.synchronize()
-
-    hip = HipEvents()
-    evs = [hip.create(M.MOE_EV_COUNT) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        M.moe_layer_fwd(desc, inp, inp["x"], y=y, aux=aux, ws=ws, events=evs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    stage_ms = {n: 0.0 for n in M.EV_NAMES[1:]}
-    for s in range(args.steps):
-        for i in range(1, M.MOE_EV_COUNT):
-            stage_ms[M.EV_NAMES[i]] += hip.elapsed_ms(evs[s][i - 1], evs[s][i]) / args.steps
-    gpu_ms = sum(hip.elapsed_ms(evs[s][0], evs[s][-1]) for s in range(args.steps)) / args.steps
+    wall, per_stage, per_step = time_layer(M, desc, inp, xs, ys, aux, ws, args.warmup,
+                                           args.steps)
+    stage_ms = {n: float(np.mean(v)) for n, v in per_stage.items()}
 
     cnt = aux["counts"].cpu().numpy().astype(np.int64)
     kept = int(cnt.sum()) - int(aux["n_dropped"].item())
@@ -278,13 +359,24 @@ def bench_layer(args, cfg, M, dev):
     es = 2 if cfg.dtype == "bf16" else 4
     de, H, T, k = cfg.d_e, cfg.H, cfg.T, cfg.k
     active = int((cnt > 0).sum())
-    # gate/up + SwiGLU: every active expert's [2H, de] weights, each routed row of
-    # the expert input read once, each hidden row written once.
-    g1_bytes = active * 2 * H * de * es + kept * de * es + kept * H * es
-    g1_flops = 2 * kept * de * 2 * H
-    g2_bytes = active * de * H * es + kept * H * es + kept * de * es
-    g2_flops = 2 * kept * H * de
-    traffic = measured_traffic(cfg.name)
+    g1, g2 = layer_rooflines(cfg, kept, cnt, stage_ms, cfg.dtype)
+    g1["traffic"] = measured_traffic(cfg.name)
+    # the dense GEMMs: down-projection (x W_dn^T), the shared experts' gate/up +
+    # SwiGLU, and the K-concatenated output GEMM [c | h_s] [W_up | W2_s]^T
+    dense = {}
+    if cfg.L > 0:
+        dense["down_projection"] = gemm_roofline(
+            "down-projection GEMM", 2 * T * cfg.D * cfg.L,
+            (T * cfg.D + cfg.L * cfg.D) * es + T * cfg.L * 4, stage_ms["downproj"], cfg.dtype)
+    if cfg.n_shared > 0:
+        sh = cfg.n_shared * cfg.Hs
+        dense["shared_gate_up"] = gemm_roofline(
+            "shared experts' gate/up + SwiGLU GEMM", 2 * T * cfg.D * 2 * sh,
+            (T * cfg.D + 2 * sh * cfg.D + T * sh) * es, stage_ms["shared"], cfg.dtype)
+        kk = (cfg.L if cfg.L > 0 else 0) + sh
+        dense["output"] = gemm_roofline(
+            "output GEMM [c | h_s] [W_up | W2_s]^T", 2 * T * kk * cfg.D,
+            (T * kk + cfg.D * kk + T * cfg.D) * es, stage_ms["output"], cfg.dtype)
     line = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -305,12 +397,13 @@ def bench_layer(args, cfg, M, dev):
         "tokens_per_s": round(T / (ms * 1e-3), 1),
         "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
         "hw_tflops": round(hw_flops / (ms * 1e-3) / 1e12, 2),
-        "gpu_ms_per_step_events": round(gpu_ms, 4),
+        "timing": {"inputs_rotated": N_ROTATE, "step_ms_events": stats_ms(per_step)},
+        "gpu_ms_per_step_events": round(float(np.mean(per_step)), 4),
         "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
-        "roofline": gemm_roofline("grouped gate/up + SwiGLU GEMM", g1_flops, g1_bytes,
-                                  stage_ms["gemm1"], cfg.dtype, traffic),
-        "grouped_down_gemm": gemm_roofline("grouped down GEMM", g2_flops, g2_bytes,
-                                           stage_ms["gemm2"], cfg.dtype),
+        "stage_ms_median": {n: round(float(np.median(v)), 4) for n, v in per_stage.items()},
+        "roofline": g1,
+        "grouped_down_gemm": g2,
+        "dense_gemms": dense,
         "routed_rows": {"kept": kept, "padded_to_tiles": pad, "active_experts": active,
                         "max_per_expert": int(cnt.max()), "min_per_expert": int(cnt.min())},
     }
@@ -367,6 +460,68 @@ def bench_layer(args, cfg, M, dev):
     return line, inp
 
 
+def bench_longctx_leg(args, M, dev, inp3):
+    """The long-context batch's layer (65,536 tokens, 10% of the experts biased to
+    about 5x the mean load) on the 535B layer's weights, so that no second 22 GB
+    bank is drawn: the same shapes and distributions as that workload, with its own
+    tokens and router bias.  Times the layer and reports its grouped GEMMs against
+    the MFMA peak (at 524,288 routed rows they are MFMA-bound)."""
+    import numpy as np
+    import torch
+
+    from moe_synth import by_name
+    from moe_synth.gen import gen_tokens, hot_experts, router_bias
+
+    cfg = by_name(LONGCTX_WORKLOAD)
+    x = gen_tokens(cfg, dev)
+    W = dict(inp3)
+    W["b_r"] = router_bias(cfg, dev)
+    desc = M.layer_desc(cfg.T, cfg.D, cfg.L, cfg.E, cfg.k, cfg.H, cfg.n_shared, cfg.Hs,
+                        cfg.dtype, cfg.eps)
+    ws = torch.empty(M.moe_layer_workspace_size(desc), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    i32 = dict(dtype=torch.int32, device=dev)
+    aux = dict(counts=torch.empty(cfg.E, **i32),
+               n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+    steps = max(5, args.steps // 5)
+    wall, per_stage, per_step = time_layer(M, desc, W, [x], [y], aux, ws, 2, steps)
+    stage_ms = {n: float(np.mean(v)) for n, v in per_stage.items()}
+    cnt = aux["counts"].cpu().numpy().astype(np.int64)
+    kept = int(cnt.sum()) - int(aux["n_dropped"].item())
+    ms = wall * 1e3 / steps
+    g1, g2 = layer_rooflines(cfg, kept, cnt, stage_ms, cfg.dtype)
+    hot = hot_experts(cfg)
+    out = {"workload": cfg.name, "weights": "the 535B layer's banks (same shapes and "
+                                            "distributions), this workload's tokens and bias",
+           "steps": steps, "ms_per_step": round(ms, 3),
+           "tflops": round(cfg.flops(kept) / (ms * 1e-3) / 1e12, 1),
+           "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+           "step_ms_events": stats_ms(per_step),
+           "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+           "hot_expert_load": round(float(cnt[hot].mean() / cnt.mean()), 2),
+           "rows_per_expert": {"max": int(cnt.max()), "min": int(cnt.min())},
+           "gate_up_gemm": g1, "down_gemm": g2}
+    del ws, x, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def bench_pool_leg(args, M, dev):
+    """The expert-parallel share's step (the receiver pool), timed after the headline."""
+    from moe_synth import by_name
+
+    cfg = by_name(EP_SHARE_WORKLOAD)
+    a = argparse.Namespace(**vars(args))
+    line, pool = bench_pool(a, cfg, M, dev)
+    out = {k: line[k] for k in ["ms_per_step", "value", "rows_per_s", "stage_ms",
+                                "stage_ms_median", "step_ms_events"] if k in line}
+    out["tflops"] = out.pop("value")
+    out.update(workload=cfg.name, steps=a.steps, grouped_ffn=line["roofline"],
+               hbm_kernels=line["hbm_kernels"])
+    del pool
+    return out
+
+
 def bench_pool(args, cfg, M, dev):
     import numpy as np
     import torch
@@ -411,8 +566,9 @@ def bench_pool(args, cfg, M, dev):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     names = ["permute", "grouped_ffn", "unpermute"]
-    stage_ms = {n: sum(e[i].elapsed_time(e[i + 1]) for e in evs) / args.steps
-                for i, n in enumerate(names)}
+    per_stage = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(names)}
+    stage_ms = {n: float(np.mean(v)) for n, v in per_stage.items()}
+    per_step = [e[0].elapsed_time(e[3]) for e in evs]
     cnt = g["counts"].cpu().numpy().astype(np.int64)
     valid = int(cnt.sum())
     ms = wall * 1e3 / args.steps
@@ -440,7 +596,9 @@ def bench_pool(args, cfg, M, dev):
                    "local_experts": E, "expert_hidden": H, "parallelism": "none (1 GPU)"},
         "rows_per_s": round(valid / (ms * 1e-3), 1),
         "pct_peak_mfma": round(100 * tflops / PEAK_TFLOPS[cfg.dtype], 2),
+        "step_ms_events": stats_ms(per_step),
         "stage_ms": {n: round(v, 4) for n, v in stage_ms.items()},
+        "stage_ms_median": {n: round(float(np.median(v)), 4) for n, v in per_stage.items()},
         "roofline": gemm_roofline("grouped FFN (gate/up + SwiGLU and down GEMMs)", flops,
                                   ffn_bytes, stage_ms["grouped_ffn"], cfg.dtype),
         "hbm_kernels": {"permute_with_row_copy": hbm_entry(perm_bytes, stage_ms["permute"]),
@@ -933,6 +1091,12 @@ def main():
             line, data = bench_pool(args, cfg, M, dev)
         else:
             line, data = bench_layer(args, cfg, M, dev)
+            if cfg.name == DEFAULT_WORKLOAD and not args.no_kernel_extras:
+                # the workloads where the grouped GEMMs are MFMA-bound, timed after
+                # the headline: the expert-parallel share's pool and the
+                # long-context batch
+                line["ep_share_pool"] = bench_pool_leg(args, M, dev)
+                line["long_context"] = bench_longctx_leg(args, M, dev, data)
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -942,9 +1106,11 @@ def main():
         del src, dst
     if not args.no_cpu_baseline and cfg is not None:
         if isinstance(cfg, PoolConfig):
-            line["cpu_baseline"] = cpu_baseline_pool(cfg, data, args.cpu_seconds)
+            line["cpu_baseline"] = cpu_baseline_both(
+                lambda t: cpu_baseline_pool(cfg, data, t), args.cpu_seconds)
         else:
-            line["cpu_baseline"] = cpu_baseline_layer(cfg, data, args.cpu_seconds)
+            line["cpu_baseline"] = cpu_baseline_both(
+                lambda t: cpu_baseline_layer(cfg, data, t), args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

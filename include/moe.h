@@ -135,7 +135,10 @@ size_t moe_permute_workspace_size(int64_t n_assign, int32_t E);
  *          offsets[0] = 0, offsets[E] <= R_phys
  *   W_gu   (device) [E, 2H, d];  W_d (device) [E, d, H]  (dt)
  *   Y      (device) [R_phys, d] in dt
- *   ws     (device) moe_grouped_ffn_workspace_size(E, R_phys, H, dt) bytes
+ *   ws     (device) moe_grouped_ffn_workspace_size(E, R_phys, H, dt) bytes: the
+ *          row-tile prefix ([E+1] int32, padded to 256 bytes), then the hidden
+ *          h [R_phys, H] in dt (rows past offsets[E] unwritten), which the caller
+ *          may read back once the stream has synchronised
  * Accumulation is float32; the hidden h is stored in dt.
  * Limits: d and H multiples of 64 for MOE_BF16 and of 32 for MOE_F32 (whole
  * 128-byte steps along each reduction), E <= 1024, and every expert's weight
@@ -412,6 +415,34 @@ moe_status moe_layer_fwd(const moe_layer_desc *d, const moe_layer_weights *W, co
                          void *y, const moe_layer_aux *aux, void *ws, size_t ws_bytes,
                          moe_stream stream);
 size_t moe_layer_workspace_size(const moe_layer_desc *d);
+
+/* Where moe_layer_fwd keeps its intermediate stages inside ws, as byte offsets
+ * from ws (SIZE_MAX where the configuration has no such stage), so that a
+ * caller can read each stage back after the stream has synchronised (the
+ * per-kernel parity checks do).  Valid for calls with the same desc; the
+ * contents are those of the last call that used the workspace.
+ *   z_pre   [T, L] float32    latent before RMSNorm (latent only)
+ *   z_e     [T, L] dtype      normalised latent: the routed experts' input
+ *                             (latent only; without one they read x)
+ *   row_src [T*k] int32       assignment a = t*k + j held by each grouped row
+ *   h       [T*k, H] dtype    routed experts' hidden silu(G) * U, rows grouped
+ *                             by expert as offsets says (rows past offsets[E]
+ *                             hold nothing)
+ *   Y       [T*k, d_e] dtype  routed experts' outputs, the same rows
+ *   c       [T, d_e] dtype    the ordered weighted combine (SIZE_MAX when there
+ *                             is neither a latent nor a shared expert: the
+ *                             combine then writes y)
+ *   h_s     [T, n_shared*Hs] dtype  the shared experts' hidden, expert i in
+ *                             columns [i Hs, (i + 1) Hs)
+ *   total   moe_layer_workspace_size(d)
+ * The ids, weights, counts, offsets, n_dropped and slot_row are read through
+ * moe_layer_aux instead.  Host only; returns MOE_EINVAL for a NULL argument,
+ * MOE_ESHAPE / MOE_EDTYPE for a desc moe_layer_workspace_size rejects. */
+typedef struct {
+    size_t z_pre, z_e, row_src, h, Y, c, h_s;
+    size_t total;
+} moe_layer_ws_layout;
+moe_status moe_layer_workspace_layout(const moe_layer_desc *d, moe_layer_ws_layout *out);
 
 #ifdef __cplusplus
 }

@@ -11,7 +11,7 @@ using namespace moe;
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -270,6 +270,40 @@ struct LayerBufs {
     void* h_s;
 };
 
+}  // namespace
+
+namespace moe {
+
+// moe_permute's argument checks, shared with its allocation-free variant (every
+// check except the workspace's).
+moe_status permute_check(const int32_t* ids, int64_t n_assign, int32_t E, int64_t capacity,
+                         const void* src, moe_dtype dt, int64_t width, int32_t src_div,
+                         const void* dst, int64_t R_phys, const int32_t* slot_row,
+                         const int32_t* row_src, const int32_t* counts, const int32_t* offsets,
+                         const int64_t* n_dropped) {
+    if (E < 1 || E > 1024) return MOE_ESHAPE;
+    if (n_assign < 0 || n_assign >= ((int64_t)1 << 31) || R_phys < 0) return MOE_ESHAPE;
+    const int64_t max_kept = capacity < 0 ? n_assign
+                                          : (capacity * E < n_assign ? capacity * E : n_assign);
+    if (R_phys < max_kept || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
+    if (!counts || !offsets || !n_dropped) return MOE_EINVAL;
+    if (n_assign > 0 && (!ids || !slot_row)) return MOE_EINVAL;
+    if (R_phys > 0 && !row_src) return MOE_EINVAL;
+    if ((src == nullptr) != (dst == nullptr)) return MOE_EINVAL;
+    if (src) {
+        if (!dt_ok(dt)) return MOE_EDTYPE;
+        if (width <= 0 || (width * esize(dt)) % 16 || src_div < 1) return MOE_ESHAPE;
+    }
+    const void* ptrs[] = {ids, src, dst, slot_row, row_src, counts, offsets, n_dropped};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return MOE_EALIGN;
+    return MOE_OK;
+}
+
+}  // namespace moe
+
+namespace {
+
 LayerBufs carve_layer(const moe_layer_desc* d, void* ws, size_t* total) {
     Carver cv(ws);
     LayerBufs b;
@@ -375,22 +409,10 @@ moe_status moe_permute(const int32_t* ids, int64_t n_assign, int32_t E, int64_t 
                        int64_t R_phys, int32_t* slot_row, int32_t* row_src, int32_t* counts,
                        int32_t* offsets, int64_t* n_dropped, void* ws, size_t ws_bytes,
                        moe_stream stream) {
-    if (E < 1 || E > 1024) return MOE_ESHAPE;
-    if (n_assign < 0 || n_assign >= ((int64_t)1 << 31) || R_phys < 0) return MOE_ESHAPE;
-    const int64_t max_kept = capacity < 0 ? n_assign
-                                          : (capacity * E < n_assign ? capacity * E : n_assign);
-    if (R_phys < max_kept || R_phys >= ((int64_t)1 << 31)) return MOE_ESHAPE;
-    if (!counts || !offsets || !n_dropped) return MOE_EINVAL;
-    if (n_assign > 0 && (!ids || !slot_row)) return MOE_EINVAL;
-    if (R_phys > 0 && !row_src) return MOE_EINVAL;
-    if ((src == nullptr) != (dst == nullptr)) return MOE_EINVAL;
-    if (src) {
-        if (!dt_ok(dt)) return MOE_EDTYPE;
-        if (width <= 0 || (width * esize(dt)) % 16 || src_div < 1) return MOE_ESHAPE;
-    }
-    const void* ptrs[] = {ids, src, dst, slot_row, row_src, counts, offsets, n_dropped, ws};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return MOE_EALIGN;
+    const moe_status st = permute_check(ids, n_assign, E, capacity, src, dt, width, src_div, dst,
+                                        R_phys, slot_row, row_src, counts, offsets, n_dropped);
+    if (st != MOE_OK) return st;
+    if (ws && !aligned16(ws)) return MOE_EALIGN;
     if (!ws || ws_bytes < permute_ws_bytes(n_assign, E)) return MOE_EWORKSPACE;
     MOE_TRY(launch_permute(ids, n_assign, E, capacity, src, src ? esize(dt) : 0, width, src_div,
                            dst, R_phys, slot_row, row_src, counts, offsets, n_dropped, nullptr, 0,
@@ -780,6 +802,28 @@ size_t moe_layer_workspace_size(const moe_layer_desc* d) {
     size_t total = 0;
     carve_layer(d, nullptr, &total);
     return total;
+}
+
+moe_status moe_layer_workspace_layout(const moe_layer_desc* d, moe_layer_ws_layout* out) {
+    if (!d || !out) return MOE_EINVAL;
+    if (d->T < 0 || d->E < 1 || d->k < 1) return MOE_ESHAPE;
+    if (!dt_ok(d->dtype)) return MOE_EDTYPE;
+    // carve from a fake base of 0, so each pointer is its region's offset
+    constexpr size_t kNone = ~(size_t)0;
+    char* const base = (char*)(uintptr_t)4096;
+    size_t total = 0;
+    const LayerBufs b = carve_layer(d, base, &total);
+    auto off = [&](const void* p) { return p ? (size_t)((const char*)p - base) : kNone; };
+    out->z_pre = off(b.z_pre);
+    out->z_e = off(b.z_e);
+    out->row_src = off(b.row_src);
+    out->h = off(b.h);
+    out->Y = off(b.Y);
+    // without a latent or shared experts the combine writes y itself
+    out->c = (d->L == 0 && d->n_shared == 0) ? kNone : off(b.c);
+    out->h_s = off(b.h_s);
+    out->total = total;
+    return MOE_OK;
 }
 
 moe_status moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* W, const void* x,

@@ -102,6 +102,14 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                           hipStream_t s, bool out_e4m3 = false, const float* scale = nullptr,
                           float* amax = nullptr);
 
+// moe_permute's host-side argument checks (all but the workspace's), shared by
+// the entry points that group assignments (abi.hip)
+moe_status permute_check(const int32_t* ids, int64_t n_assign, int32_t E, int64_t capacity,
+                         const void* src, moe_dtype dt, int64_t width, int32_t src_div,
+                         const void* dst, int64_t R_phys, const int32_t* slot_row,
+                         const int32_t* row_src, const int32_t* counts, const int32_t* offsets,
+                         const int64_t* n_dropped);
+
 // --------------------------------------------------------------- combine ---
 hipError_t launch_combine(const void* Y, moe_dtype dt, const int32_t* slot_row, const float* w,
                           int64_t T, int k, int64_t width, void* out, int flags, hipStream_t s);

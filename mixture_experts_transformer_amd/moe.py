@@ -117,6 +117,14 @@ _lib.moe_layer_workspace_size.restype = _sz
 _lib.moe_layer_workspace_size.argtypes = [C.POINTER(LayerDesc)]
 
 
+class LayerWsLayout(C.Structure):
+    _fields_ = [(n, _sz) for n in ["z_pre", "z_e", "row_src", "h", "Y", "c", "h_s", "total"]]
+
+
+_lib.moe_layer_workspace_layout.restype = C.c_int
+_lib.moe_layer_workspace_layout.argtypes = [C.POINTER(LayerDesc), C.POINTER(LayerWsLayout)]
+
+
 class MoeError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
@@ -498,6 +506,23 @@ def layer_desc(T, D, L, E, k, H, n_shared, Hs, dtype, eps=1e-5, capacity=-1) -> 
 
 def moe_layer_workspace_size(desc: LayerDesc) -> int:
     return int(_lib.moe_layer_workspace_size(C.byref(desc)))
+
+
+def moe_layer_workspace_layout(desc: LayerDesc) -> dict:
+    """Byte offsets of the layer's intermediate stages inside its workspace (None where
+    the configuration has no such stage), and the workspace's total size."""
+    lay = LayerWsLayout()
+    _check(_lib.moe_layer_workspace_layout(C.byref(desc), C.byref(lay)),
+           "moe_layer_workspace_layout")
+    none = (1 << (8 * C.sizeof(_sz))) - 1
+    return {n: (None if getattr(lay, n) == none else int(getattr(lay, n)))
+            for n, _ in LayerWsLayout._fields_}
+
+
+def moe_grouped_ffn_hidden_offset(E: int) -> int:
+    """Byte offset of the hidden h inside moe_grouped_ffn's workspace (after the
+    row-tile prefix of E + 1 int32, padded to 256 bytes)."""
+    return ((E + 1) * 4 + 255) // 256 * 256
 
 
 def moe_layer_fwd(desc: LayerDesc, W: dict, x, y=None, aux: dict | None = None, ws=None,

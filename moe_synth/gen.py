@@ -76,6 +76,25 @@ def hot_experts(cfg: LayerConfig) -> np.ndarray:
     return np.sort(np.random.default_rng(5).permutation(cfg.E)[:n_hot]).astype(np.int64)
 
 
+def gen_tokens(cfg: LayerConfig, device="cpu", seed: int | None = None) -> torch.Tensor:
+    """The layer's input x alone (the same bytes gen_layer draws for it)."""
+    seed = cfg.seed if seed is None else seed
+    return _normal((cfg.T, cfg.D), 1.0, _gen(seed, "x", device), device, _TORCH_DT[cfg.dtype],
+                   chunk_rows=4096)
+
+
+def router_bias(cfg: LayerConfig, device="cpu", seed: int | None = None,
+                bias_std: float = 0.0) -> torch.Tensor:
+    """The router bias alone (the same values gen_layer draws for it)."""
+    seed = cfg.seed if seed is None else seed
+    b = torch.zeros((cfg.E,), dtype=torch.float32, device=device)
+    if bias_std > 0:
+        b += bias_std * torch.randn((cfg.E,), generator=_gen(seed, "b_r", device), device=device)
+    if cfg.hot_frac > 0:
+        b[torch.as_tensor(hot_experts(cfg), device=device)] += HOT_BIAS
+    return b
+
+
 def gen_layer(cfg: LayerConfig, device="cpu", seed: int | None = None, gain_noise: bool = False,
               bias_std: float = 0.0) -> dict:
     """All inputs of one layer forward, on `device`."""
@@ -84,7 +103,7 @@ def gen_layer(cfg: LayerConfig, device="cpu", seed: int | None = None, gain_nois
     sh = layer_shapes(cfg)
     de = cfg.d_e
     out = {}
-    out["x"] = _normal(sh["x"], 1.0, _gen(seed, "x", device), device, dt, chunk_rows=4096)
+    out["x"] = gen_tokens(cfg, device, seed)
     if cfg.L > 0:
         out["W_dn"] = _normal(sh["W_dn"], 1 / math.sqrt(cfg.D), _gen(seed, "W_dn", device),
                               device, dt, chunk_rows=1024)
@@ -95,12 +114,7 @@ def gen_layer(cfg: LayerConfig, device="cpu", seed: int | None = None, gain_nois
         out["norm_g"] = g
     out["W_r"] = _normal(sh["W_r"], 1 / math.sqrt(de), _gen(seed, "W_r", device), device,
                          torch.float32)
-    b = torch.zeros(sh["b_r"], dtype=torch.float32, device=device)
-    if bias_std > 0:
-        b += bias_std * torch.randn(sh["b_r"], generator=_gen(seed, "b_r", device), device=device)
-    if cfg.hot_frac > 0:
-        b[torch.as_tensor(hot_experts(cfg), device=device)] += HOT_BIAS
-    out["b_r"] = b
+    out["b_r"] = router_bias(cfg, device, seed, bias_std)
     rows_per_chunk = max(1, (1 << 27) // max(1, 2 * cfg.H * de))
     out["W_gu"] = _normal(sh["W_gu"], 1 / math.sqrt(de), _gen(seed, "W_gu", device), device, dt,
                           chunk_rows=rows_per_chunk)

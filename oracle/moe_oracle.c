@@ -47,12 +47,25 @@
  * closed forms, brute force and library routines (see tests/test_oracle_*.py).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define DT_F32 0
 #define DT_BF16 1
+
+/* Threads the parallel loops below use (timing plumbing for the CPU baseline;
+ * results do not depend on it: each loop iteration writes its own outputs). */
+void moe_ref_set_threads(int n)
+{
+    omp_set_num_threads(n > 0 ? n : 1);
+}
+
+int moe_ref_max_threads(void)
+{
+    return omp_get_max_threads();
+}
 
 /* ---------------------------------------------------------------- storage --- */
 

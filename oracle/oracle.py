@@ -57,6 +57,8 @@ def lib():
             build()
             L = C.CDLL(LIB)
             vp, i32, i64, f64 = C.c_void_p, C.c_int32, C.c_int64, C.c_double
+            L.moe_ref_set_threads.argtypes = [C.c_int]
+            L.moe_ref_max_threads.restype = C.c_int
             L.moe_ref_to_bf16.restype = C.c_uint16
             L.moe_ref_to_bf16.argtypes = [f64]
             L.moe_ref_rmsnorm_row.argtypes = [vp, i64, vp, f64, vp]
@@ -87,6 +89,14 @@ def lib():
                                                 vp, vp, vp, vp, vp]
             _lib = L
     return _lib
+
+
+def set_threads(n: int) -> int:
+    """Threads the oracle's parallel loops use from now on; returns the previous
+    count.  Timing plumbing only: no result depends on it."""
+    prev = int(lib().moe_ref_max_threads())
+    lib().moe_ref_set_threads(int(n))
+    return prev
 
 
 def _p(a):

@@ -27,3 +27,16 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    """Every float comparison's figures against the spec's bound (gpu_util.record)."""
+    try:
+        import gpu_util
+    except Exception:
+        return
+    lines = gpu_util.summary_lines()
+    if lines:
+        terminalreporter.section("parity figures (max|err| / RMS of the reference)")
+        for line in lines:
+            terminalreporter.write_line(line)

@@ -41,7 +41,7 @@ def test_status_strings(lib):
     lib.moe_status_str.restype = C.c_char_p
     assert lib.moe_status_str(0) == b"ok"
     assert lib.moe_status_str(5) == b"workspace too small"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def _route(lib, T=4, d=32, E=8, k=2, h=1, W=1, ids=1, w=1, hdt=0):
@@ -256,3 +256,27 @@ def test_forward_ragged_dot_and_fp8_entry_points_reject_bad_arguments(lib):
     assert su(n=0) == 2 and su(n=1025) == 2
     assert su(h=0) == 1 and su(s=0) == 1
     assert su(am=a + 2) == 4
+
+
+def test_layer_workspace_layout(lib):
+    """The stage offsets lie inside the workspace, 256-byte aligned, in carve order,
+    and the stages a configuration lacks are reported absent."""
+    import mixture_experts_transformer_amd as M
+    for args, has_latent, has_c in [((8192, 6144, 3072, 384, 8, 3072, 2, 3072), True, True),
+                                    ((8192, 2048, 0, 64, 4, 1024, 1, 2048), False, True),
+                                    ((100, 256, 0, 16, 2, 128, 0, 128), False, False)]:
+        desc = M.layer_desc(*args, "bf16")
+        lay = M.moe_layer_workspace_layout(desc)
+        assert lay["total"] == M.moe_layer_workspace_size(desc)
+        assert (lay["z_pre"] is not None) == has_latent and (lay["z_e"] is not None) == has_latent
+        assert (lay["c"] is not None) == has_c
+        T, D, L, E, k, H, ns, Hs = args
+        de = L if L else D
+        order = [("row_src", T * k * 4), ("h", T * k * H * 2), ("Y", T * k * de * 2)]
+        for (a, na), (b, _) in zip(order, order[1:]):
+            assert lay[a] % 256 == 0 and lay[a] + na <= lay[b]
+        assert lay["Y"] + T * k * de * 2 <= lay["total"]
+    # a rejected desc is an error, not a layout
+    bad = M.layer_desc(8, 64, 0, 0, 1, 64, 0, 64, "bf16")
+    with pytest.raises(M.MoeError):
+        M.moe_layer_workspace_layout(bad)

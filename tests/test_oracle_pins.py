@@ -262,9 +262,10 @@ def test_hand_worked_three_expert_example():
     np.testing.assert_allclose(y, np.array(G["expected_y"]), rtol=1e-6, atol=1e-7)
 
 
-def _dense_masked_layer(cfg, inp, ids_override=None):
+def _dense_masked_layer(cfg, inp, ids_override=None, parts=False):
     """Brute force in numpy: evaluate EVERY expert on EVERY token and combine
-    with a mask of routing weights -- no permutation, no gather."""
+    with a mask of routing weights -- no permutation, no gather.  parts=True also
+    returns the weights and every expert's stored output on every token."""
     f32 = cfg["dtype"] == "f32"
 
     def val(t):
@@ -292,10 +293,12 @@ def _dense_masked_layer(cfg, inp, ids_override=None):
     M = np.zeros((T, E))
     np.put_along_axis(M, ids, w, 1)
     c = np.zeros((T, ze.shape[1]))
+    Y_all = []
     for e in range(E):
         u = ze @ val(inp["W_gu"][e]).T
         h = store(u[:, :H] / (1 + np.exp(-u[:, :H])) * u[:, H:])
         Ye = store(h @ val(inp["W_d"][e]).T)
+        Y_all.append(Ye)
         c += M[:, e:e + 1] * Ye
     c = store(c)
     y = c @ val(inp["W_up"]).T if cfg["L"] > 0 else c.copy()
@@ -304,6 +307,8 @@ def _dense_masked_layer(cfg, inp, ids_override=None):
         u = x @ val(inp["W_gu_s"][s]).T
         h = store(u[:, :Hs] / (1 + np.exp(-u[:, :Hs])) * u[:, Hs:])
         y += h @ val(inp["W_d_s"][s]).T
+    if parts:
+        return dict(y=y, ids=ids, lg=lg, w=w, Y_all=Y_all)
     return y, ids, lg
 
 
@@ -410,3 +415,54 @@ def test_dropped_assignment_skips_only_that_expert():
     y_first = O.output_tokens(dm1, W, inp["x"].numpy(), np.arange(T), r1, w1)
     np.testing.assert_allclose(y_drop - y_none, y_first, rtol=0, atol=1e-12)
     assert not np.allclose(y_drop, y_full)
+
+
+@pytest.mark.parametrize("dtype,L,cf", [("bf16", 32, None), ("f32", 0, None), ("bf16", 32, 110),
+                                        ("f32", 32, 100)])
+def test_combine_equals_dense_masked_sum(dtype, L, cf):
+    """The oracle's ordered gather over the grouped rows (moe_ref_combine through
+    the oracle's own permutation, optionally with a capacity cut) equals the
+    brute-force sum over EVERY expert of mask x that expert's output, where the
+    mask holds the routing weight of each kept (token, expert) pair and zero
+    elsewhere (dropped pairs contribute nothing and nothing is renormalised)."""
+    cfg, inp = _small(dtype, L, bias=0.3)
+    dn = _dense_masked_layer(cfg, inp, parts=True)
+    ids, w, Y_all = dn["ids"], dn["w"], dn["Y_all"]
+    T, k, E = ids.shape[0], cfg["k"], cfg["E"]
+    cap = O.capacity(cf, 100, T * k, E) if cf else -1
+    g = O.permute(ids.ravel(), E, capacity=cap)
+    if cf:
+        assert g["n_dropped"] > 0
+    R = int(g["offsets"][E])
+    rows = np.zeros((T * k, Y_all[0].shape[1]))
+    for r in range(R):
+        t, j = divmod(int(g["row_src"][r]), k)
+        rows[r] = Y_all[ids[t, j]][t]
+    stored = rows.astype(np.float32) if dtype == "f32" else O.to_bf16(rows)
+    c = O.combine(stored, g["slot_row"], w.astype(np.float32).ravel(), T, k)
+    mask = np.zeros((T, E))
+    kept = g["slot_row"].reshape(T, k) >= 0
+    for t in range(T):
+        for j in range(k):
+            if kept[t, j]:
+                mask[t, ids[t, j]] = w[t, j]
+    dense = sum(mask[:, e:e + 1] * Y_all[e] for e in range(E))
+    scale = np.sqrt(np.mean(dense ** 2))
+    np.testing.assert_allclose(c, dense, rtol=0, atol=1e-12 * scale)
+
+
+def test_combine_with_one_unit_weight_is_the_inverse_permutation():
+    """k = 1 and no weights: the combine scatters each grouped row back to the
+    pool row it came from (row_src is the permutation's inverse); padding rows,
+    which have no grouped row, come out zero."""
+    rng = np.random.default_rng(12)
+    P, E, d = 200, 5, 7
+    ids = rng.integers(0, E, size=P).astype(np.int32)
+    ids[rng.choice(P, 40, replace=False)] = -1
+    g = O.permute(ids, E, R_phys=P)
+    Y = rng.standard_normal((P, d)).astype(np.float32)
+    c = O.combine(Y, g["slot_row"], None, P, 1)
+    R = int(g["offsets"][E])
+    assert R == int((ids >= 0).sum())
+    assert np.array_equal(c[g["row_src"][:R]], Y[:R].astype(np.float64))
+    assert np.all(c[ids < 0] == 0)
