@@ -122,6 +122,26 @@ moe_status moe_permute(const int32_t *ids, int64_t n_assign, int32_t E, int64_t 
                        void *ws, size_t ws_bytes, moe_stream stream);
 size_t moe_permute_workspace_size(int64_t n_assign, int32_t E);
 
+/* moe_permute_noalloc: moe_permute for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation), so cannot provide a workspace.  Arguments, outputs, limits and errors
+ * are moe_permute's, without ws and ws_bytes: the scratch of the grouping passes
+ * lives in a device array inside the library, MOE_PERMUTE_NOALLOC_SCRATCH_BYTES
+ * (16 MiB) on each device, held until the process ends.  It serves every (n_assign,
+ * E) with moe_permute_workspace_size(n_assign, E) <= that size (for example
+ * 1,048,576 assignments over up to 768 experts); larger sizes return
+ * MOE_EWORKSPACE and enqueue nothing.  The call allocates nothing; the first call on
+ * a device looks up that device's copy of the array (host only) and returns
+ * MOE_ELAUNCH if that fails.  Every call on a device shares its copy, which keeps
+ * the last call's contents: calls that overlap on one device (on different streams,
+ * or from several threads without ordering) race, so order them on one stream. */
+#define MOE_PERMUTE_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+moe_status moe_permute_noalloc(const int32_t *ids, int64_t n_assign, int32_t E,
+                               int64_t capacity, const void *src, moe_dtype dt, int64_t width,
+                               int32_t src_div, void *dst, int64_t R_phys, int32_t *slot_row,
+                               int32_t *row_src, int32_t *counts, int32_t *offsets,
+                               int64_t *n_dropped, moe_stream stream);
+
 /* ------------------------------------------------------------ grouped FFN -- */
 /* Per-expert gated MLP over contiguous row groups (the pages' ragged_dot with
  * group sizes: Marin: Week of April 26th summary; the gated expert MLP: Marin:

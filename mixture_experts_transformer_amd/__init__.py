@@ -17,5 +17,5 @@ from .moe import (  # noqa: F401
     moe_ragged_dot, moe_ragged_dot_dlhs, moe_ragged_dot_drhs, moe_ragged_dot_e4m3, moe_route,
     moe_swiglu_quantize_e4m3, status_str, MOE_COMBINE_KEEP_UNROUTED,
     EV_NAMES, MOE_EV_COUNT, moe_layer_workspace_layout, moe_grouped_ffn_hidden_offset,
-    MOE_OK, MOE_EINVAL, MOE_ESHAPE,
+    moe_permute_noalloc, MOE_PERMUTE_NOALLOC_SCRATCH_BYTES, MOE_OK, MOE_EINVAL, MOE_ESHAPE,
     MOE_EDTYPE, MOE_EALIGN, MOE_EWORKSPACE, MOE_ELAUNCH)

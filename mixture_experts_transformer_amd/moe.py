@@ -56,6 +56,10 @@ _lib.moe_permute.argtypes = [_vp, _i64, _i32, _i64, _vp, C.c_int, _i64, _i32, _v
                              _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.moe_permute_workspace_size.restype = _sz
 _lib.moe_permute_workspace_size.argtypes = [_i64, _i32]
+_lib.moe_permute_noalloc.restype = C.c_int
+_lib.moe_permute_noalloc.argtypes = [_vp, _i64, _i32, _i64, _vp, C.c_int, _i64, _i32, _vp, _i64,
+                                     _vp, _vp, _vp, _vp, _vp, _vp]
+MOE_PERMUTE_NOALLOC_SCRATCH_BYTES = 16 << 20
 _lib.moe_grouped_ffn.restype = C.c_int
 _lib.moe_grouped_ffn.argtypes = [_vp, _vp, _i32, _i64, _vp, _vp, _i64, _i64, C.c_int, _vp, _vp,
                                  _sz, _vp]
@@ -223,6 +227,34 @@ def moe_permute(ids, E, capacity=-1, src=None, src_div=1, dst=None, R_phys=None,
                             _ptr(out["counts"]), _ptr(out["offsets"]), _ptr(out["n_dropped"]),
                             _ptr(ws), ws.numel(), _stream()), "moe_permute")
     out["row_src"] = out["row_src"][:R_phys]
+    return out
+
+
+def moe_permute_noalloc(ids, E, out, capacity=-1, src=None, src_div=1, dst=None, R_phys=None):
+    """moe_permute without a workspace, for callers that cannot allocate: the library's
+    own device scratch (MOE_PERMUTE_NOALLOC_SCRATCH_BYTES) serves the grouping passes.
+    Nothing is allocated here either: `out` supplies slot_row [>= n], row_src
+    [>= max(R_phys, 1)], counts [>= E], offsets [>= E + 1] (int32) and n_dropped
+    (int64 [>= 1]).  Calls that overlap on one device race on that scratch."""
+    ids = ids.reshape(-1)
+    n = ids.numel()
+    R_phys = n if R_phys is None else R_phys
+    need = dict(slot_row=(n, torch.int32), row_src=(max(R_phys, 1), torch.int32),
+                counts=(E, torch.int32), offsets=(E + 1, torch.int32),
+                n_dropped=(1, torch.int64))
+    for key, (size, dtype) in need.items():
+        t = out[key]
+        if t.numel() < size or t.dtype != dtype:
+            raise ValueError(f"moe_permute_noalloc: out[{key!r}] must hold {size} {dtype}")
+    if src is not None and (dst is None or dst.dtype != src.dtype
+                            or dst.shape[-1] != src.shape[-1] or dst.shape[0] < R_phys):
+        raise ValueError("moe_permute_noalloc: dst must be [>= R_phys, width] of src's dtype")
+    width = src.shape[-1] if src is not None else 0
+    dt = _dt(src) if src is not None else MOE_F32
+    _check(_lib.moe_permute_noalloc(_ptr(ids), n, E, capacity, _ptr(src), dt, width, src_div,
+                                    _ptr(dst), R_phys, _ptr(out["slot_row"]), _ptr(out["row_src"]),
+                                    _ptr(out["counts"]), _ptr(out["offsets"]),
+                                    _ptr(out["n_dropped"]), _stream()), "moe_permute_noalloc")
     return out
 
 
