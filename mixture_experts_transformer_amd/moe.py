@@ -168,6 +168,24 @@ def _ws(nbytes: int, device, ws):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _check_group_out(out: dict, n: int, R_phys: int, G: int, where: str):
+    """Caller-supplied grouping outputs: sizes and dtypes the kernels will write."""
+    need = dict(slot_row=(n, torch.int32), row_src=(max(R_phys, 1), torch.int32),
+                counts=(G, torch.int32), offsets=(G + 1, torch.int32),
+                n_dropped=(1, torch.int64))
+    for key, (size, dtype) in need.items():
+        t = out.get(key)
+        if t is None or t.numel() < size or t.dtype != dtype:
+            raise ValueError(f"{where}: out[{key!r}] must hold at least {size} {dtype}")
+
+
+def _check_rows(t, rows: int, width: int, dtype, where: str, what: str):
+    """A destination matrix of at least `rows` rows of `width` elements of dtype."""
+    if t.dtype != dtype or t.dim() != 2 or t.shape[0] < rows or t.shape[1] != width:
+        raise ValueError(f"{where}: {what} must be [>= {rows}, {width}] {dtype}, "
+                         f"got {tuple(t.shape)} {t.dtype}")
+
+
 def abi_version() -> int:
     return _lib.moe_abi_version()
 
@@ -215,9 +233,11 @@ def moe_permute(ids, E, capacity=-1, src=None, src_div=1, dst=None, R_phys=None,
                    n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
     else:
         out = dict(out)
-        if (out["slot_row"].numel() < n or out["row_src"].numel() < max(R_phys, 1)
-                or out["counts"].numel() < E or out["offsets"].numel() < E + 1):
-            raise ValueError("moe_permute: an `out` tensor is too small")
+        _check_group_out(out, n, R_phys, E, "moe_permute")
+    if src is not None:
+        if dst is None:
+            raise ValueError("moe_permute: a row copy needs dst")
+        _check_rows(dst, R_phys, src.shape[-1], src.dtype, "moe_permute", "dst")
     need = moe_permute_workspace_size(n, E)
     ws = _ws(need, dev, ws)
     width = src.shape[-1] if src is not None else 0
@@ -239,16 +259,11 @@ def moe_permute_noalloc(ids, E, out, capacity=-1, src=None, src_div=1, dst=None,
     ids = ids.reshape(-1)
     n = ids.numel()
     R_phys = n if R_phys is None else R_phys
-    need = dict(slot_row=(n, torch.int32), row_src=(max(R_phys, 1), torch.int32),
-                counts=(E, torch.int32), offsets=(E + 1, torch.int32),
-                n_dropped=(1, torch.int64))
-    for key, (size, dtype) in need.items():
-        t = out[key]
-        if t.numel() < size or t.dtype != dtype:
-            raise ValueError(f"moe_permute_noalloc: out[{key!r}] must hold {size} {dtype}")
-    if src is not None and (dst is None or dst.dtype != src.dtype
-                            or dst.shape[-1] != src.shape[-1] or dst.shape[0] < R_phys):
-        raise ValueError("moe_permute_noalloc: dst must be [>= R_phys, width] of src's dtype")
+    _check_group_out(out, n, R_phys, E, "moe_permute_noalloc")
+    if src is not None:
+        if dst is None:
+            raise ValueError("moe_permute_noalloc: a row copy needs dst")
+        _check_rows(dst, R_phys, src.shape[-1], src.dtype, "moe_permute_noalloc", "dst")
     width = src.shape[-1] if src is not None else 0
     dt = _dt(src) if src is not None else MOE_F32
     _check(_lib.moe_permute_noalloc(_ptr(ids), n, E, capacity, _ptr(src), dt, width, src_div,
@@ -274,11 +289,8 @@ def moe_permute_e4m3(ids, E, src, dst, capacity=-1, src_div=1, R_phys=None, scal
                    n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
     else:
         out = dict(out)
-        if (out["slot_row"].numel() < n or out["row_src"].numel() < max(R_phys, 1)
-                or out["counts"].numel() < E or out["offsets"].numel() < E + 1):
-            raise ValueError("moe_permute_e4m3: an `out` tensor is too small")
-    if dst.dtype != torch.uint8 or dst.shape[-1] != src.shape[-1]:
-        raise ValueError("moe_permute_e4m3: dst is uint8 codes of src's width")
+        _check_group_out(out, n, R_phys, E, "moe_permute_e4m3")
+    _check_rows(dst, R_phys, src.shape[-1], torch.uint8, "moe_permute_e4m3", "dst")
     ws = _ws(moe_permute_workspace_size(n, E), dev, ws)
     _check(_lib.moe_permute_e4m3(_ptr(ids), n, E, capacity, _ptr(src), _dt(src), src.shape[-1],
                                  src_div, _ptr(dst), R_phys, _ptr(out["slot_row"]),
@@ -311,10 +323,14 @@ def moe_dispatch_pack(expert_ids, E, n_peers, x, capacity=-1, R_phys=None, send_
                    n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
     else:
         out = dict(out)
+        _check_group_out(out, n, R_phys, n_peers, "moe_dispatch_pack")
     if send_rows is None:
         send_rows = torch.empty((R_phys, x.shape[-1]), dtype=x.dtype, device=dev)
+    _check_rows(send_rows, R_phys, x.shape[-1], x.dtype, "moe_dispatch_pack", "send_rows")
     if send_expert is None:
         send_expert = torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev)
+    if send_expert.dtype != torch.int32 or send_expert.numel() < max(R_phys, 1):
+        raise ValueError(f"moe_dispatch_pack: send_expert must hold at least {max(R_phys, 1)} int32")
     ws = _ws(moe_dispatch_pack_workspace_size(n, n_peers), dev, ws)
     _check(_lib.moe_dispatch_pack(_ptr(expert_ids), T, k, E, n_peers, capacity, _ptr(x), _dt(x),
                                   x.shape[-1], _ptr(send_rows), _ptr(send_expert), R_phys,
@@ -340,8 +356,13 @@ def moe_dispatch_pack_e4m3(expert_ids, E, n_peers, x, capacity=-1, R_phys=None, 
                n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
     if send_rows is None:
         send_rows = torch.empty((R_phys, x.shape[-1]), dtype=torch.uint8, device=dev)
+    _check_rows(send_rows, R_phys, x.shape[-1], torch.uint8, "moe_dispatch_pack_e4m3",
+                "send_rows")
     if send_expert is None:
         send_expert = torch.empty(max(R_phys, 1), dtype=torch.int32, device=dev)
+    if send_expert.dtype != torch.int32 or send_expert.numel() < max(R_phys, 1):
+        raise ValueError("moe_dispatch_pack_e4m3: send_expert must hold at least "
+                         f"{max(R_phys, 1)} int32")
     ws = _ws(moe_dispatch_pack_workspace_size(n, n_peers), dev, ws)
     _check(_lib.moe_dispatch_pack_e4m3(_ptr(expert_ids), T, k, E, n_peers, capacity, _ptr(x),
                                        _dt(x), x.shape[-1], _ptr(send_rows), _ptr(send_expert),
