@@ -36,10 +36,14 @@
 // sub-tile, 128 accumulators).  The wave's 32-row blocks are interleaved (wm,
 // wm+2, ...) so both row waves stay busy on a partial tile, and the tile body is
 // specialised on how many of them are active, so each case is straight-line
-// MFMA code.  For the SwiGLU epilogue a wave's two column blocks are the gate
-// and the up rows of the same 32 hidden columns, so the activation is formed on
-// the way out and neither G nor U is ever stored.  Results leave through a
-// per-wave LDS piece in 16-byte row chunks, with no block-wide barrier.
+// MFMA code.  The MFMAs take the B fragment as their first operand, so each
+// lane ends up holding one output row and four consecutive columns per group
+// of accumulator registers.  For the SwiGLU epilogue a wave's two column blocks
+// are the gate and the up rows of the same 32 hidden columns, so the activation
+// is formed on the way out and neither G nor U is ever stored.  Results are
+// rounded to bf16 two at a time by the hardware conversion and leave through a
+// per-wave LDS piece (written four values per lane at a time, read back in
+// 16-byte row chunks), with no block-wide barrier.
 //
 // Scheduling: a persistent grid (a multiple of 8 workgroups).  Workgroups are
 // dealt to the 8 XCDs round-robin, so workgroup b runs on XCD b % 8; each XCD
@@ -200,17 +204,17 @@ template <>
 __device__ __forceinline__ void store_vec<bf16_t, 8>(bf16_t* C, int64_t off, const float* v,
                                                      bool nt) {
     u32x4 x;
-    x[0] = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    x[1] = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-    x[2] = (uint32_t)f32_to_bf16(v[4]) | ((uint32_t)f32_to_bf16(v[5]) << 16);
-    x[3] = (uint32_t)f32_to_bf16(v[6]) | ((uint32_t)f32_to_bf16(v[7]) << 16);
+    x[0] = pack_bf16x2(v[0], v[1]);
+    x[1] = pack_bf16x2(v[2], v[3]);
+    x[2] = pack_bf16x2(v[4], v[5]);
+    x[3] = pack_bf16x2(v[6], v[7]);
     store16(C + off, x, nt);
 }
 
 // AA: A's steps run two ahead in the three-slot ring (dense GEMMs, and grouped
 // ones whose weights serve several row tiles); otherwise B's do (grouped GEMMs
 // that stream each expert's weights once).
-template <typename T, typename OutT, int EPI, bool AA, int LAY>
+template <typename T, typename OutT, int EPI, bool AA, int LAY, bool SPLIT = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     constexpr bool kAT = (LAY & 1) != 0;      // A stored [reduction][row]
     constexpr bool kBT = (LAY & 2) != 0;      // B stored [reduction][column]
@@ -258,6 +262,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             hi = uniform64(p.xcd_split[xcd + 1]);
         }
     }
+    // SPLIT (dense GEMMs whose last round of tiles is at most half full): each
+    // XCD's workgroups take its tiles in rounds of nslots, and the tiles of the
+    // last round are split by rows into `pieces` (2 or 4) parts, so that it keeps
+    // as many CUs busy as it can (384 tiles on 256 CUs: the 16 tiles per XCD of
+    // the second round become 32 half tiles).  A row's result is computed the
+    // same way whichever piece it is in.  A separate instantiation: adding this
+    // to every GEMM made the grouped ones 4-7% slower.
+    static_assert(!SPLIT || !kRK, "no row split of a weight-gradient tile");
+    int64_t full = hi - lo, rem = 0;
+    int pieces = 1;
+    if constexpr (SPLIT) {
+        full = ((hi - lo) / nslots) * nslots;
+        rem = (hi - lo) - full;
+        if (rem * 4 <= nslots) pieces = 4;
+        else if (rem * 2 <= nslots) pieces = 2;
+    }
+    const int64_t n_units = full + rem * pieces;
 
     // fragment read offsets (the swizzle depends only on row % 32)
     const int fl = swz(lane & 31);
@@ -331,6 +352,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         }
         tl.nrb = (int)((tl.rows_valid + 31) >> 5);       // active 32-row blocks
         tl.n0 = tn * kColsOut;
+        return tl;
+    };
+    // the tile (or the rows of a tile) that unit u of this XCD computes
+    auto unit_at = [&](int64_t u) __attribute__((always_inline)) {
+        int64_t ti = u, skip = 0;
+        int sub = kBM;
+        if (u >= full) {
+            const int64_t v = u - full;
+            ti = full + v / pieces;
+            sub = kBM / pieces;
+            skip = (v - (ti - full) * pieces) * sub;
+        }
+        Tile tl = tile_at(lo + ti);
+        tl.row0 += skip;
+        tl.rows_valid = max((int64_t)0, min((int64_t)sub, tl.rows_valid - skip));
+        tl.nrb = (int)((tl.rows_valid + 31) >> 5);
         return tl;
     };
 
@@ -499,9 +536,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     float* const stage = (float*)(lds + (AA ? 0 : kBBase) + 2 * kOpBytes + wave * 4096);
     static_assert(kSlotsFar == 3 && kWaves * 4096 == kOpBytes, "staging layout");
 
-    int64_t t = lo + slot;
-    if (t >= hi) return;
-    Tile cur = tile_at(t);
+    // this workgroup's unit (SPLIT) or tile
+    int64_t t = SPLIT ? (int64_t)slot : lo + slot;
+    if (t >= (SPLIT ? n_units : hi)) return;
+    Tile cur = SPLIT ? unit_at(t) : tile_at(t);
     set_sources(cur);
     set_segment(cur, 0);
     __syncthreads();
@@ -614,11 +652,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 if (q & 1) {
 #pragma unroll
                     for (int i = 0; i < NACT; i++)
-                        acc[i][1] = Mfma<T>::mma(as_frag(fa[0][i]), as_frag(fb[0][0]), acc[i][1]);
+                        acc[i][1] = Mfma<T>::mma(as_frag(fb[0][0]), as_frag(fa[0][i]), acc[i][1]);
                 } else {
 #pragma unroll
                     for (int i = 0; i < NACT; i++)
-                        acc[i][0] = Mfma<T>::mma(as_frag(fa[0][i]), as_frag(fb[0][0]), acc[i][0]);
+                        acc[i][0] = Mfma<T>::mma(as_frag(fb[0][0]), as_frag(fa[0][i]), acc[i][0]);
                 }
             } else {
 #pragma unroll
@@ -627,7 +665,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                     for (int i = 0; i < NACT; i++)
 #pragma unroll
                         for (int j = 0; j < 2; j++)
-                            acc[i][j] = Mfma<T>::mma(as_frag(fa[hs][i]), as_frag(fb[hs][j]), acc[i][j]);
+                            acc[i][j] = Mfma<T>::mma(as_frag(fb[hs][j]), as_frag(fa[hs][i]), acc[i][j]);
             }
         };
         // Instruction order within a quarter step: one MFMA, then the fragment
@@ -766,13 +804,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         __syncthreads();
 
         const Tile done = cur;
-        const bool more = t + nslots < hi;
+        const bool more = t + nslots < (SPLIT ? n_units : hi);
 
-        // ---- epilogue.  Each 32-row block of the wave is staged through its
-        // own LDS piece (no block-wide barrier: only the wave reads what it
-        // wrote) so that every global store is a 16-byte chunk of a row.  For
-        // SwiGLU a wave's two column blocks are the gate and the up rows of the
-        // same hidden columns, so h = silu(G) * U is formed in registers first.
+        // ---- epilogue.  The MFMAs take the B fragment first, so in each 32 x 32
+        // block a lane holds one row (lane % 32) and, in accumulator registers
+        // 4 q .. 4 q + 3, the four consecutive columns 8 q + 4 (lane / 32) + 0..3.
+        // A block goes through the wave's own 4 KB LDS piece (no block-wide
+        // barrier: only the wave reads what it wrote), written four values at a
+        // time and read back a row chunk at a time, so every global store is a
+        // 16-byte chunk of a row.  Rows of the piece are 128 bytes; their 16-byte
+        // chunks are XOR-swizzled by the row so that the writes of 8 consecutive
+        // rows fall on distinct banks.
         OutT* const C = (OutT*)p.C;
         const bool nt_out = p.nt_store != 0;
         if constexpr (kFp8) {
@@ -784,14 +826,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
 #pragma unroll
                     for (int v = 0; v < 16; v++) acc[i][j][v] *= sc;
         }
-        constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
-        // write back R staged rows of W columns starting at tile row rbase
-        auto store_rows = [&](auto r_c, auto w_c, int rbase, int64_t cbase)
-            __attribute__((always_inline)) {
-            constexpr int R = decltype(r_c)::value, W = decltype(w_c)::value;
-            constexpr int kChunks = W / kVec;
+        const int er = lane & 31;          // the lane's row within a block
+        const int eh = lane >> 5;          // which four of each eight columns
+        const int esw = er & 7;            // chunk swizzle of that row
+        char* const piece = (char*)stage;
+        // float32 staging of one 32 x 32 block: four floats (one 16-byte chunk)
+        // per write; chunk c of row r at chunk c ^ (r & 7)
+        auto stage_f32 = [&](const float (&vals)[16]) __attribute__((always_inline)) {
 #pragma unroll
-            for (int q = lane; q < R * kChunks; q += 64) {
+            for (int q = 0; q < 4; q++) {
+                const float4 x = {vals[4 * q], vals[4 * q + 1], vals[4 * q + 2], vals[4 * q + 3]};
+                *(float4*)(piece + er * 128 + (((2 * q + eh) ^ esw) << 4)) = x;
+            }
+        };
+        // value of row r, columns c .. c + 3 (c a multiple of 4) of a staged
+        // float32 block
+        auto staged_f32 = [&](int r, int c) __attribute__((always_inline)) {
+            return *(const float4*)(piece + r * 128 + ((((c >> 2)) ^ (r & 7)) << 4));
+        };
+        constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
+        // write back a staged float32 block (32 rows of 32 columns starting at
+        // tile row rbase, column cbase), with the epilogue's per-element work
+        auto store_f32_block = [&](int rbase, int64_t cbase) __attribute__((always_inline)) {
+            constexpr int kChunks = 32 / kVec;
+#pragma unroll
+            for (int q = lane; q < 32 * kChunks; q += 64) {
                 const int r = q / kChunks;
                 const int cc = (q % kChunks) * kVec;
                 const int64_t grow = rbase + r;
@@ -799,7 +858,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 if (grow < done.rows_valid && col < p.N) {
                     float vals[kVec];
 #pragma unroll
-                    for (int e = 0; e < kVec; e++) vals[e] = stage[r * W + cc + e];
+                    for (int e = 0; e < kVec; e += 4) {
+                        const float4 x = staged_f32(r, cc + e);
+                        vals[e] = x.x;
+                        vals[e + 1] = x.y;
+                        vals[e + 2] = x.z;
+                        vals[e + 3] = x.w;
+                    }
                     if (EPI == EPI_ADD) {
                         const int64_t aoff = (done.row0 + grow) * p.ld_add + col;
 #pragma unroll
@@ -832,35 +897,88 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                 }
             }
         };
-        using I16 = std::integral_constant<int, 16>;
+        // bf16 staging of 32 rows x W columns (W = 32 or 64, rows of 2 W bytes):
+        // four values (8 bytes) per write at columns cbase + 8 q + 4 (lane / 32);
+        // 16-byte chunk c of row r at chunk c ^ (r & 7) (W = 64) or c ^ (r & 3)
+        // (W = 32)
+        auto stage_bf16 = [&](auto w_c, int cbase, const float (&vals)[16])
+            __attribute__((always_inline)) {
+            constexpr int W = decltype(w_c)::value;
+            constexpr int kRow = 2 * W, kMask = W / 8 - 1;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const int c = cbase / 8 + q;
+                uint2 x;
+                x.x = pack_bf16x2(vals[4 * q], vals[4 * q + 1]);
+                x.y = pack_bf16x2(vals[4 * q + 2], vals[4 * q + 3]);
+                *(uint2*)(piece + er * kRow + ((c ^ (er & kMask)) << 4) + (eh << 3)) = x;
+            }
+        };
+        // write back a staged bf16 block of 32 rows x W columns
+        auto store_bf16_block = [&](auto w_c, int rbase, int64_t cbase) __attribute__((always_inline)) {
+            constexpr int W = decltype(w_c)::value;
+            constexpr int kRow = 2 * W, kMask = W / 8 - 1, kChunks = W / 8;
+#pragma unroll
+            for (int q = lane; q < 32 * kChunks; q += 64) {
+                const int r = q / kChunks;
+                const int cc = q % kChunks;
+                const int64_t grow = rbase + r;
+                const int64_t col = cbase + cc * 8;
+                if (grow < done.rows_valid && col < p.N) {
+                    const u32x4 x = *(const u32x4*)(piece + r * kRow + ((cc ^ (r & kMask)) << 4));
+                    store16(C + (done.row0 + grow) * p.ldc + col, x, nt_out);
+                }
+            }
+        };
         using I32 = std::integral_constant<int, 32>;
         using I64 = std::integral_constant<int, 64>;
+        constexpr bool kBf16Out = std::is_same<OutT, bf16_t>::value;
 #pragma unroll
         for (int i = 0; i < NACT; i++) {
             const int rbase = (wm + 2 * i) * 32;
             if (EPI == EPI_SWIGLU) {
+                // a wave's two column blocks are the gate and the up rows of the
+                // same 32 hidden columns: h = silu(G) * U in registers
+                float hv[16];
 #pragma unroll
-                for (int v = 0; v < 16; v++)
-                    stage[acc_row(v, lane) * 32 + (lane & 31)] =
-                        silu_f(acc[i][0][v]) * acc[i][1][v];
-                store_rows(I32{}, I32{}, rbase, done.n0 + wn * 32);
+                for (int v = 0; v < 16; v++) hv[v] = silu_fast(acc[i][0][v]) * acc[i][1][v];
+                if constexpr (kBf16Out) {
+                    stage_bf16(I32{}, 0, hv);
+                    store_bf16_block(I32{}, rbase, done.n0 + wn * 32);
+                } else {
+                    stage_f32(hv);
+                    store_f32_block(rbase, done.n0 + wn * 32);
+                }
+            } else if (EPI == EPI_STORE && kBf16Out) {
+                // both column blocks at once: 64 columns of bf16, 128-byte rows
+                float v0[16], v1[16];
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    v0[v] = acc[i][0][v];
+                    v1[v] = acc[i][1][v];
+                }
+                stage_bf16(I64{}, 0, v0);
+                stage_bf16(I64{}, 32, v1);
+                store_bf16_block(I64{}, rbase, done.n0 + wn * 64);
             } else {
-                // two halves of 16 rows: registers v < 8 hold rows 0-15
 #pragma unroll
-                for (int h = 0; h < 2; h++) {
+                for (int j = 0; j < 2; j++) {
+                    float vv[16];
 #pragma unroll
-                    for (int j = 0; j < 2; j++)
-#pragma unroll
-                        for (int v = 0; v < 8; v++)
-                            stage[(acc_row(v, lane)) * 64 + j * 32 + (lane & 31)] =
-                                acc[i][j][v + 8 * h];
-                    store_rows(I16{}, I64{}, rbase + 16 * h, done.n0 + wn * 64);
+                    for (int v = 0; v < 16; v++) vv[v] = acc[i][j][v];
+                    stage_f32(vv);
+                    store_f32_block(rbase, done.n0 + wn * 64 + j * 32);
                 }
             }
         }
+        // The next tile's first loads go out after the epilogue.  Issued before
+        // it, they would overlap its work, but the epilogue reloads registers
+        // the K loop spilled, and every scratch reload waits for all
+        // outstanding loads (vmcnt(0)), the new tile's included: measured
+        // slower (535B gate/up GEMM 3.10 -> 3.28 ms, pool FFN 2.84 -> 2.92 ms).
         if (more) {
             t += nslots;
-            cur = tile_at(t);
+            cur = SPLIT ? unit_at(t) : tile_at(t);
             set_sources(cur);
             set_segment(cur, 0);
             prologue();
@@ -967,15 +1085,30 @@ __global__ __launch_bounds__(64) void dw_split_kernel(const int32_t* offsets, in
 
 constexpr size_t kLdsBytes = (size_t)(kSlotsFar + kSlotsNear) * kOpBytes;   // 163,840 bytes
 
-template <typename T, typename OutT, int EPI, bool AA, int LAY>
+template <typename T, typename OutT, int EPI, bool AA, int LAY, bool SPLIT = false>
 hipError_t launch_aa(const GemmParams& p, int grid, hipStream_t s) {
     // opting in to more than 64 KB of dynamic LDS is idempotent and cheap
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI, AA, LAY>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_kernel<T, OutT, EPI, AA, LAY, SPLIT>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsBytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI, AA, LAY>), dim3(grid), dim3(kThreads),
+    hipLaunchKernelGGL((gemm_kernel<T, OutT, EPI, AA, LAY, SPLIT>), dim3(grid), dim3(kThreads),
                        kLdsBytes, s, p);
     return hipGetLastError();
+}
+
+// Whether a dense GEMM's last round of tiles is at most half full on some XCD
+// (then the row-split variant keeps more CUs busy in that round).
+bool dense_split_pays(const GemmParams& p, int epi, int grid) {
+    if (p.offsets || p.layout != LAY_NN) return false;
+    const int64_t cols = epi == EPI_SWIGLU ? kBN / 2 : kBN;
+    const int64_t total = ((p.M + kBM - 1) / kBM) * ((p.N + cols - 1) / cols);
+    const int nslots = grid / kNumXcd;
+    for (int x = 0; x < kNumXcd; x++) {
+        const int64_t n_x = total * (x + 1) / kNumXcd - total * x / kNumXcd;
+        const int64_t rem = n_x % nslots;
+        if (rem > 0 && 2 * rem <= nslots) return true;
+    }
+    return false;
 }
 
 template <typename T, typename OutT, int EPI, int LAY = LAY_NN>
@@ -1065,6 +1198,14 @@ hipError_t launch_gemm(const GemmParams& p, moe_dtype in_dt, bool out_f32, int e
         if (epi != EPI_STORE) return hipErrorInvalidValue;    // E4M3 operands: plain stores
         return out_f32 ? launch_t<fp8_t, float, EPI_STORE>(p, (int)grid, s)
                        : launch_t<fp8_t, bf16_t, EPI_STORE>(p, (int)grid, s);
+    }
+    if (in_dt == MOE_BF16 && p.a_ahead && dense_split_pays(p, epi, (int)grid)) {
+        if (epi == EPI_STORE)
+            return out_f32 ? launch_aa<bf16_t, float, EPI_STORE, true, LAY_NN, true>(p, (int)grid, s)
+                           : launch_aa<bf16_t, bf16_t, EPI_STORE, true, LAY_NN, true>(p, (int)grid, s);
+        if (epi == EPI_SWIGLU)
+            return launch_aa<bf16_t, bf16_t, EPI_SWIGLU, true, LAY_NN, true>(p, (int)grid, s);
+        return launch_aa<bf16_t, bf16_t, EPI_ADD, true, LAY_NN, true>(p, (int)grid, s);
     }
     if (in_dt == MOE_BF16) {
         if (epi == EPI_STORE)

@@ -377,3 +377,63 @@ def test_expert_parallel_legs_reproduce_the_local_routed_output(M):
     c_ep = M.moe_combine(ret, d["slot_row"], w_d, T, k)
     torch.cuda.synchronize()
     assert torch.equal(c_ep.view(torch.int16), c_local.view(torch.int16))
+
+
+def test_swiglu_activation_accuracy(M):
+    """The expert MLP's activation on its own, through moe_grouped_ffn in float32
+    with identity-structured weights: the gate row i picks x_i, the up row i picks
+    a column of ones and the down projection picks h_i, so every product and sum
+    is exact and Y = silu(x) as the GEMM epilogue computes it.  Against silu in
+    double precision over 2^20 values from -80 to 80 (dense near 0): within 4
+    units in the last place of float32 (an exact exp and an exact division; the
+    pages report that an approximate fused activation broke parity).  Below -80
+    the result is below 1e-30 in magnitude, as is the exact value."""
+    H, R = 128, 8192
+    d = 2 * H
+    n = R * H
+    g = np.random.default_rng(5)
+    x = np.concatenate([np.linspace(-80.0, 80.0, n // 2),
+                        g.standard_normal(n // 2 - 1024) * 4.0,
+                        -80.0 - np.arange(1024) * 0.05]).astype(np.float32)
+    X = np.zeros((R, d), np.float32)
+    X[:, :H] = x.reshape(R, H)
+    X[:, H:] = 1.0
+    W_gu = np.zeros((1, 2 * H, d), np.float32)
+    W_gu[0, np.arange(H), np.arange(H)] = 1.0            # gate row i: x_i
+    W_gu[0, H + np.arange(H), H + np.arange(H)] = 1.0    # up row i: 1
+    W_d = np.zeros((1, d, H), np.float32)
+    W_d[0, np.arange(H), np.arange(H)] = 1.0             # Y[:, i] = h_i
+    off = torch.tensor([0, R], dtype=torch.int32, device=DEV)
+    Y = M.moe_grouped_ffn(torch.from_numpy(X).to(DEV), off, torch.from_numpy(W_gu).to(DEV),
+                          torch.from_numpy(W_d).to(DEV))
+    torch.cuda.synchronize()
+    got = Y.cpu().numpy()[:, :H].ravel().astype(np.float64)
+    assert np.all(Y.cpu().numpy()[:, H:] == 0)
+    xd = x.astype(np.float64)
+    ref = xd / (1.0 + np.exp(-xd))
+    main = xd >= -80.0
+    ulp = np.spacing(np.abs(ref[main]).astype(np.float32)).astype(np.float64)
+    err_ulp = np.abs(got[main] - ref[main]) / ulp
+    print(f"silu: max error {err_ulp.max():.2f} ulp, mean {err_ulp.mean():.3f} ulp over "
+          f"{main.sum()} values")
+    assert err_ulp.max() <= 4.0
+    assert np.all(np.abs(got[~main]) < 1e-30) and np.all(np.abs(ref[~main]) < 1e-30)
+
+
+@pytest.mark.parametrize("tiles,pieces", [(320, 4), (384, 2), (8 * 36 + 8 * 9, 2)])
+def test_partial_last_round_split_by_rows(M, tiles, pieces):
+    """A GEMM whose last round of tiles is at most half full splits those tiles
+    by rows (into `pieces` parts per XCD's range): one 256-row x 256-column tile
+    per 256 rows of a single group, on the full 256-CU grid.  Against the oracle's
+    grouped matmul; the rows are computed the same way as in an unsplit tile."""
+    K, N = 128, 256
+    R = tiles * 256 - 100                      # a ragged last tile
+    g = torch.Generator().manual_seed(tiles)
+    X = torch.randn((R, K), generator=g).to(torch.bfloat16)
+    W = (torch.randn((1, N, K), generator=g) / K ** 0.5).to(torch.bfloat16)
+    off = torch.tensor([0, R], dtype=torch.int32)
+    Z = M.moe_ragged_dot(X.to(DEV), off.to(DEV), W.to(DEV), z_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = O.ragged_dot(TB.host(X), TB.host(W), off.numpy())
+    # bf16 products summed in float32 and stored in float32: the float32 bound
+    assert_close(Z.cpu().numpy(), ref, "f32", f"split last round ({tiles} tiles)")
