@@ -17,12 +17,20 @@
 //           local ranks and per-segment counts.
 //   pass 2  one workgroup per expert: exclusive scan of that expert's segment
 //           counts (each segment's base) and the expert's total.
-//   pass 3  one workgroup: the capacity cut, the exclusive scan of kept rows
-//           (offsets), the drop count and optionally the GEMM's row-tile prefix.
-//   pass 4  one thread per assignment: row = offsets[e] + base + local rank,
-//           dropped if that rank reaches the capacity; writes slot_row/row_src,
-//           and marks the rows past the last kept one empty.
-//   pass 5  (only with a source) one wave per destination row copies the row.
+//   pass 3  every workgroup first recomputes, into LDS, the capacity cut and the
+//           exclusive scan of kept rows over all experts (E <= 1024 counts, a
+//           few hundred cycles), so no workgroup waits on another and no pass
+//           of its own is launched for it; workgroup 0 also writes the offsets,
+//           the drop count and optionally the GEMM's row-tile prefix.  Then
+//           row = offsets[e] + base + local rank, dropped if that rank reaches
+//           the capacity; writes slot_row/row_src and marks the rows past the
+//           last kept one empty.  With a source row shared by several
+//           assignments, the same kernel copies each source row (one wave per
+//           source row) to the rows of its kept assignments; otherwise one thread
+//           per assignment places, and with one source row per assignment a
+//           fourth pass gathers the rows in destination order.
+#include <algorithm>
+
 #include "common.h"
 #include "e4m3.h"
 #include "kernels.h"
@@ -114,53 +122,87 @@ __global__ __launch_bounds__(256) void colscan_kernel(int64_t nseg, int E, int32
     if (tid == 0) counts[e] = total;
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(int E, int64_t capacity, const int32_t* counts,
-                                                    int32_t* offsets, int64_t* n_dropped,
-                                                    int32_t* tile_prefix, int tile_bm) {
-    __shared__ int red[16];
-    __shared__ long long dred[16];
+// Start of every placement workgroup (256 threads): kept = min(count, capacity)
+// per expert and offs[x] = the exclusive prefix of kept (offs[E] the total), into
+// the workgroup's LDS.  Workgroup 0 also writes offsets[0..E], n_dropped and,
+// if tile_prefix is given, the exclusive prefix of each expert's row tiles of
+// tile_bm rows (tile_prefix[E] the total).  Returns the kept total.
+__device__ int expert_offsets(const int32_t* counts, int E, int64_t capacity, int32_t* offs,
+                              int* red, int32_t* offsets, int64_t* n_dropped,
+                              int32_t* tile_prefix, int tile_bm) {
+    __shared__ long long dred[4];
+    constexpr int kPer = kMaxE / 256;                 // experts per thread
     const int tid = threadIdx.x;
-    int kept = 0, tiles = 0;
-    long long dropped = 0;
-    if (tid < E) {
-        const int run = counts[tid];
-        kept = (capacity >= 0 && run > capacity) ? (int)capacity : run;
-        dropped = run - kept;
-        if (tile_prefix) tiles = (kept + tile_bm - 1) / tile_bm;
-    }
-    int total;
-    const int ex = block_exclusive_scan_1024(kept, red, total);
-    if (tid < E) offsets[tid] = ex;
-    if (tid == 0) offsets[E] = total;
-    if (tile_prefix) {
-        int ttot;
-        const int tex = block_exclusive_scan_1024(tiles, red, ttot);
-        if (tid < E) tile_prefix[tid] = tex;
-        if (tid == 0) tile_prefix[E] = ttot;
-    }
-    // drop count: wave sums, then one wave over the partials
-    long long d = dropped;
+    int kept[kPer];
+    int ksum = 0;
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) d += __shfl_xor(d, off, 64);
-    if ((tid & 63) == 0) dred[tid >> 6] = d;
-    __syncthreads();
-    if (tid == 0) {
-        long long s = 0;
-        for (int i = 0; i < (int)(blockDim.x >> 6); i++) s += dred[i];
-        *n_dropped = s;
+    for (int q = 0; q < kPer; q++) {
+        const int x = tid * kPer + q;
+        const int c = x < E ? counts[x] : 0;
+        kept[q] = (capacity >= 0 && c > capacity) ? (int)capacity : c;
+        ksum += kept[q];
     }
+    int ktot;
+    const int kex = block_exclusive_scan_1024(ksum, red, ktot);
+    int run = kex;
+#pragma unroll
+    for (int q = 0; q < kPer; q++) {
+        const int x = tid * kPer + q;
+        if (x < E) offs[x] = run;
+        run += kept[q];
+    }
+    if (tid == 0) offs[E] = ktot;
+    if (blockIdx.x == 0) {                            // uniform over the workgroup
+        run = kex;
+        int tsum = 0;
+        long long dsum = 0;
+#pragma unroll
+        for (int q = 0; q < kPer; q++) {
+            const int x = tid * kPer + q;
+            if (x < E) {
+                offsets[x] = run;
+                dsum += counts[x] - kept[q];
+            }
+            run += kept[q];
+            if (tile_prefix) tsum += (kept[q] + tile_bm - 1) / tile_bm;
+        }
+        if (tid == 0) offsets[E] = ktot;
+        if (tile_prefix) {
+            int ttot;
+            int tex = block_exclusive_scan_1024(tsum, red, ttot);
+#pragma unroll
+            for (int q = 0; q < kPer; q++) {
+                const int x = tid * kPer + q;
+                if (x < E) tile_prefix[x] = tex;
+                tex += (kept[q] + tile_bm - 1) / tile_bm;
+            }
+            if (tid == 0) tile_prefix[E] = ttot;
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) dsum += __shfl_xor(dsum, off, 64);
+        if ((tid & 63) == 0) dred[tid >> 6] = dsum;
+        __syncthreads();
+        if (tid == 0) *n_dropped = dred[0] + dred[1] + dred[2] + dred[3];
+    }
+    __syncthreads();
+    return ktot;
 }
 
 // One thread per index i < max(n, R_phys): places assignment i (if i < n) and
 // marks row i empty if it lies past the last kept row (if i < R_phys).
 __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t n, int64_t seg_n,
-                                                    int E, int64_t capacity,
+                                                    int E, int64_t capacity, const int32_t* counts,
                                                     const int32_t* local_rank,
-                                                    const int32_t* seg_base, const int32_t* offsets,
-                                                    int64_t R_phys, int32_t* slot_row,
+                                                    const int32_t* seg_base, int32_t* offsets,
+                                                    int64_t* n_dropped, int32_t* tile_prefix,
+                                                    int tile_bm, int64_t R_phys, int32_t* slot_row,
                                                     int32_t* row_src) {
+    __shared__ int32_t offs[kMaxE + 1];
+    __shared__ int red[16];
+    const int kept_total = expert_offsets(counts, E, capacity, offs, red, offsets, n_dropped,
+                                          tile_prefix, tile_bm);
     const int64_t a = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (a < R_phys && a >= offsets[E]) row_src[a] = -1;
+    if (a < R_phys && a >= kept_total) row_src[a] = -1;
     if (a >= n) return;
     const int lr = local_rank[a];
     if (lr < 0) {
@@ -173,68 +215,59 @@ __global__ __launch_bounds__(256) void place_kernel(const int32_t* ids, int64_t 
         slot_row[a] = -1;
         return;
     }
-    const int row = offsets[e] + rank;
+    const int row = offs[e] + rank;
     slot_row[a] = row;
     row_src[row] = (int32_t)a;
 }
 
-// Row copy when each source row feeds one assignment (src_div == 1): one wave
-// per kept destination row.  Each pass issues the loads of 8 16-byte chunks per
-// lane before any store, so a wave keeps 8 KB in flight; lanes past the row's
-// end re-read its last chunk and store nothing.  Every row is read once and
-// written once, so loads and stores are both non-temporal.
-constexpr int kCopyChunks = 8;
+constexpr int kCopyChunks = 8;   // 16-byte loads in flight per lane (E4M3 copies)
 
-__global__ __launch_bounds__(256) void copy_kernel(const int32_t* offsets, int E, int64_t R_phys,
-                                                   const int32_t* row_src, const char* src,
-                                                   char* dst, int64_t row_bytes) {
+// Placement fused with the row copy: one wave per source row s, whose
+// assignments are a = s * src_div + j (j < src_div).  Lane j places assignment
+// a as place_kernel does (slot_row, row_src); the wave then reads the row once
+// (C 16-byte chunks per lane per pass, sized to the row width so that no lane
+// re-reads a chunk) and stores it to the row of each kept assignment.  A source
+// row none of whose assignments was kept is not read.  The rows of row_src past
+// the kept total are cleared by all waves in a grid-stride pass.  Loads and
+// stores are non-temporal: every byte is read once and written once.
+template <int C>
+__global__ __launch_bounds__(256) void place_copy_kernel(
+    const int32_t* ids, int64_t n, int64_t seg_n, int E, int64_t capacity, const int32_t* counts,
+    const int32_t* local_rank, const int32_t* seg_base, int32_t* offsets, int64_t* n_dropped,
+    int32_t* tile_prefix, int tile_bm, int64_t R_phys, int32_t* slot_row, int32_t* row_src,
+    int64_t n_src, const char* src, char* dst, int64_t row_bytes, int src_div) {
+    __shared__ int32_t offs[kMaxE + 1];
+    __shared__ int red[16];
+    const int64_t kept_total = expert_offsets(counts, E, capacity, offs, red, offsets, n_dropped,
+                                              tile_prefix, tile_bm);
     const int lane = threadIdx.x & 63;
-    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (r >= R_phys || r >= offsets[E]) return;
-    const char* s = src + (int64_t)row_src[r] * row_bytes;
-    char* d = dst + r * row_bytes;
-    const int64_t nchunk = row_bytes / 16;
-    for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * kCopyChunks) {
-        u32x4 v[kCopyChunks];
-#pragma unroll
-        for (int q = 0; q < kCopyChunks; q++) {
-            const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
-            v[q] = __builtin_nontemporal_load((const u32x4*)(s + c * 16));
-        }
-#pragma unroll
-        for (int q = 0; q < kCopyChunks; q++) {
-            const int64_t c = c0 + lane + 64 * q;
-            if (c < nchunk) __builtin_nontemporal_store(v[q], (u32x4*)(d + c * 16));
-        }
-    }
-}
-
-// One wave per source row, for source rows shared by several assignments
-// (src_div > 1): the row is loaded once and stored to the destination row of
-// each of its kept assignments, so each source byte crosses HBM once rather
-// than once per assignment.  Lane j of a block of 64 assignments holds the
-// row of assignment a0 + jb + j; a source row none of whose assignments was
-// kept is not read.  Each kept row has exactly one assignment, so this writes
-// the same rows as the gather above.
-__global__ __launch_bounds__(256) void scatter_copy_kernel(const int32_t* slot_row, int64_t n,
-                                                           int64_t n_src, const char* src,
-                                                           char* dst, int64_t row_bytes,
-                                                           int src_div) {
-    const int lane = threadIdx.x & 63;
-    const int64_t s = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (s >= n_src) return;
-    const int64_t a0 = s * src_div;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    for (int64_t r = kept_total + wave * 64 + lane; r < R_phys; r += nwaves * 64) row_src[r] = -1;
+    if (wave >= n_src) return;
+    const int64_t a0 = wave * src_div;
     const int64_t na = min((int64_t)src_div, n - a0);
-    const char* sp = src + s * row_bytes;
+    const char* sp = src + wave * row_bytes;
     const int64_t nchunk = row_bytes / 16;
     for (int64_t jb = 0; jb < na; jb += 64) {
-        const int32_t my = jb + lane < na ? slot_row[a0 + jb + lane] : -1;
+        int32_t my = -1;
+        if (jb + lane < na) {
+            const int64_t a = a0 + jb + lane;
+            const int lr = local_rank[a];
+            if (lr >= 0) {
+                const int e = ids[a];
+                const int rank = seg_base[(a / seg_n) * E + e] + lr;
+                if (capacity < 0 || rank < capacity) my = offs[e] + rank;
+            }
+            slot_row[a] = my;
+            if (my >= 0) row_src[my] = (int32_t)a;
+        }
         const uint64_t kept = __ballot(my >= 0);
         if (!kept) continue;
-        for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * kCopyChunks) {
-            u32x4 v[kCopyChunks];
+        for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * C) {
+            u32x4 v[C];
 #pragma unroll
-            for (int q = 0; q < kCopyChunks; q++) {
+            for (int q = 0; q < C; q++) {
                 const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
                 v[q] = __builtin_nontemporal_load((const u32x4*)(sp + c * 16));
             }
@@ -243,7 +276,7 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(const int32_t* slot_r
                 const int64_t r = __builtin_amdgcn_readlane(my, j);
                 char* d = dst + r * row_bytes;
 #pragma unroll
-                for (int q = 0; q < kCopyChunks; q++) {
+                for (int q = 0; q < C; q++) {
                     const int64_t c = c0 + lane + 64 * q;
                     if (c < nchunk) __builtin_nontemporal_store(v[q], (u32x4*)(d + c * 16));
                 }
@@ -252,10 +285,60 @@ __global__ __launch_bounds__(256) void scatter_copy_kernel(const int32_t* slot_r
     }
 }
 
-// The same two copies writing E4M3 codes of the rows divided by the scale (the
-// fp8 permutation leg: the rows leave the grouping step already quantised, as
-// moe_quantize_e4m3 would quantise them).  A lane converts 16 elements (32 or 64
-// bytes read, 16 bytes written) and keeps kCopyChunks 16-byte loads in flight.
+// Row copy when each source row feeds one assignment (src_div == 1), after the
+// placement: one wave per kept destination row, in row order, gathers its source
+// row through row_src, so the stores run through the destination in sequence.
+// C 16-byte chunks per lane per pass; loads and stores are non-temporal.
+template <int C>
+__global__ __launch_bounds__(256) void gather_copy_kernel(const int32_t* offsets, int E,
+                                                          int64_t R_phys, const int32_t* row_src,
+                                                          const char* src, char* dst,
+                                                          int64_t row_bytes) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= R_phys || r >= offsets[E]) return;
+    const char* sp = src + (int64_t)row_src[r] * row_bytes;
+    char* d = dst + r * row_bytes;
+    const int64_t nchunk = row_bytes / 16;
+    for (int64_t c0 = 0; c0 < nchunk; c0 += 64 * C) {
+        u32x4 v[C];
+#pragma unroll
+        for (int q = 0; q < C; q++) {
+            const int64_t c = min(c0 + lane + 64 * q, nchunk - 1);
+            v[q] = __builtin_nontemporal_load((const u32x4*)(sp + c * 16));
+        }
+#pragma unroll
+        for (int q = 0; q < C; q++) {
+            const int64_t c = c0 + lane + 64 * q;
+            if (c < nchunk) __builtin_nontemporal_store(v[q], (u32x4*)(d + c * 16));
+        }
+    }
+}
+
+// 16-byte chunks per lane per pass for rows of nchunk chunks: the choice among
+// 4, 6 and 8 that leaves the fewest idle lane slots (the larger on a tie).
+int copy_chunks_for(int64_t nchunk) {
+    int best = 8;
+    int64_t waste = -1;
+    for (int c : {8, 6, 4}) {
+        const int64_t per = 64 * (int64_t)c;
+        const int64_t w = (nchunk + per - 1) / per * per - nchunk;
+        if (waste < 0 || w < waste) {
+            waste = w;
+            best = c;
+        }
+    }
+    return best;
+}
+
+// The row copies writing E4M3 codes of the rows divided by the scale (the fp8
+// permutation leg: the rows leave the grouping step already quantised, as
+// moe_quantize_e4m3 would quantise them), after the placement kernel: with one
+// source row per assignment (src_div == 1) one wave per kept destination row
+// gathers its source row through row_src; otherwise one wave per source row
+// stores it to each kept assignment's row, found in slot_row.  A lane converts
+// 16 elements (32 or 64 bytes read, 16 bytes written) and keeps kCopyChunks
+// 16-byte loads in flight.
 // amax: max |x| over the source rows read, i.e. those with a kept assignment.
 // Waves stride over the rows on a grid of at most kE4m3Blocks blocks, so the
 // amax takes one atomic per block, not per four rows.
@@ -409,13 +492,44 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
     // with no segments this writes zero counts
     hipLaunchKernelGGL(colscan_kernel, dim3((unsigned)E), dim3(256), 0, s, nseg, E, seg_count,
                        counts);
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, E, capacity, counts, offsets,
-                       n_dropped, tile_prefix, tile_bm);
-    const int64_t m = n > R_phys ? n : R_phys;
-    if (m > 0) {
-        hipLaunchKernelGGL(place_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, ids,
-                           n, seg_n, E, capacity, local_rank, seg_count, offsets, R_phys, slot_row,
-                           row_src);
+    // the placement always runs, at least one workgroup: workgroup 0 writes the
+    // offsets, the drop count and the tile prefix
+    const int64_t row_bytes = width * elem_bytes;
+    if (src && R_phys > 0 && !out_e4m3 && src_div > 1) {
+        // placement and the row copy in one kernel, one wave per source row
+        const int64_t n_src = (n + src_div - 1) / src_div;
+        const int64_t waves = std::max<int64_t>(n_src, (R_phys + 63) / 64);
+        const dim3 g((unsigned)std::max<int64_t>(1, (waves + 3) / 4));
+#define MOE_PLACE_COPY(C)                                                                       \
+    hipLaunchKernelGGL(place_copy_kernel<C>, g, dim3(256), 0, s, ids, n, seg_n, E, capacity,    \
+                       counts, local_rank, seg_count, offsets, n_dropped, tile_prefix, tile_bm, \
+                       R_phys, slot_row, row_src, n_src, (const char*)src, (char*)dst,          \
+                       row_bytes, src_div)
+        switch (copy_chunks_for(row_bytes / 16)) {
+            case 4: MOE_PLACE_COPY(4); break;
+            case 6: MOE_PLACE_COPY(6); break;
+            default: MOE_PLACE_COPY(8);
+        }
+#undef MOE_PLACE_COPY
+        return hipGetLastError();
+    }
+    const int64_t m = std::max<int64_t>(1, n > R_phys ? n : R_phys);
+    hipLaunchKernelGGL(place_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, ids, n,
+                       seg_n, E, capacity, counts, local_rank, seg_count, offsets, n_dropped,
+                       tile_prefix, tile_bm, R_phys, slot_row, row_src);
+    if (src && R_phys > 0 && !out_e4m3) {
+        // one source row per assignment: gather in destination order
+        const dim3 g((unsigned)((R_phys + 3) / 4));
+#define MOE_GATHER_COPY(C)                                                                       \
+    hipLaunchKernelGGL(gather_copy_kernel<C>, g, dim3(256), 0, s, offsets, E, R_phys, row_src,   \
+                       (const char*)src, (char*)dst, row_bytes)
+        switch (copy_chunks_for(row_bytes / 16)) {
+            case 4: MOE_GATHER_COPY(4); break;
+            case 6: MOE_GATHER_COPY(6); break;
+            default: MOE_GATHER_COPY(8);
+        }
+#undef MOE_GATHER_COPY
+        return hipGetLastError();
     }
     if (out_e4m3) {
         // dst holds E4M3 codes of width bytes a row; elem_bytes is the source's
@@ -449,18 +563,6 @@ hipError_t launch_permute(const int32_t* ids, int64_t n, int E, int64_t capacity
                                    scale, ab);
         }
         return hipGetLastError();
-    }
-    if (src && R_phys > 0) {
-        if (src_div == 1) {
-            hipLaunchKernelGGL(copy_kernel, dim3((unsigned)((R_phys + 3) / 4)), dim3(256),
-                               0, s, offsets, E, R_phys, row_src, (const char*)src, (char*)dst,
-                               width * elem_bytes);
-        } else if (n > 0) {
-            const int64_t n_src = (n + src_div - 1) / src_div;
-            hipLaunchKernelGGL(scatter_copy_kernel, dim3((unsigned)((n_src + 3) / 4)), dim3(256),
-                               0, s, slot_row, n, n_src, (const char*)src, (char*)dst,
-                               width * elem_bytes, src_div);
-        }
     }
     return hipGetLastError();
 }
