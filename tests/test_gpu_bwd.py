@@ -85,6 +85,10 @@ DRHS_CASES = [  # dt, out, E, N, K, kind, scale
     ("f32", "f32", 8, 96, 64, "tails", 0),
     ("f32", "f32", 3, 32, 160, "uniform", 90),
     ("bf16", "f32", 2, 256, 256, "uniform", 1500),  # long reductions (about 24 steps)
+    # groups of 8 to 15 tiles (the XCD ranges split groups between XCDs)
+    ("bf16", "f32", 5, 640, 1088, "tails", 0),     # 15 tiles a group, partial row and column
+    ("bf16", "bf16", 3, 512, 1024, "skewed", 150),  # 8 tiles a group
+    ("f32", "f32", 4, 768, 768, "uniform", 100),   # 9 tiles a group
 ]
 
 
@@ -116,6 +120,7 @@ FFN_BWD_CASES = [  # dt, dw, E, d, H, kind, scale
     ("f32", "f32", 3, 64, 96, "uniform", 100),
     ("f32", "f32", 5, 32, 64, "sparse", 0),
     ("bf16", "f32", 2, 128, 128, "uniform", 700),
+    ("bf16", "f32", 3, 512, 512, "uniform", 300),  # dW_gu of 8 tiles a group
 ]
 
 
