@@ -67,8 +67,8 @@ def parse():
                          "workload; default workload: the 535B expert shape")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed steps, run one 1 GiB device copy (a kernel of known "
-                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and report "
-                         "its bandwidth")
+                         "traffic, to scale the FETCH_SIZE / WRITE_SIZE counters) and a 1 GiB "
+                         "fill, and report their bandwidths")
     return ap.parse_args()
 
 
@@ -1107,6 +1107,11 @@ def main():
         cms = time_ms(lambda: dst.copy_(src), reps=1)
         line["copy_1GiB"] = {"ms": round(cms, 4),
                              "GB_per_s": round(2 * (1 << 30) / (cms * 1e-3) / 1e9, 1)}
+        # the write ceiling that a write-dominated kernel (a row copy fanning each
+        # source row out to k destinations) is held to
+        fms = time_ms(lambda: dst.fill_(1), reps=3)
+        line["fill_1GiB"] = {"ms": round(fms, 4),
+                             "GB_per_s": round((1 << 30) / (fms * 1e-3) / 1e9, 1)}
         del src, dst
     if not args.no_cpu_baseline and cfg is not None:
         if isinstance(cfg, PoolConfig):
