@@ -175,12 +175,27 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Wave-uniform reads of the launch's read-only tables (group offsets, tile
+// prefix, XCD ranges: written by kernels before this one on the stream, never
+// during it), through the constant address space, so they are scalar loads.
+// A vector load would wait with vmcnt, which on gfx950 also counts stores: the
+// next tile's group lookup after an epilogue would wait for that tile's output
+// stores to be acknowledged, once per step of the binary search.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_p;
+typedef const __attribute__((address_space(4))) int64_t* const_i64_p;
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* t, int64_t i) {
+    return ((const_i32_p)t)[i];
+}
+__device__ __forceinline__ int64_t ld_uniform(const int64_t* t, int64_t i) {
+    return ((const_i64_p)t)[i];
+}
+
 __device__ __forceinline__ int find_group(const int32_t* tp, int G, int m) {
     // largest g in [0, G) with tp[g] <= m  (tp non-decreasing, tp[0] = 0)
     int lo = 0, hi = G;           // invariant: tp[lo] <= m < tp[hi]
     while (hi - lo > 1) {
         int mid = (lo + hi) >> 1;
-        if (tp[mid] <= m) lo = mid; else hi = mid;
+        if (ld_uniform(tp, mid) <= m) lo = mid; else hi = mid;
     }
     return lo;
 }
@@ -247,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
     const int64_t n_tiles_n = (p.N + kColsOut - 1) / kColsOut;
     int64_t n_tiles_m;
     if constexpr (kRK) n_tiles_m = (int64_t)p.G * ((p.M + kBM - 1) / kBM);
-    else n_tiles_m = p.offsets ? (int64_t)p.tile_prefix[p.G] : (p.M + kBM - 1) / kBM;
+    else n_tiles_m = p.offsets ? (int64_t)ld_uniform(p.tile_prefix, p.G) : (p.M + kBM - 1) / kBM;
     const int64_t total = n_tiles_m * n_tiles_n;
     const int xcd = blockIdx.x % kNumXcd;
     const int slot = blockIdx.x / kNumXcd;
@@ -258,8 +273,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         // reduction over each group's rows: the XCD ranges come balanced by cost
         // (launch_dw_split); without them, equal tile counts
         if (p.xcd_split) {
-            lo = uniform64(p.xcd_split[xcd]);
-            hi = uniform64(p.xcd_split[xcd + 1]);
+            lo = uniform64(ld_uniform(p.xcd_split, xcd));
+            hi = uniform64(ld_uniform(p.xcd_split, xcd + 1));
         }
     }
     // SPLIT (dense GEMMs whose last round of tiles is at most half full): each
@@ -339,13 +354,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
             tl.mc0 = (tm - (int64_t)tl.g * ntm) * kBM;
             tl.row0 = (int64_t)tl.g * p.M + tl.mc0;
             tl.rows_valid = min((int64_t)kBM, p.M - tl.mc0);
-            tl.kbeg = p.offsets[tl.g];
-            tl.klen = p.offsets[tl.g + 1] - p.offsets[tl.g];
+            tl.kbeg = ld_uniform(p.offsets, tl.g);
+            tl.klen = ld_uniform(p.offsets, tl.g + 1) - (int)tl.kbeg;
         } else if (p.offsets) {
             tl.g = find_group(p.tile_prefix, p.G, (int)tm);
-            const int64_t mloc = tm - p.tile_prefix[tl.g];
-            tl.row0 = p.offsets[tl.g] + mloc * kBM;
-            tl.rows_valid = min((int64_t)kBM, (int64_t)p.offsets[tl.g + 1] - tl.row0);
+            const int64_t mloc = tm - ld_uniform(p.tile_prefix, tl.g);
+            tl.row0 = ld_uniform(p.offsets, tl.g) + mloc * kBM;
+            tl.rows_valid = min((int64_t)kBM, (int64_t)ld_uniform(p.offsets, tl.g + 1) - tl.row0);
         } else {
             tl.row0 = tm * kBM;
             tl.rows_valid = min((int64_t)kBM, p.M - tl.row0);
