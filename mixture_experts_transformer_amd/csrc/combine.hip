@@ -123,9 +123,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const char* Y, const int32
     }
 }
 
-// Chunks per lane for a row of nchunk 16-byte chunks: among the candidates, the
-// one that leaves the fewest idle lane slots over the row's segments (the larger
-// on a tie).
+// Chunks per lane for a row of nchunk 16-byte chunks: among the candidates (in
+// decreasing order), the one that leaves the fewest idle lane slots over the
+// row's segments (the larger on a tie).
 template <int N>
 int chunks_for(int64_t nchunk, const int (&cand)[N]) {
     int best = cand[0];
@@ -164,17 +164,12 @@ void launch_t(const void* Y, const int32_t* slot_row, const float* w, int64_t T_
             default: launch_jc<T, 1, 8>(Y, slot_row, w, T_, k, row_bytes, out, flags, s);
         }
     } else {
-        static const int cand[] = {3, 2, 4};
-        switch (chunks_for(nchunk, cand)) {
-            case 2:
-                launch_jc<T, kRowsInFlight, 2>(Y, slot_row, w, T_, k, row_bytes, out, flags, s);
-                break;
-            case 4:
-                launch_jc<T, kRowsInFlight, 4>(Y, slot_row, w, T_, k, row_bytes, out, flags, s);
-                break;
-            default:
-                launch_jc<T, kRowsInFlight, 3>(Y, slot_row, w, T_, k, row_bytes, out, flags, s);
-        }
+        // 2 or 3 chunks (4 would never leave fewer idle lanes than 2)
+        static const int cand[] = {3, 2};
+        if (chunks_for(nchunk, cand) == 2)
+            launch_jc<T, kRowsInFlight, 2>(Y, slot_row, w, T_, k, row_bytes, out, flags, s);
+        else
+            launch_jc<T, kRowsInFlight, 3>(Y, slot_row, w, T_, k, row_bytes, out, flags, s);
     }
 }
 

@@ -179,6 +179,8 @@ def test_permute_bit_exact(M, case):
     ("bf16", 256, 3, 6000, 16, 200, 0.1),      # capacity drops and padding ids
     ("f32", 64, 70, 7000, 5, -1, 0.3),         # more than 64 assignments per source row
     ("bf16", 128, 4, 4096, 8, 0, 0.0),         # capacity 0: nothing kept, nothing copied
+    ("bf16", 4096, 8, 2000, 24, -1, 0.0),      # 8 KB rows: 8 chunks per lane, shared rows
+    ("bf16", 4096, 1, 3000, 24, 100, 0.1),     # 8 KB rows, one source row per assignment
 ])
 def test_permute_row_copy(M, dt, width, div, n, E, cap, pad):
     rng = np.random.default_rng(width + n)
@@ -256,8 +258,15 @@ def test_grouped_ffn_parity(M, dt, E, d, H, kind, scale):
 
 # --------------------------------------------------------------- combine ----
 
-@pytest.mark.parametrize("dt,T,k,width", [("bf16", 8192, 8, 3072), ("f32", 256, 2, 128),
-                                          ("bf16", 1000, 4, 2048)])
+@pytest.mark.parametrize("dt,T,k,width", [
+    ("bf16", 8192, 8, 3072),     # two row segments of 3 chunks per lane
+    ("f32", 256, 2, 128),        # one segment of 2 chunks, most lanes idle
+    ("bf16", 1000, 4, 2048),     # two segments of 2 chunks
+    ("bf16", 700, 3, 1536),      # one segment of 3 chunks
+    ("bf16", 3000, 1, 4096),     # k = 1: one segment of 8 chunks
+    ("bf16", 2000, 1, 3072),     # k = 1: one segment of 6 chunks
+    ("f32", 500, 1, 96),         # k = 1: 4 chunks, most lanes idle
+])
 def test_combine_parity(M, dt, T, k, width):
     rng = np.random.default_rng(T + k)
     slot = rng.permutation(T * k).astype(np.int32)
