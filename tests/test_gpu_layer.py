@@ -159,7 +159,7 @@ def check_layer_protocol(cfg, inp, y, aux, st, capacity=-1, n_sample=N_SAMPLE):
     keep = (sr >= 0).astype(np.int32) if capacity >= 0 else None
     y_ref = O.output_tokens(TB.dims(cfg), W, x_host, tok, ids[tok], ref_w[tok], keep=keep)
     stats = assert_close(y[tsel].float().cpu().numpy(), y_ref, cfg.dtype,
-                         f"{name} y ({tok.size} tokens)")
+                         f"{name} y ({tok.size} tokens)", strict=True)
     print(f"{name}: y max|err| = {stats['err_rms']:.2e} x RMS, max|y|/RMS = "
           f"{stats['max_ref_rms']:.1f}")
     return ref
@@ -278,4 +278,4 @@ def test_ep_share_pool_path(M):
     what = f"pool ({sample.size} rows: hottest expert {hot}, coldest {cold}, 4,096 sampled)"
     assert_close(h_ws[psel].float().cpu().numpy(), href, "bf16", f"{what} h")
     assert_close(Y_perm[psel].float().cpu().numpy(), Yref, "bf16", f"{what} Y")
-    assert_close(got[sample], Yref, "bf16", f"{what} unpermuted")
+    assert_close(got[sample], Yref, "bf16", f"{what} unpermuted", strict=True)
