@@ -348,7 +348,8 @@ def bench_layer(args, cfg, M, dev):
     aux = dict(ids=torch.empty((cfg.T, cfg.k), **i32),
                w=torch.empty((cfg.T, cfg.k), dtype=torch.float32, device=dev),
                counts=torch.empty(cfg.E, **i32),
-               n_dropped=torch.empty(1, dtype=torch.int64, device=dev))
+               n_dropped=torch.empty(1, dtype=torch.int64, device=dev),
+               slot_row=torch.empty(cfg.T * cfg.k, **i32))
     wall, per_stage, per_step = time_layer(M, desc, inp, xs, ys, aux, ws, args.warmup,
                                            args.steps)
     stage_ms = {n: float(np.mean(v)) for n, v in per_stage.items()}
@@ -413,7 +414,15 @@ def bench_layer(args, cfg, M, dev):
     }
     # ordered combine: every kept Y row read once, slot_row and weights, c written once
     comb_bytes = kept * de * es + T * k * 8 + T * de * es
-    hbm = {"combine": hbm_entry(comb_bytes, stage_ms["combine"])}
+    # The combine timed alone, back to back on the layer's own expert rows (Y, read
+    # from the workspace) and routing: its kernel time.  The in-layer figure also
+    # holds the gap between the stage events and the kernel.
+    lay = M.moe_layer_workspace_layout(desc)
+    y_rows = ws[lay["Y"]:lay["Y"] + T * k * de * es].view(inp["x"].dtype).view(T * k, de)
+    c_out = torch.empty((T, de), dtype=inp["x"].dtype, device=dev)
+    cms = time_ms(lambda: M.moe_combine(y_rows, aux["slot_row"], aux["w"], T, k, out=c_out))
+    hbm = {"combine": hbm_entry(comb_bytes, cms),
+           "combine_in_layer": hbm_entry(comb_bytes, stage_ms["combine"])}
     if not args.no_kernel_extras:
         # The layer's grouping copies no rows (the expert GEMM gathers them); the
         # stand-alone moe_permute with the row copy is timed here at the same shape.
