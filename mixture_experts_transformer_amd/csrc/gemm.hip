@@ -901,15 +901,41 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         constexpr int kVec = 16 / sizeof(typename Elem<OutT>::store_t);
         // write back a staged float32 block (32 rows of 32 columns starting at
         // tile row rbase, column cbase), with the epilogue's per-element work
+        // A block's global addresses are a wave-uniform base (its first row and
+        // column) plus a 32-bit lane offset: row r < 32 of rows ld elements apart
+        // (every leading dimension here is far below 2^26).  The lane offsets are
+        // formed from a copy of the lane index that an empty asm "redefines" inside
+        // the helper, so they are recomputed at each block instead of being hoisted
+        // out of the tile loop: hoisted (and, before, kept as 64-bit row and column
+        // numbers) they were spilled and reloaded on every tile, and a reload after
+        // the epilogue's stores waits for them to drain.
+        auto blk_base = [&](const void* base, int64_t ld, int rbase, int64_t cbase)
+            __attribute__((always_inline)) {
+            return (const char*)uniform64(
+                (int64_t)((const char*)base + ((done.row0 + rbase) * ld + cbase) * (int64_t)sizeof(OutT)));
+        };
+        // rows and columns of a block (32 rows at rbase, W columns at cbase) inside
+        // the tile's valid rows and the output's columns
+        auto blk_rows = [&](int rbase) __attribute__((always_inline)) {
+            return (int)max((int64_t)0, min((int64_t)32, done.rows_valid - rbase));
+        };
+        auto blk_cols = [&](int64_t cbase, int W) __attribute__((always_inline)) {
+            return (int)max((int64_t)0, min((int64_t)W, p.N - cbase));
+        };
+        // write back a staged float32 block (32 rows of 32 columns starting at
+        // tile row rbase, column cbase), with the epilogue's per-element work
         auto store_f32_block = [&](int rbase, int64_t cbase) __attribute__((always_inline)) {
             constexpr int kChunks = 32 / kVec;
+            const int rv = blk_rows(rbase), cv = blk_cols(cbase, 32);
+            const int ldc = (int)p.ldc;
+            OutT* const Cb = (OutT*)blk_base(p.C, p.ldc, rbase, cbase);
+            int lane_v = lane;
+            asm volatile("" : "+v"(lane_v));
 #pragma unroll
-            for (int q = lane; q < 32 * kChunks; q += 64) {
+            for (int q = lane_v; q < 32 * kChunks; q += 64) {
                 const int r = q / kChunks;
                 const int cc = (q % kChunks) * kVec;
-                const int64_t grow = rbase + r;
-                const int64_t col = cbase + cc;
-                if (grow < done.rows_valid && col < p.N) {
+                if (r < rv && cc < cv) {
                     float vals[kVec];
 #pragma unroll
                     for (int e = 0; e < kVec; e += 4) {
@@ -920,17 +946,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                         vals[e + 3] = x.w;
                     }
                     if (EPI == EPI_ADD) {
-                        const int64_t aoff = (done.row0 + grow) * p.ld_add + col;
+                        const OutT* const Ab = (const OutT*)blk_base(p.addend, p.ld_add, rbase, cbase);
+                        const int aoff = r * (int)p.ld_add + cc;
 #pragma unroll
-                        for (int e = 0; e < kVec; e++)
-                            vals[e] += Elem<OutT>::load((const OutT*)p.addend, aoff + e);
+                        for (int e = 0; e < kVec; e++) vals[e] += Elem<OutT>::load(Ab, aoff + e);
                     }
                     if constexpr (EPI == EPI_SWIGLU_BWD) {
                         // vals = dh.  With the forward's pre-activations g, u
                         // (float32): dG = dh u silu'(g), dU = dh silu(g), and
                         // h = silu(g) u, silu'(g) = s (1 + g (1 - s)), s = 1 / (1 + exp(-g))
-                        const int64_t row = done.row0 + grow;
-                        const float* gu = (const float*)p.addend + row * p.ld_add + col;
+                        const float* const gb = (const float*)uniform64((int64_t)(
+                            (const float*)p.addend + (done.row0 + rbase) * p.ld_add + cbase));
+                        const float* gu = gb + r * (int)p.ld_add + cc;
                         float dg[kVec], du[kVec], hv[kVec];
 #pragma unroll
                         for (int e = 0; e < kVec; e++) {
@@ -942,16 +969,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                             du[e] = vals[e] * si;
                             hv[e] = si * u;
                         }
-                        store_vec<OutT, kVec>(C, row * p.ldc + col, dg, nt_out);
-                        store_vec<OutT, kVec>(C, row * p.ldc + p.n_per + col, du, nt_out);
-                        store_vec<OutT, kVec>((OutT*)p.C2, row * p.ldc2 + col, hv, nt_out);
+                        const int off = r * ldc + cc;
+                        OutT* const C2b = (OutT*)blk_base(p.C2, p.ldc2, rbase, cbase);
+                        store_vec<OutT, kVec>(Cb, off, dg, nt_out);
+                        store_vec<OutT, kVec>(Cb, off + p.n_per, du, nt_out);
+                        store_vec<OutT, kVec>(C2b, r * (int)p.ldc2 + cc, hv, nt_out);
                     } else {
                         if constexpr (kRK && std::is_same<OutT, float>::value) {
                             const u32x4 x = {__float_as_uint(vals[0]), __float_as_uint(vals[1]),
                                              __float_as_uint(vals[2]), __float_as_uint(vals[3])};
-                            store16_stream(C + (done.row0 + grow) * p.ldc + col, x);
+                            store16_stream(Cb + r * ldc + cc, x);
                         } else {
-                            store_vec<OutT, kVec>(C, (done.row0 + grow) * p.ldc + col, vals, nt_out);
+                            store_vec<OutT, kVec>(Cb, r * ldc + cc, vals, nt_out);
                         }
                     }
                 }
@@ -978,15 +1007,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
         auto store_bf16_block = [&](auto w_c, int rbase, int64_t cbase) __attribute__((always_inline)) {
             constexpr int W = decltype(w_c)::value;
             constexpr int kRow = 2 * W, kMask = W / 8 - 1, kChunks = W / 8;
+            const int rv = blk_rows(rbase), cv = blk_cols(cbase, W);
+            const int ldc = (int)p.ldc;
+            OutT* const Cb = (OutT*)blk_base(p.C, p.ldc, rbase, cbase);
+            int lane_v = lane;
+            asm volatile("" : "+v"(lane_v));
 #pragma unroll
-            for (int q = lane; q < 32 * kChunks; q += 64) {
+            for (int q = lane_v; q < 32 * kChunks; q += 64) {
                 const int r = q / kChunks;
                 const int cc = q % kChunks;
-                const int64_t grow = rbase + r;
-                const int64_t col = cbase + cc * 8;
-                if (grow < done.rows_valid && col < p.N) {
+                if (r < rv && cc * 8 < cv) {
                     const u32x4 x = *(const u32x4*)(piece + r * kRow + ((cc ^ (r & kMask)) << 4));
-                    store16(C + (done.row0 + grow) * p.ldc + col, x, nt_out);
+                    store16(Cb + r * ldc + cc * 8, x, nt_out);
                 }
             }
         };
