@@ -213,11 +213,22 @@ __device__ __forceinline__ int find_group(const int32_t* tp, int G, int m) {
     return lo;
 }
 
-// 16-byte output store; nt: non-temporal (the output is re-read from HBM anyway)
+// 16-byte output store; nt: non-temporal (the output is re-read from HBM anyway).
+// Outputs are global memory: the pointer is cast to the global address space, so
+// the store is a global store even where the address came through an integer
+// (a flat store would also count in lgkmcnt, and every later LDS wait of the
+// epilogue would then wait for it to complete).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 __device__ __forceinline__ void store16(void* dst, u32x4 x, bool nt) {
-    if (nt) __builtin_nontemporal_store(x, (u32x4*)dst);
-    else *(u32x4*)dst = x;
+    g_u32x4* const g = (g_u32x4*)dst;
+    if (nt) __builtin_nontemporal_store(x, g);
+    else *g = x;
+}
+// an element of a global array (the epilogue's addends)
+template <typename E>
+__device__ __forceinline__ E ld_global(const E* p, int i) {
+    return ((const __attribute__((address_space(1))) E*)p)[i];
 }
 // 16-byte store at system scope, non-temporal (sc0 sc1 nt).  The float32 weight
 // gradients (29 GB at the 535B expert shape) are written once and never re-read by
@@ -949,7 +960,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                         const OutT* const Ab = (const OutT*)blk_base(p.addend, p.ld_add, rbase, cbase);
                         const int aoff = r * (int)p.ld_add + cc;
 #pragma unroll
-                        for (int e = 0; e < kVec; e++) vals[e] += Elem<OutT>::load(Ab, aoff + e);
+                        for (int e = 0; e < kVec; e++) {
+                            if constexpr (std::is_same<OutT, float>::value)
+                                vals[e] += ld_global(Ab, aoff + e);
+                            else
+                                vals[e] += bf16_to_f32(ld_global((const u16*)Ab, aoff + e));
+                        }
                     }
                     if constexpr (EPI == EPI_SWIGLU_BWD) {
                         // vals = dh.  With the forward's pre-activations g, u
@@ -961,8 +977,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmParams p) {
                         float dg[kVec], du[kVec], hv[kVec];
 #pragma unroll
                         for (int e = 0; e < kVec; e++) {
-                            const float g = gu[e];
-                            const float u = gu[p.n_per + e];
+                            const float g = ld_global(gu, e);
+                            const float u = ld_global(gu, (int)p.n_per + e);
                             const float sg = 1.0f / (1.0f + expf(-g));
                             const float si = silu_f(g);
                             dg[e] = vals[e] * u * (sg * (1.0f + g * (1.0f - sg)));
