@@ -87,6 +87,9 @@ const char *moe_status_str(moe_status s);
  *   logits_out (device) [T, E] float32, or NULL
  *   topk_ids   (device) [T, k] int32: j-th best expert of token t
  *   topk_w     (device) [T, k] float32 routing weights
+ * With logits_out given and E > 256 the router runs as two kernels (logits for
+ * 64 tokens x half of the experts per workgroup, then top-k per token); topk_w then
+ * carries each token's inverse RMS from the first to the second.
  * Limits: 1 <= E <= 512, 1 <= k <= min(E, 16), d_r a multiple of 16 and at
  * least 32, T >= 0. */
 moe_status moe_route(const void *h, moe_dtype h_dt, int64_t T, int64_t d_r,

@@ -851,7 +851,7 @@ moe_status moe_layer_fwd(const moe_layer_desc* d, const moe_layer_weights* W, co
     const int64_t R = T * k;
     const int64_t de = L > 0 ? L : D;
     const int es = esize(dt);
-    float* logits = (aux && aux->logits) ? aux->logits : nullptr;
+    float* logits = (aux && aux->logits) ? aux->logits : b.logits;
     int32_t* ids = (aux && aux->ids) ? aux->ids : b.ids;
     float* w = (aux && aux->w) ? aux->w : b.w;
     int32_t* counts = (aux && aux->counts) ? aux->counts : b.counts;

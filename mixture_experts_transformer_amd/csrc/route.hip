@@ -1,5 +1,6 @@
 // Router: RMSNorm scale, float32 logits on the matrix cores, top-k and routing
-// weights, in one kernel.
+// weights, in one kernel (route_kernel), or in two for wide routers (the
+// expert-split form further down).
 //
 // Each workgroup owns 32 tokens and every expert.  With r = h * inv_rms * g the
 // logits are l = inv_rms * ((h * g) W_r^T) + b, so the row scale is applied once
@@ -105,6 +106,48 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
         x = y > x ? y : x;
     }
     return x;
+}
+
+// Top-k of one token's E logits by one wave, and its routing weights
+// exp(l_j - l_max) / sum over the selected exp(l_i - l_max), which equal softmax
+// over all experts renormalised over the selected ones.  Each lane holds experts
+// lane, lane + 64, ... as packed (value, id) keys: a wavefront argmax per pick,
+// taken keys cleared.  logit(e) returns expert e's logit.
+template <int kPer, typename Get>
+__device__ __forceinline__ void select_topk(int lane, int E, int k, Get logit, int32_t* ids,
+                                            float* w) {
+    uint64_t key[kPer];
+#pragma unroll
+    for (int qq = 0; qq < kPer; qq++) {
+        const int e = lane + 64 * qq;
+        key[qq] = (e < E) ? (((uint64_t)order_key(logit(e)) << 32) |
+                             (uint64_t)(0xFFFFFFFFu - (uint32_t)e))
+                          : 0ull;
+    }
+    float lmax = 0.0f, sum = 0.0f, my_val = 0.0f;
+    int my_id = 0;
+    for (int j = 0; j < k; j++) {
+        uint64_t best = 0ull;
+#pragma unroll
+        for (int qq = 0; qq < kPer; qq++) best = key[qq] > best ? key[qq] : best;
+        best = wave_max_u64(best);
+        const int sel_e = (int)(0xFFFFFFFFu - (uint32_t)best);
+        const float sel_l = logit(sel_e);
+#pragma unroll
+        for (int qq = 0; qq < kPer; qq++)
+            if (lane + 64 * qq == sel_e) key[qq] = 0ull;
+        if (j == 0) lmax = sel_l;
+        const float ex = expf(sel_l - lmax);
+        sum += ex;
+        if (lane == j) {
+            my_val = ex;
+            my_id = sel_e;
+        }
+    }
+    if (lane < k) {
+        ids[lane] = my_id;
+        w[lane] = my_val / sum;
+    }
 }
 
 struct RouteParams {
@@ -353,6 +396,10 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
         // the next stage's gains, once this stage's MFMAs are issued
         load_g(min(kt + 1, nk - 1));
     }
+    // The last stage's re-read may still be landing in a ring slot the logits
+    // tile below overlaps; the compiler does not see the DMAs, so the wait is
+    // explicit.
+    wait_vmcnt<0>();
     __syncthreads();
 
     // ---- 3. logits tile in LDS (first K half, then the second added in a
@@ -387,42 +434,318 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
             rp.logits[(t0 + tt) * E + e] = lt[tt * ldl + e];
         }
     }
-    for (int tt = wave; tt < ntok; tt += kWaves) {
-        // each lane holds experts lane, lane + 64, ... ; taken ones are cleared
-        constexpr int kPer = kEPad / 64;
-        uint64_t key[kPer];
+    for (int tt = wave; tt < ntok; tt += kWaves)
+        select_topk<kEPad / 64>(
+            lane, E, k, [&](int e) { return lt[tt * ldl + e]; }, rp.ids + (t0 + tt) * k,
+            rp.w + (t0 + tt) * k);
+}
+
+// ---- Expert-split form, for wide routers (E > 256) whose float32 W_r does not
+// fit one XCD's L2 (384 x 3,072 x 4 bytes = 4.7 MB against 4 MB).  Each CU
+// streams its operands through its own LDS ring at a bounded rate, so the time
+// is set by the bytes each workgroup loads: a workgroup owning 32 tokens and
+// every expert loads all of W_r for 32 tokens' worth of MFMAs.  Here a
+// workgroup owns 64 tokens and one half of the experts (the same MFMAs per
+// byte of W_r twice over), and the halves are dealt by XCD: workgroup b runs on
+// XCD b % 8, and XCDs 0-3 take the first half, 4-7 the second, so each XCD's
+// L2 serves one 2.4 MB half to its 32 CUs.  Two kernels:
+//   route_logits_kernel: the logits of its 64 tokens x E/2 experts, as in
+//     route_kernel (float32 MFMAs on g-scaled h, K halves summed in a fixed
+//     order, then scaled by the inverse RMS, plus bias), written to the logits
+//     output.  The inverse RMS is summed from the h values the K loop already
+//     reads (no separate pass over the rows); the first half's workgroups leave
+//     it in topk_w[t * k] for the second kernel;
+//   route_select_kernel: one wave per token: the normalised row r (when asked),
+//     then top-k and the weights from the logits.
+constexpr int kTokS = 64;   // tokens per workgroup in the expert-split form
+
+// CB: 32-expert MFMA column blocks per wave; a half holds up to 64 CB experts
+template <typename Tin, int CB>
+__global__ __launch_bounds__(kThreads, 1) void route_logits_kernel(RouteParams rp, int EH) {
+    constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
+    constexpr int kARow = kKS * kInB;                 // bytes of an h row per stage
+    constexpr int kAChunks = kARow / 16;
+    constexpr int kASlices = kTokS * kARow / 1024;    // 1-KB h slices per stage (8 or 4)
+    constexpr int kEP = 64 * CB;                      // experts of a half, padded
+    constexpr int kStageBytes = kTokS * kARow + kEP * 128;
+    constexpr int kStages = kStageBytes <= 32768 ? 4 : 3;
+    constexpr int kDma = CB + 1;                      // DMAs per wave per stage
+    static_assert(kASlices <= kWaves, "one h slice per wave at most");
+
+    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ float inv_rms[kTokS];
+    __shared__ float ss_half[2][kTokS];
+    char* const dummy = lds + kStages * kStageBytes;  // sink of the padding DMAs
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int kh = wave >> 2;                         // which half of each stage's MFMA steps
+    const int wr = (wave >> 1) & 1;                   // which 32 of the 64 rows
+    const int wc = wave & 1;                          // which CB column blocks of the half
+    const int xcd = blockIdx.x & 7;
+    const int hf = xcd >> 2;                          // expert half
+    const int64_t t0 = ((int64_t)(xcd & 3) + 4 * (int64_t)(blockIdx.x >> 3)) * kTokS;
+    if (t0 >= rp.T) return;
+    const int ntok = (int)min((int64_t)kTokS, rp.T - t0);
+    const int e0 = hf * EH;                           // first expert of the half
+    const int ne = min(EH, rp.E - e0);                // experts of the half
+    const int d = rp.d;
+    const int nk = (d + kKS - 1) / kKS;
+    const bool tail16 = (d % kKS) != 0;
+
+    // DMA sources: wave-uniform bases advanced per stage plus fixed 32-bit lane
+    // offsets, as in route_kernel (the tail stage is moved back by 16 values)
+    const char* const a_base = (const char*)rp.h + t0 * (int64_t)d * kInB;
+    const char* const b_base = (const char*)rp.W_r + (int64_t)e0 * d * 4;
+    uint32_t a_off;
+    {
+        const int slice = wave < kASlices ? wave : 0;
+        const int r = slice * (1024 / kARow) + lane / kAChunks;
+        const int c = lane % kAChunks;
+        const int pc = kAChunks == 8 ? (c ^ swz128(r)) : (c ^ swz64(r));
+        const int rr = r < ntok ? r : 0;
+        a_off = (uint32_t)(rr * d * kInB + pc * 16);
+    }
+    uint32_t b_off[CB];
 #pragma unroll
-        for (int qq = 0; qq < kPer; qq++) {
-            const int e = lane + 64 * qq;
-            key[qq] = (e < E) ? (((uint64_t)order_key(lt[tt * ldl + e]) << 32) |
-                                 (uint64_t)(0xFFFFFFFFu - (uint32_t)e))
-                              : 0ull;
+    for (int i = 0; i < CB; i++) {
+        const int r = (wave * CB + i) * 8 + (lane >> 3);
+        const int pc = (lane & 7) ^ swz128(r & 31);
+        const int e = r < ne ? r : 0;
+        b_off[i] = (uint32_t)(e * d * 4 + pc * 16);
+    }
+    auto issue = [&](int kt, int buf) __attribute__((always_inline)) {
+        char* st = lds + buf * kStageBytes;
+        const int64_t k0 = (int64_t)kt * kKS - (tail16 && kt == nk - 1 ? kKS / 2 : 0);
+        const void* const Ak = uniform_ptr(a_base + k0 * kInB);
+        const void* const Bk = uniform_ptr(b_base + k0 * 4);
+        const uint32_t st_addr = lds_addr(st);
+        dma16_off(Ak, a_off, wave < kASlices ? st_addr + wave * 1024 : lds_addr(dummy));
+#pragma unroll
+        for (int i = 0; i < CB; i++)
+            dma16_off(Bk, b_off[i], st_addr + kTokS * kARow + (wave * CB + i) * 1024);
+    };
+
+    floatx16 acc[CB];
+#pragma unroll
+    for (int i = 0; i < CB; i++)
+#pragma unroll
+        for (int v = 0; v < 16; v++) acc[i][v] = 0.0f;
+
+    const int q = lane >> 5;                // which half of the stage's K this lane takes
+    const int row = lane & 31;
+    const int arow = wr * 32 + row;         // this lane's h row within the 64
+    typedef const __attribute__((address_space(4))) float* cgp;
+    typedef float f32x8 __attribute__((ext_vector_type(8)));
+    f32x8 g0n, g1n;
+    auto load_g = [&](int kt) __attribute__((always_inline)) {
+        const int kb = kt * kKS;
+        const bool tl = tail16 && kt == nk - 1;
+        if (rp.g) {
+            const cgp g = (cgp)rp.g + kb + 8 * kh;
+            g0n = *(const __attribute__((address_space(4))) f32x8*)g;
+            g1n = *(const __attribute__((address_space(4))) f32x8*)(g + (tl ? 0 : 16));
+        } else {
+            g0n = 1.0f;
+            g1n = 1.0f;
         }
-        float lmax = 0.0f, sum = 0.0f, my_val = 0.0f;
-        int my_id = 0;
-        for (int j = 0; j < k; j++) {
-            uint64_t best = 0ull;
+    };
+    load_g(0);
 #pragma unroll
-            for (int qq = 0; qq < kPer; qq++) best = key[qq] > best ? key[qq] : best;
-            best = wave_max_u64(best);
-            const int sel_e = (int)(0xFFFFFFFFu - (uint32_t)best);
-            const float sel_l = lt[tt * ldl + sel_e];
+    for (int s0 = 0; s0 < kStages - 1; s0++)
+        if (s0 < nk) issue(s0, s0);
+
+    // sum of squares of this lane's h values (waves of the first column half
+    // only: the other half reads the same values)
+    float ss = 0.0f;
+    int buf = 0;
+    for (int kt = 0; kt < nk; kt++) {
+        // stage kt has landed once at most the kStages - 2 later stages are in
+        // flight (every iteration issues one, re-reads past the end included)
+        if (nk >= kStages - 1) wait_vmcnt<(kStages - 2) * kDma>();
+        else wait_vmcnt<0>();
+        bare_barrier();
+        const bool dead = tail16 && kt == nk - 1 && q == 0;
+        const f32x8 gq = q ? g1n : g0n;
+        float gs[8];
 #pragma unroll
-            for (int qq = 0; qq < kPer; qq++)
-                if (lane + 64 * qq == sel_e) key[qq] = 0ull;
-            if (j == 0) lmax = sel_l;
-            const float ex = expf(sel_l - lmax);
-            sum += ex;
-            if (lane == j) {
-                my_val = ex;
-                my_id = sel_e;
+        for (int s2 = 0; s2 < 8; s2++) gs[s2] = dead ? 0.0f : gq[s2];
+        {
+            // into the slot of stage kt-1; past the last stage the DMAs re-read
+            // it into a slot nothing reads any more
+            const int nb = buf == 0 ? kStages - 1 : buf - 1;
+            issue(min(kt + kStages - 1, nk - 1), nb);
+        }
+        const char* st = lds + buf * kStageBytes;
+        buf = buf + 1 == kStages ? 0 : buf + 1;
+        float a[8];
+        if (kInB == 4) {
+            const int c0 = 4 * q + 2 * kh;
+            const float4 v0 = *(const float4*)(st + arow * 128 + ((c0) ^ swz128(arow)) * 16);
+            const float4 v1 = *(const float4*)(st + arow * 128 + ((c0 + 1) ^ swz128(arow)) * 16);
+            a[0] = v0.x; a[1] = v0.y; a[2] = v0.z; a[3] = v0.w;
+            a[4] = v1.x; a[5] = v1.y; a[6] = v1.z; a[7] = v1.w;
+        } else {
+            const uint4 u = *(const uint4*)(st + arow * 64 + ((2 * q + kh) ^ swz64(arow)) * 16);
+            const uint32_t ww[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                a[2 * e] = __uint_as_float(ww[e] << 16);
+                a[2 * e + 1] = __uint_as_float(ww[e] & 0xffff0000u);
             }
         }
-        if (lane < k) {
-            rp.ids[(t0 + tt) * k + lane] = my_id;
-            rp.w[(t0 + tt) * k + lane] = my_val / sum;
+        if (wc == 0 && !dead) {
+#pragma unroll
+            for (int s2 = 0; s2 < 8; s2++) ss += a[s2] * a[s2];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 8; s2++) a[s2] *= gs[s2];
+        // the column blocks' MFMAs interleaved step by step (CB independent
+        // accumulations in flight)
+        float b[CB][8];
+#pragma unroll
+        for (int i = 0; i < CB; i++) {
+            const char* brow = st + kTokS * kARow + ((wc * CB + i) * 32 + row) * 128;
+            const int c0 = 4 * q + 2 * kh;
+            const float4 b0 = *(const float4*)(brow + ((c0) ^ swz128(row)) * 16);
+            const float4 b1 = *(const float4*)(brow + ((c0 + 1) ^ swz128(row)) * 16);
+            b[i][0] = b0.x; b[i][1] = b0.y; b[i][2] = b0.z; b[i][3] = b0.w;
+            b[i][4] = b1.x; b[i][5] = b1.y; b[i][6] = b1.z; b[i][7] = b1.w;
+        }
+#pragma unroll
+        for (int s2 = 0; s2 < 8; s2++)
+#pragma unroll
+            for (int i = 0; i < CB; i++)
+                acc[i] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[s2], b[i][s2], acc[i], 0, 0, 0);
+        load_g(min(kt + 1, nk - 1));
+    }
+    // the last re-read may still be landing in a slot the logits tile overlaps
+    wait_vmcnt<0>();
+
+    // ---- inverse RMS of the 64 rows: lanes row and row + 32 hold the two K
+    // quarters of a stage, the kh waves its two halves (summed in that order)
+    ss += __shfl_xor(ss, 32, 64);
+    if (wc == 0 && lane < 32) ss_half[kh][arow] = ss;
+    __syncthreads();
+    if (tid < kTokS) {
+        const float t2 = ss_half[0][tid] + ss_half[1][tid];
+        inv_rms[tid] = rp.apply_norm ? 1.0f / sqrtf(t2 / (float)d + rp.eps) : 1.0f;
+    }
+    __syncthreads();
+
+    // ---- logits tile in LDS (first K half, then the second added, scaled,
+    // plus bias), written out
+    float* lt = (float*)lds;                 // [kTokS][kEP + 1]
+    constexpr int ldl = kEP + 1;
+    for (int half = 0; half < 2; half++) {
+        if (kh == half) {
+#pragma unroll
+            for (int i = 0; i < CB; i++) {
+                const int el = (wc * CB + i) * 32 + row;
+                const float bias = (rp.b_r && el < ne) ? rp.b_r[e0 + el] : 0.0f;
+#pragma unroll
+                for (int v = 0; v < 16; v++) {
+                    const int tr = wr * 32 + acc_row(v, lane);
+                    if (half == 0)
+                        lt[tr * ldl + el] = acc[i][v];
+                    else
+                        lt[tr * ldl + el] = (lt[tr * ldl + el] + acc[i][v]) * inv_rms[tr] + bias;
+                }
+            }
+        }
+        __syncthreads();
+    }
+    const int E = rp.E;
+    for (int idx = tid; idx < ntok * ne; idx += kThreads) {
+        const int tt = idx / ne, j = idx % ne;
+        rp.logits[(t0 + tt) * E + e0 + j] = lt[tt * ldl + j];
+    }
+    if (hf == 0 && rp.r_out)
+        for (int tt = tid; tt < ntok; tt += kThreads) rp.w[(t0 + tt) * rp.k] = inv_rms[tt];
+}
+
+// One wave per token: the normalised row r = h * inv_rms * g (when asked), then
+// top-k over the token's logits.  KPER = experts per lane (E padded to 64 KPER).
+template <typename Tin, typename Tr, int KPER>
+__global__ __launch_bounds__(256) void route_select_kernel(RouteParams rp) {
+    constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= rp.T) return;
+    const int E = rp.E, k = rp.k, d = rp.d;
+    if (rp.r_out) {
+        // the inverse RMS the logits kernel left in this token's first weight
+        const float ir = rp.w[t * k];
+        const char* row = (const char*)rp.h + t * (int64_t)d * kInB;
+        // U chunks of 4 values per lane per pass, all loaded before any is stored
+        // (one pass per 6 KB of float32 row: the wave's loads are in flight together)
+        constexpr int U = 6;
+        for (int c0 = lane * 4; c0 < d; c0 += 256 * U) {
+            float v[U][4];
+            float4 gg[U];
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int c = c0 + 256 * u;
+                if (c < d) {
+                    if (kInB == 4) {
+                        const float4 f = *(const float4*)(row + (int64_t)c * 4);
+                        v[u][0] = f.x; v[u][1] = f.y; v[u][2] = f.z; v[u][3] = f.w;
+                    } else {
+                        const uint2 x = *(const uint2*)(row + (int64_t)c * 2);
+                        v[u][0] = __uint_as_float(x.x << 16);
+                        v[u][1] = __uint_as_float(x.x & 0xffff0000u);
+                        v[u][2] = __uint_as_float(x.y << 16);
+                        v[u][3] = __uint_as_float(x.y & 0xffff0000u);
+                    }
+                    gg[u] = rp.g ? *(const float4*)(rp.g + c) : make_float4(1, 1, 1, 1);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int c = c0 + 256 * u;
+                if (c < d) {
+                    v[u][0] *= ir * gg[u].x;
+                    v[u][1] *= ir * gg[u].y;
+                    v[u][2] *= ir * gg[u].z;
+                    v[u][3] *= ir * gg[u].w;
+                    const int64_t o = t * (int64_t)d + c;
+                    if (sizeof(typename Elem<Tr>::store_t) == 4) {
+                        *(float4*)((float*)rp.r_out + o) =
+                            make_float4(v[u][0], v[u][1], v[u][2], v[u][3]);
+                    } else {
+                        uint2 x;
+                        x.x = (uint32_t)f32_to_bf16(v[u][0]) | ((uint32_t)f32_to_bf16(v[u][1]) << 16);
+                        x.y = (uint32_t)f32_to_bf16(v[u][2]) | ((uint32_t)f32_to_bf16(v[u][3]) << 16);
+                        *(uint2*)((u16*)rp.r_out + o) = x;
+                    }
+                }
+            }
         }
     }
+    const float* lrow = rp.logits + t * E;
+    select_topk<KPER>(lane, E, k, [&](int e) { return lrow[e]; }, rp.ids + t * k, rp.w + t * k);
+}
+
+template <typename Tin, typename Tr, int CB>
+hipError_t launch_split(const RouteParams& rp, hipStream_t s) {
+    constexpr int kInB = (int)sizeof(typename Elem<Tin>::store_t);
+    constexpr size_t kStage = (size_t)kTokS * kKS * kInB + (size_t)64 * CB * 128;
+    constexpr size_t kRing = (kStage <= 32768 ? 4 : 3) * kStage + 1024;
+    constexpr size_t kTile = (size_t)kTokS * (64 * CB + 1) * 4;
+    const size_t lds = kRing > kTile ? kRing : kTile;
+    hipError_t e = hipFuncSetAttribute((const void*)route_logits_kernel<Tin, CB>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int EH = (rp.E + 1) / 2;
+    const int64_t ntb = (rp.T + kTokS - 1) / kTokS;      // token blocks
+    const int64_t blocks = 8 * ((ntb + 3) / 4);          // 4 token blocks per XCD row
+    hipLaunchKernelGGL((route_logits_kernel<Tin, CB>), dim3((unsigned)blocks), dim3(kThreads), lds,
+                       s, rp, EH);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((route_select_kernel<Tin, Tr, 2 * CB>), dim3((unsigned)((rp.T + 3) / 4)),
+                       dim3(256), 0, s, rp);
+    return hipGetLastError();
 }
 
 template <typename Tin, typename Tr, int NH>
@@ -443,6 +766,9 @@ hipError_t launch_nh(const RouteParams& rp, hipStream_t s) {
 
 template <typename Tin, typename Tr>
 hipError_t launch_rt(const RouteParams& rp, hipStream_t s) {
+    // wide routers whose logits have somewhere to go take the expert-split form
+    if (rp.E > 256 && rp.logits)
+        return rp.E > 384 ? launch_split<Tin, Tr, 4>(rp, s) : launch_split<Tin, Tr, 3>(rp, s);
     switch ((rp.E + 127) / 128) {
         case 1: return launch_nh<Tin, Tr, 1>(rp, s);
         case 2: return launch_nh<Tin, Tr, 2>(rp, s);

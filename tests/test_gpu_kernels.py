@@ -43,6 +43,11 @@ ROUTE_SHAPES = [  # T, d_r, E, k
     (1000, 128, 64, 4),
     (8192, 64, 384, 8),     # 535B router width and expert count, full token count
     (300, 32, 512, 16),     # largest E and k
+    # expert-split form (E > 256 with a logits output): halves of ceil(E/2) experts,
+    # 64-token workgroups
+    (129, 48, 257, 3),      # odd E (halves of 129 and 128), a 16-value K tail, ragged tokens
+    (70, 1040, 300, 6),     # K = 32.5 stages, halves of 150
+    (200, 96, 449, 9),      # the four-column-block form (halves of 225)
 ]
 
 
@@ -81,6 +86,8 @@ def test_route_signed_zero_and_ties(M):
 
 
 @pytest.mark.parametrize("T,d,E,k,hdt,rdt", [(777, 3072, 384, 8, "f32", "bf16"),
+                                              (301, 1040, 384, 8, "bf16", "f32"),
+                                              (97, 2064, 512, 16, "f32", "f32"),
                                               (256, 128, 16, 2, "f32", "f32"),
                                               (500, 2048, 64, 4, "bf16", "f32"),
                                               (129, 1040, 96, 6, "bf16", "bf16")])
@@ -120,6 +127,28 @@ def test_route_rmsnorm_router_on_real_distribution(M, T, d, E, k, hdt, rdt):
     # the rest is valid: every chosen expert is within the tolerance of the k-th logit
     for t in np.flatnonzero(~clear):
         assert np.all(lg64[t, gi[t]] >= srt[t, k - 1] - 2 * tol_l)
+
+
+@pytest.mark.parametrize("hdt", ["f32", "bf16"])
+@pytest.mark.parametrize("E", [384, 512])
+def test_route_forms_agree(M, E, hdt):
+    """A wide router runs in its expert-split form (two kernels) when it has a logits
+    output and in the one-kernel form without: on exactly representable logits both
+    must give the same ids and bit-identical weights, and the same router input r."""
+    g = torch.Generator().manual_seed(E)
+    T, d, k = 333, 80, 8
+    h = torch.randint(-2, 3, (T, d), generator=g).to(TDT[hdt])
+    W = torch.randint(-3, 4, (E, d), generator=g).float()
+    b = torch.randint(-2, 3, (E,), generator=g).float() * 0.5
+    r1 = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    r2 = torch.empty((T, d), dtype=torch.float32, device=DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    ids1, w1 = M.moe_route(h.to(DEV), W.to(DEV), k, b_r=b.to(DEV), r_out=r1, logits_out=logits)
+    ids2, w2 = M.moe_route(h.to(DEV), W.to(DEV), k, b_r=b.to(DEV), r_out=r2)
+    torch.cuda.synchronize()
+    assert torch.equal(ids1.cpu(), ids2.cpu())
+    assert torch.equal(w1.cpu(), w2.cpu())
+    assert torch.equal(r1.cpu(), r2.cpu()) and torch.equal(r1.cpu(), h.float())
 
 
 @pytest.mark.parametrize("hdt,rdt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16")])
