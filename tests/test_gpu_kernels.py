@@ -151,6 +151,28 @@ def test_route_forms_agree(M, E, hdt):
     assert torch.equal(r1.cpu(), r2.cpu()) and torch.equal(r1.cpu(), h.float())
 
 
+def test_route_split_form_logits_do_not_depend_on_the_router_input_output(M):
+    """In the expert-split form the inverse RMS scales the logits in the first
+    kernel whether or not the router input r is asked for (only then is it handed to
+    the second kernel): logits, ids and weights are bit-identical either way."""
+    g = torch.Generator().manual_seed(5)
+    T, d, E, k = 515, 3072, 384, 8
+    h = (torch.randn((T, d), generator=g) * 3).to(DEV)
+    W = (torch.randn((E, d), generator=g) / math.sqrt(d)).to(DEV)
+    b = (0.1 * torch.randn(E, generator=g)).to(DEV)
+    gain = (1 + 0.1 * torch.randn(d, generator=g)).to(DEV)
+    out = []
+    for with_r in (True, False):
+        r_out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV) if with_r else None
+        logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        ids, w = M.moe_route(h, W, k, b_r=b, norm_g=gain, eps=1e-5, apply_norm=True,
+                             r_out=r_out, logits_out=logits)
+        out.append((logits, ids, w))
+    torch.cuda.synchronize()
+    for a, c in zip(out[0], out[1]):
+        assert torch.equal(a.cpu(), c.cpu())
+
+
 @pytest.mark.parametrize("hdt,rdt", [("f32", "f32"), ("f32", "bf16"), ("bf16", "bf16")])
 def test_route_writes_router_input_without_norm(M, hdt, rdt):
     """Without the norm the router input r is h itself, stored in r's dtype."""
