@@ -440,21 +440,23 @@ __global__ __launch_bounds__(kThreads, 1) void route_kernel(RouteParams rp) {
             rp.w + (t0 + tt) * k);
 }
 
-// ---- Expert-split form, for wide routers (E > 256) whose float32 W_r does not
-// fit one XCD's L2 (384 x 3,072 x 4 bytes = 4.7 MB against 4 MB).  Each CU
-// streams its operands through its own LDS ring at a bounded rate, so the time
-// is set by the bytes each workgroup loads: a workgroup owning 32 tokens and
-// every expert loads all of W_r for 32 tokens' worth of MFMAs.  Here a
-// workgroup owns 64 tokens and one half of the experts (the same MFMAs per
-// byte of W_r twice over), and the halves are dealt by XCD: workgroup b runs on
-// XCD b % 8, and XCDs 0-3 take the first half, 4-7 the second, so each XCD's
-// L2 serves one 2.4 MB half to its 32 CUs.  Two kernels:
+// ---- Expert-split form, for wide routers (E > 256) with a logits output.  The
+// float32 W_r of 384 experts (384 x 3,072 x 4 bytes = 4.7 MB) does not fit one
+// XCD's 4 MB L2, and every workgroup of route_kernel streams all of it for its
+// 32 tokens.  Here a workgroup owns 64 tokens and one half of the experts, and
+// the halves are dealt by XCD: workgroup b runs on XCD b % 8, and XCDs 0-3 take
+// the first half, 4-7 the second, so each XCD's L2 serves one 2.4 MB half to its
+// 32 CUs.  The row pass of route_kernel (the inverse RMS and the normalised
+// rows, computed by each workgroup for its 32 rows before its logits loop) is
+// replaced:
+// the inverse RMS is summed from the h values the K loop already reads, and the
+// normalised rows are written by a second kernel with one wave per token.  Two
+// kernels:
 //   route_logits_kernel: the logits of its 64 tokens x E/2 experts, as in
 //     route_kernel (float32 MFMAs on g-scaled h, K halves summed in a fixed
 //     order, then scaled by the inverse RMS, plus bias), written to the logits
-//     output.  The inverse RMS is summed from the h values the K loop already
-//     reads (no separate pass over the rows); the first half's workgroups leave
-//     it in topk_w[t * k] for the second kernel;
+//     output; the first half's workgroups leave the inverse RMS in
+//     topk_w[t * k] for the second kernel;
 //   route_select_kernel: one wave per token: the normalised row r (when asked),
 //     then top-k and the weights from the logits.
 constexpr int kTokS = 64;   // tokens per workgroup in the expert-split form
